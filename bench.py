@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Throughput of the block-sparse attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  bsa_plan          layout -> per-row CSR   (causal Bernoulli layout, 32 heads,
+                                             256 x 256 blocks)
+  bsa_forward       block-sparse attention  (B1 H32 S32768 bs128 d128, bf16)
+  topk_sparse_attn  top-k gathered attention with sink
+                                            (M4096 H64 d512 N8192 top-k 2048)
+Inputs are drawn once, copied to the GPU, and stay resident; W untimed warm-up
+steps precede K timed steps, bracketed by device synchronisation.  HIP events
+recorded on the launch stream between the three calls give each kernel's
+average duration.
+
+Prints ONE JSON line.  `value` = live-tile FLOPs of the step (4*b^2*d per live
+tile per head per batch item + 4*d*H per valid top-k index) / step time.
+
+Flags: --gpus N (only 1 is supported), --steps K, --warmup W,
+--no-cpu-baseline (skip the oracle timing), --cpu-seconds S (oracle sample
+budget per kernel), --copy-calibration (also run one plain device copy of
+known size, for HBM counter scaling under a profiler).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+REPO = os.path.dirname(os.path.abspath(__file__))
+FWD_WORKLOAD = "causal_bernoulli_h32_s32768_bs128_d128"
+TOPK_WORKLOAD = "topk2048_m4096_h64_d512_n8192"
+METRIC = "effective TFLOP/s on live tiles and % of bf16 MFMA peak, 1×MI355X"
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA, TFLOP/s
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, GB/s
+TRAFFIC_FILE = os.path.join(REPO, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = {
+    "bsa_forward": os.path.join(REPO, "block_sparse_attention_plan_amd", "csrc", "forward.hip"),
+    "topk_sparse_attn": os.path.join(REPO, "block_sparse_attention_plan_amd", "csrc", "topk.hip"),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(path: str) -> str:
+    h = hashlib.sha256()
+    for p in (path, os.path.join(os.path.dirname(path), "bsa_device.h")):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    absent or taken on a different version of the kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(kernel)
+    if not ent or ent.get("source_sha") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def bsa_counts(layout: np.ndarray, B: int, bs: int, d: int, elem: int = 2):
+    """Live tiles, algorithmic FLOPs and bytes of one block-sparse forward."""
+    H, Mb, Nb = layout.shape
+    tiles = int((layout != 0).sum())
+    flops = 4.0 * bs * bs * d * tiles * B
+    q_o = 2.0 * B * H * Mb * bs * d * elem          # read q, write out
+    kv = 2.0 * bs * d * elem * tiles * B            # live K and V tiles
+    lse = 4.0 * B * H * Mb * bs
+    return tiles * B, flops, q_o + kv + lse
+
+
+def topk_counts(idx: np.ndarray, H: int, d: int):
+    """Valid indices, algorithmic FLOPs and bytes of one top-k forward."""
+    B, M, topk = idx.shape
+    valid = int((idx >= 0).sum())
+    flops = 4.0 * d * H * valid
+    nbytes = valid * d * 2.0 + B * M * (2.0 * H * d * 2 + topk * 4)
+    return valid, flops, nbytes
+
+
+def cpu_baseline(fwd, topk_in, budget_s: float):
+    """Time the oracle, as it stands, on a bounded sample of the same step."""
+    from oracle import bsa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    B, H, S, d = fwd.q.shape
+    bs = fwd.bs
+    q64, k64, v64 = (t.float().numpy().astype(np.float64) for t in (fwd.q, fwd.k, fwd.v))
+    nnz = (fwd.layout != 0).sum(-1)
+    rng = np.random.default_rng(0)
+    all_rows = [(b, h, m) for b in range(B) for h in range(H) for m in range(S // bs)]
+    order = rng.permutation(len(all_rows))
+    flops_f, t_f, n_rows = 0.0, 0.0, 0
+    t_plan0 = time.perf_counter()
+    O.plan(fwd.layout)
+    t_plan = time.perf_counter() - t_plan0
+    chunk = 16
+    i = 0
+    while t_f < budget_s and i < len(order):
+        rows = [all_rows[j] for j in order[i:i + chunk]]
+        i += chunk
+        t0 = time.perf_counter()
+        O.attention_live_tiles(q64, k64, v64, fwd.layout, bs, fwd.scale, row_blocks=rows)
+        t_f += time.perf_counter() - t0
+        flops_f += sum(4.0 * bs * bs * d * nnz[h, m] for _, h, m in rows)
+        n_rows += len(rows)
+    qk64, kv64 = (t.float().numpy().astype(np.float64) for t in (topk_in.q, topk_in.kv))
+    idx = topk_in.idx.numpy()
+    sink = topk_in.sink.numpy() if topk_in.sink is not None else None
+    Bq, M, Hq, dq = topk_in.q.shape
+    pos_all = rng.permutation(Bq * M)
+    flops_t, t_t, n_pos = 0.0, 0.0, 0
+    i = 0
+    while t_t < budget_s and i < len(pos_all):
+        pos = [(int(p) // M, int(p) % M) for p in pos_all[i:i + 4]]
+        i += 4
+        t0 = time.perf_counter()
+        O.topk_attention(qk64, kv64, idx, sink, topk_in.scale, positions=pos)
+        t_t += time.perf_counter() - t0
+        flops_t += sum(4.0 * dq * Hq * int((idx[b, m] >= 0).sum()) for b, m in pos)
+        n_pos += len(pos)
+    total_t = t_plan + t_f + t_t
+    value = (flops_f + flops_t) / (t_f + t_t) / 1e12
+    return {
+        "value": value,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"fp64 NumPy oracle on {n_rows} random row blocks of {FWD_WORKLOAD} "
+                   f"({t_f:.1f} s) and {n_pos} random positions of {TOPK_WORKLOAD} "
+                   f"({t_t:.1f} s), plus the full plan ({t_plan:.2f} s); value = sampled "
+                   f"live-tile FLOPs / sampled time"),
+        "seconds": round(total_t, 2),
+        "host_cores_visible": len(os.sched_getaffinity(0)),
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by heads or query blocks with no exchange, see the design notes)",
+              file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+    import block_sparse_attention_plan_amd as bsa
+    from block_sparse_attention_plan_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    bsa.load_library()
+
+    log(f"[bench] drawing {FWD_WORKLOAD}")
+    fwd = W.make_workload(FWD_WORKLOAD)
+    log(f"[bench] drawing {TOPK_WORKLOAD}")
+    tk = W.make_workload(TOPK_WORKLOAD)
+    B, H, S, d = (int(x) for x in fwd.q.shape)
+    tiles, f_flops, f_bytes = bsa_counts(fwd.layout, B, fwd.bs, d)
+    Bq, M, Hq, dq = (int(x) for x in tk.q.shape)
+    valid, t_flops, t_bytes = topk_counts(tk.idx.numpy(), Hq, dq)
+
+    layout = torch.from_numpy(fwd.layout).to(dev)
+    q, k, v = (t.to(dev) for t in (fwd.q, fwd.k, fwd.v))
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    tq, tkv, tidx, tsink = tk.q.to(dev), tk.kv.to(dev), tk.idx.to(dev), tk.sink.to(dev)
+    tout = torch.empty_like(tq)
+    pbuf = bsa.plan_buffer(layout.shape, dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        plan = bsa.bsa_plan(layout, buf=pbuf)
+        if ev is not None:
+            ev[1].record()
+        bsa.bsa_forward(q, k, v, plan, fwd.scale, out=out, lse=lse)
+        if ev is not None:
+            ev[2].record()
+        bsa.topk_sparse_attn(tq, tkv, tidx, tsink, tk.scale, out=tout)
+        if ev is not None:
+            ev[3].record()
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_plan = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    t_fwd = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    t_topk = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+    t_step_ev = sum(e[0].elapsed_time(e[3]) for e in events) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 1 GiB device-to-device copy issued")
+
+    fwd_tflops = f_flops / (t_fwd * 1e-3) / 1e12
+    topk_tflops = t_flops / (t_topk * 1e-3) / 1e12
+    topk_gbs = t_bytes / (t_topk * 1e-3) / 1e9
+    fwd_gbs = f_bytes / (t_fwd * 1e-3) / 1e9
+    kernels = {
+        "bsa_plan": {"avg_ms": round(t_plan, 5)},
+        "bsa_forward": {
+            "avg_ms": round(t_fwd, 5), "live_tiles": tiles, "flops": f_flops,
+            "tflops": round(fwd_tflops, 2), "pct_bf16_peak": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
+            "algorithmic_bytes": f_bytes, "algorithmic_gbs": round(fwd_gbs, 1)},
+        "topk_sparse_attn": {
+            "avg_ms": round(t_topk, 5), "valid_indices": valid, "flops": t_flops,
+            "tflops": round(topk_tflops, 2), "pct_bf16_peak": round(100 * topk_tflops / PEAK_BF16_TFLOPS, 2),
+            "algorithmic_bytes": t_bytes, "algorithmic_gbs": round(topk_gbs, 1),
+            "pct_hbm_peak": round(100 * topk_gbs / PEAK_HBM_GBS, 2)},
+    }
+    # dominant kernel of the step and its roofline
+    if t_fwd >= t_topk:
+        roof = {"kernel": "bsa_forward", "bound": "mfma", "achieved": round(fwd_tflops, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic("bsa_forward")}
+    else:
+        roof = {"kernel": "topk_sparse_attn", "bound": "hbm", "achieved": round(topk_gbs, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(topk_gbs / PEAK_HBM_GBS, 4),
+                "traffic": measured_traffic("topk_sparse_attn")}
+    value = (f_flops + t_flops) / (ms_per_step * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{FWD_WORKLOAD} + {TOPK_WORKLOAD}",
+            "block_sparse": {"B": B, "H": H, "S": S, "bs": fwd.bs, "d": d,
+                             "layout": "causal Bernoulli(0.10) + diagonal", "live_tiles": tiles},
+            "topk": {"B": Bq, "M": M, "H": Hq, "d": dq, "N": int(tk.kv.shape[1]),
+                     "topk": int(tk.idx.shape[2]), "valid_indices": valid, "sink": True},
+            "event_ms_per_step": round(t_step_ev, 4),
+            "pct_bf16_peak_step": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        },
+        "roofline": roof,
+        "kernels": kernels,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the CPU oracle (about {2 * args.cpu_seconds:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline(fwd, tk, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,280 @@
+"""Block-sparse attention forward for AMD Instinct MI355X (gfx950).
+
+Thin Python binding of ``libbsa.so`` (C ABI in ``include/bsa.h``).  The
+functions below only check and marshal arguments; every step of the
+computation runs in the library's HIP kernels.  PyTorch supplies device
+memory and the current stream.  There is no CPU fallback: if the library is
+missing, every call raises.
+
+    bsa_plan(layout)                      -> Plan   (per-row CSR of live tiles)
+    bsa_forward(q, k, v, plan, scale)     -> (out, lse)
+    topk_sparse_attn(q, kv, idx, attn_sink, scale) -> out
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "BsaError",
+    "Plan",
+    "bsa_plan",
+    "plan_buffer",
+    "bsa_plan_nnz",
+    "bsa_forward",
+    "topk_sparse_attn",
+    "library_path",
+    "load_library",
+]
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG_DIR, "libbsa.so")
+_lib = None
+
+BSA_BF16 = 0
+BSA_F32 = 1
+
+
+class BsaError(RuntimeError):
+    """A libbsa call returned a non-zero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class _PlanT(ctypes.Structure):
+    _fields_ = [
+        ("H", ctypes.c_int32),
+        ("Mb", ctypes.c_int32),
+        ("Nb", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("dev_buf", ctypes.c_void_p),
+        ("dev_bytes", ctypes.c_size_t),
+    ]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libbsa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"libbsa.so not found at {_LIB_PATH}; build it with "
+            "`python -m block_sparse_attention_plan_amd.build`")
+    # torch is imported first so that its HIP runtime (same soname) is the one
+    # the library binds to; streams and pointers then belong to one runtime.
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    lib.bsa_plan_buffer_bytes.argtypes = [i32, i32, i32]
+    lib.bsa_plan_buffer_bytes.restype = ctypes.c_size_t
+    lib.bsa_plan_sections.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.bsa_plan_sections.restype = ctypes.c_int
+    lib.bsa_plan.argtypes = [vp, i32, i32, i32, vp, ctypes.c_size_t, ctypes.POINTER(_PlanT), vp]
+    lib.bsa_plan.restype = ctypes.c_int
+    lib.bsa_plan_nnz.argtypes = [ctypes.POINTER(_PlanT), ctypes.POINTER(ctypes.c_int64), vp]
+    lib.bsa_plan_nnz.restype = ctypes.c_int
+    lib.bsa_forward.argtypes = [vp, vp, vp, ctypes.POINTER(_PlanT), i32, i32, i32, i32, i32, i32,
+                                ctypes.c_int, f32, vp, vp, vp]
+    lib.bsa_forward.restype = ctypes.c_int
+    lib.topk_sparse_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp]
+    lib.topk_sparse_attn.restype = ctypes.c_int
+    lib.bsa_status_string.argtypes = [ctypes.c_int]
+    lib.bsa_status_string.restype = ctypes.c_char_p
+    lib.bsa_last_error.argtypes = []
+    lib.bsa_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        lib = load_library()
+        msg = lib.bsa_last_error().decode(errors="replace") or lib.bsa_status_string(status).decode()
+        raise BsaError(status, msg)
+
+
+def _stream(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _require_gpu(name: str, t: torch.Tensor) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class Plan:
+    """A built plan: owns its device buffer (a uint8 tensor)."""
+
+    def __init__(self, buf: torch.Tensor, raw: _PlanT, H: int, Mb: int, Nb: int):
+        self.buf = buf
+        self._raw = raw
+        self.H, self.Mb, self.Nb = H, Mb, Nb
+        offs = (ctypes.c_size_t * 4)()
+        _check(load_library().bsa_plan_sections(H, Mb, Nb, offs))
+        self._offs = [int(o) for o in offs]
+
+    def _section(self, i: int, count: int) -> torch.Tensor:
+        off = self._offs[i]
+        return self.buf[off:off + 4 * count].view(torch.int32)
+
+    @property
+    def row_ptr(self) -> torch.Tensor:
+        return self._section(0, self.H * self.Mb + 1)
+
+    @property
+    def row_order(self) -> torch.Tensor:
+        return self._section(1, self.H * self.Mb)
+
+    @property
+    def nnz_total_dev(self) -> torch.Tensor:
+        return self._section(2, 1)
+
+    def col_idx(self, nnz_total: Optional[int] = None) -> torch.Tensor:
+        n = self.nnz() if nnz_total is None else nnz_total
+        return self._section(3, n)
+
+    def nnz(self) -> int:
+        return bsa_plan_nnz(self)
+
+
+def plan_buffer(layout_shape, device) -> torch.Tensor:
+    """Allocate a 256-byte aligned plan buffer for a layout of this shape."""
+    H, Mb, Nb = (int(x) for x in layout_shape)
+    nbytes = load_library().bsa_plan_buffer_bytes(H, Mb, Nb)
+    if nbytes == 0:
+        raise ValueError(f"invalid layout shape {tuple(layout_shape)}")
+    buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    shift = (-buf.data_ptr()) % 256
+    return buf[shift:shift + nbytes]
+
+
+def bsa_plan(layout: torch.Tensor, buf: Optional[torch.Tensor] = None) -> Plan:
+    """Build the per-row CSR plan of an int32 layout [H, Mb, Nb] on the GPU.
+
+    ``buf`` optionally supplies a buffer from plan_buffer() to reuse."""
+    _require_gpu("layout", layout)
+    if layout.dtype != torch.int32 or layout.dim() != 3:
+        raise ValueError("layout must be an int32 tensor [H, Mb, Nb]")
+    lib = load_library()
+    H, Mb, Nb = (int(x) for x in layout.shape)
+    nbytes = lib.bsa_plan_buffer_bytes(H, Mb, Nb)
+    if buf is None:
+        buf = plan_buffer(layout.shape, layout.device)
+    elif buf.dtype != torch.uint8 or buf.numel() < nbytes or buf.device != layout.device:
+        raise ValueError("buf must be a uint8 plan buffer from plan_buffer() for this shape")
+    raw = _PlanT()
+    _check(lib.bsa_plan(ctypes.c_void_p(layout.data_ptr()), H, Mb, Nb,
+                        ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.byref(raw),
+                        _stream(layout)))
+    return Plan(buf, raw, H, Mb, Nb)
+
+
+def bsa_plan_nnz(plan: Plan) -> int:
+    """Number of live tiles of a plan (synchronises the current stream)."""
+    out = ctypes.c_int64(0)
+    _check(load_library().bsa_plan_nnz(ctypes.byref(plan._raw), ctypes.byref(out),
+                                       _stream(plan.buf)))
+    return int(out.value)
+
+
+def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
+                scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, want_lse: bool = True
+                ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Block-sparse attention forward.
+
+    q: [B, H, Sq, d], k/v: [B, H, Sk, d], bf16 or fp32, with Sq = Mb*bs and
+    Sk = Nb*bs for the plan's layout.  Returns (out [B, H, Sq, d] of q's dtype,
+    lse [B, H, Sq] fp32 or None).  scale defaults to 1/sqrt(d).
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require_gpu(name, t)
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, S, d]")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q, k, v must share dtype bf16 or fp32")
+    B, H, Sq, d = (int(x) for x in q.shape)
+    if tuple(k.shape) != tuple(v.shape) or k.shape[0] != B or k.shape[1] != H or k.shape[3] != d:
+        raise ValueError("k and v must be [B, H, Sk, d] matching q")
+    Sk = int(k.shape[2])
+    if Sq % plan.Mb != 0:
+        raise ValueError("Sq must be a multiple of the layout's block rows")
+    bs = Sq // plan.Mb
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require_gpu("out", out)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q")
+    if want_lse and lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _require_gpu("lse", lse)
+        if tuple(lse.shape) != (B, H, Sq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be fp32 [B, H, Sq]")
+    dtype = BSA_BF16 if q.dtype == torch.bfloat16 else BSA_F32
+    _check(load_library().bsa_forward(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+        ctypes.c_void_p(v.data_ptr()), ctypes.byref(plan._raw), B, H, Sq, Sk, bs, d, dtype,
+        float(scale), ctypes.c_void_p(out.data_ptr()),
+        ctypes.c_void_p(lse.data_ptr() if lse is not None else 0), _stream(q)))
+    return out, lse
+
+
+def topk_sparse_attn(q: torch.Tensor, kv: torch.Tensor, idx: torch.Tensor,
+                     attn_sink: Optional[torch.Tensor], scale: Optional[float] = None,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Top-k gathered sparse attention with a per-head sink.
+
+    q: bf16 [B, M, H, d]; kv: bf16 [B, N, d]; idx: int32 [B, M, topk] (-1 =
+    unused slot); attn_sink: fp32 [H] or None.  Returns bf16 [B, M, H, d].
+    scale defaults to 1/sqrt(d).
+    """
+    for name, t in (("q", q), ("kv", kv), ("idx", idx)):
+        _require_gpu(name, t)
+    if q.dtype != torch.bfloat16 or kv.dtype != torch.bfloat16:
+        raise ValueError("q and kv must be bf16")
+    if idx.dtype != torch.int32:
+        raise ValueError("idx must be int32")
+    if q.dim() != 4 or kv.dim() != 3 or idx.dim() != 3:
+        raise ValueError("expected q [B,M,H,d], kv [B,N,d], idx [B,M,topk]")
+    B, M, H, d = (int(x) for x in q.shape)
+    N = int(kv.shape[1])
+    topk = int(idx.shape[2])
+    if kv.shape[0] != B or kv.shape[2] != d or idx.shape[0] != B or idx.shape[1] != M:
+        raise ValueError("q, kv, idx shapes disagree")
+    if attn_sink is not None:
+        _require_gpu("attn_sink", attn_sink)
+        if attn_sink.dtype != torch.float32 or tuple(attn_sink.shape) != (H,):
+            raise ValueError("attn_sink must be fp32 [H]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require_gpu("out", out)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q")
+    _check(load_library().topk_sparse_attn(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(kv.data_ptr()),
+        ctypes.c_void_p(idx.data_ptr()),
+        ctypes.c_void_p(attn_sink.data_ptr() if attn_sink is not None else 0),
+        B, M, N, H, d, topk, float(scale), ctypes.c_void_p(out.data_ptr()), _stream(q)))
+    return out

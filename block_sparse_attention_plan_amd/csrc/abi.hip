@@ -1,0 +1,178 @@
+// C ABI of libbsa: argument validation, error reporting and dispatch to the
+// kernel launchers.  Every check here runs on the host before any HIP call.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "../../include/bsa.h"
+#include "bsa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_fail(hipError_t e, const char *where) {
+  return fail(BSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_plan(const bsa_plan_t *plan, bsa::PlanGeometry *g) {
+  if (plan == nullptr) return fail(BSA_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->dev_buf == nullptr) return fail(BSA_ERR_INVALID_ARG, "plan has no buffer");
+  if (!bsa::plan_geometry(plan->H, plan->Mb, plan->Nb, g))
+    return fail(BSA_ERR_INVALID_ARG, "plan has invalid dimensions");
+  if (plan->dev_bytes < g->total)
+    return fail(BSA_ERR_BUFFER_TOO_SMALL, "plan buffer is %zu bytes, needs %zu", plan->dev_bytes,
+                g->total);
+  return BSA_OK;
+}
+
+template <typename P>
+P *at(void *base, size_t off) {
+  return reinterpret_cast<P *>(static_cast<char *>(base) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bsa_plan_buffer_bytes(int32_t H, int32_t Mb, int32_t Nb) {
+  bsa::PlanGeometry g;
+  if (!bsa::plan_geometry(H, Mb, Nb, &g)) return 0;
+  return g.total;
+}
+
+int bsa_plan_sections(int32_t H, int32_t Mb, int32_t Nb, size_t offsets_out[4]) {
+  bsa::PlanGeometry g;
+  if (offsets_out == nullptr) return fail(BSA_ERR_INVALID_ARG, "offsets_out is NULL");
+  if (!bsa::plan_geometry(H, Mb, Nb, &g))
+    return fail(BSA_ERR_INVALID_ARG, "invalid layout dimensions H=%d Mb=%d Nb=%d", H, Mb, Nb);
+  offsets_out[0] = g.off_row_ptr;
+  offsets_out[1] = g.off_row_order;
+  offsets_out[2] = g.off_nnz;
+  offsets_out[3] = g.off_col_idx;
+  return BSA_OK;
+}
+
+int bsa_plan(const int32_t *layout, int32_t H, int32_t Mb, int32_t Nb, void *dev_buf,
+             size_t dev_bytes, bsa_plan_t *plan_out, void *stream) {
+  if (layout == nullptr || dev_buf == nullptr || plan_out == nullptr)
+    return fail(BSA_ERR_INVALID_ARG, "bsa_plan: NULL pointer argument");
+  bsa::PlanGeometry g;
+  if (!bsa::plan_geometry(H, Mb, Nb, &g))
+    return fail(BSA_ERR_INVALID_ARG, "bsa_plan: invalid dimensions H=%d Mb=%d Nb=%d", H, Mb, Nb);
+  if (Nb > bsa::kPlanMaxNb)
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_plan: Nb=%d exceeds %d", Nb, bsa::kPlanMaxNb);
+  if (!aligned(dev_buf, 256)) return fail(BSA_ERR_MISALIGNED, "bsa_plan: buffer not 256-byte aligned");
+  if (dev_bytes < g.total)
+    return fail(BSA_ERR_BUFFER_TOO_SMALL, "bsa_plan: buffer is %zu bytes, needs %zu", dev_bytes,
+                g.total);
+  hipError_t e = bsa::launch_plan(layout, H, Mb, Nb, at<int32_t>(dev_buf, g.off_row_ptr),
+                                  at<int32_t>(dev_buf, g.off_row_order),
+                                  at<int32_t>(dev_buf, g.off_nnz),
+                                  at<int32_t>(dev_buf, g.off_col_idx), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "bsa_plan launch");
+  plan_out->H = H;
+  plan_out->Mb = Mb;
+  plan_out->Nb = Nb;
+  plan_out->reserved = 0;
+  plan_out->dev_buf = dev_buf;
+  plan_out->dev_bytes = dev_bytes;
+  return BSA_OK;
+}
+
+int bsa_plan_nnz(const bsa_plan_t *plan, int64_t *nnz_host, void *stream) {
+  bsa::PlanGeometry g;
+  int st = check_plan(plan, &g);
+  if (st != BSA_OK) return st;
+  if (nnz_host == nullptr) return fail(BSA_ERR_INVALID_ARG, "bsa_plan_nnz: nnz_host is NULL");
+  int32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, at<int32_t>(plan->dev_buf, g.off_nnz), sizeof(v),
+                                hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "bsa_plan_nnz copy");
+  e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "bsa_plan_nnz sync");
+  *nnz_host = v;
+  return BSA_OK;
+}
+
+int bsa_forward(const void *q, const void *k, const void *v, const bsa_plan_t *plan, int32_t B,
+                int32_t H, int32_t Sq, int32_t Sk, int32_t bs, int32_t d, bsa_dtype_t dtype,
+                float scale, void *out, float *lse, void *stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+    return fail(BSA_ERR_INVALID_ARG, "bsa_forward: NULL tensor pointer");
+  bsa::PlanGeometry g;
+  int st = check_plan(plan, &g);
+  if (st != BSA_OK) return st;
+  if (B <= 0 || H <= 0 || Sq <= 0 || Sk <= 0 || bs <= 0 || d <= 0)
+    return fail(BSA_ERR_INVALID_ARG, "bsa_forward: sizes must be positive");
+  if (H != plan->H || (int64_t)Sq != (int64_t)plan->Mb * bs || (int64_t)Sk != (int64_t)plan->Nb * bs)
+    return fail(BSA_ERR_PLAN_MISMATCH,
+                "bsa_forward: H=%d Sq=%d Sk=%d bs=%d do not match plan H=%d Mb=%d Nb=%d", H, Sq,
+                Sk, bs, plan->H, plan->Mb, plan->Nb);
+  if (dtype != BSA_BF16 && dtype != BSA_F32)
+    return fail(BSA_ERR_INVALID_ARG, "bsa_forward: unknown dtype %d", (int)dtype);
+  if (!(std::isfinite(scale) && scale > 0.f))
+    return fail(BSA_ERR_INVALID_ARG, "bsa_forward: scale must be finite and > 0");
+  if (!bsa::forward_supported(bs, d))
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_forward: no kernel for bs=%d d=%d", bs, d);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      (lse != nullptr && !aligned(lse, 4)))
+    return fail(BSA_ERR_MISALIGNED, "bsa_forward: tensors must be 16-byte aligned");
+  const int64_t work = (int64_t)B * plan->H * plan->Mb;
+  if (work > 0x7ffffff0LL) return fail(BSA_ERR_UNSUPPORTED, "bsa_forward: problem too large");
+  hipError_t e = bsa::launch_forward(
+      q, k, v, at<int32_t>(plan->dev_buf, g.off_row_ptr), at<int32_t>(plan->dev_buf, g.off_col_idx),
+      at<int32_t>(plan->dev_buf, g.off_row_order), B, plan->H, plan->Mb, plan->Nb, bs, d,
+      dtype == BSA_F32, scale, out, lse, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "bsa_forward launch");
+  return BSA_OK;
+}
+
+int topk_sparse_attn(const void *q, const void *kv, const int32_t *idx, const float *attn_sink,
+                     int32_t B, int32_t M, int32_t N, int32_t H, int32_t d, int32_t topk,
+                     float scale, void *out, void *stream) {
+  if (q == nullptr || kv == nullptr || idx == nullptr || out == nullptr)
+    return fail(BSA_ERR_INVALID_ARG, "topk_sparse_attn: NULL tensor pointer");
+  if (B <= 0 || M <= 0 || N <= 0 || H <= 0 || d <= 0 || topk <= 0)
+    return fail(BSA_ERR_INVALID_ARG, "topk_sparse_attn: sizes must be positive");
+  if (!(std::isfinite(scale) && scale > 0.f))
+    return fail(BSA_ERR_INVALID_ARG, "topk_sparse_attn: scale must be finite and > 0");
+  if (!bsa::topk_supported(H, d))
+    return fail(BSA_ERR_UNSUPPORTED, "topk_sparse_attn: no kernel for H=%d d=%d", H, d);
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 16) || !aligned(idx, 4) ||
+      (attn_sink != nullptr && !aligned(attn_sink, 4)))
+    return fail(BSA_ERR_MISALIGNED, "topk_sparse_attn: tensors must be 16-byte aligned");
+  if ((int64_t)B * M > 0x7fffffffLL)
+    return fail(BSA_ERR_UNSUPPORTED, "topk_sparse_attn: problem too large");
+  hipError_t e = bsa::launch_topk(q, kv, idx, attn_sink, B, M, N, H, d, topk, scale, out,
+                                  (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "topk_sparse_attn launch");
+  return BSA_OK;
+}
+
+const char *bsa_status_string(int status) {
+  switch (status) {
+    case BSA_OK: return "ok";
+    case BSA_ERR_INVALID_ARG: return "invalid argument";
+    case BSA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case BSA_ERR_MISALIGNED: return "misaligned pointer";
+    case BSA_ERR_PLAN_MISMATCH: return "plan does not match the call";
+    case BSA_ERR_BUFFER_TOO_SMALL: return "buffer too small";
+    case BSA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *bsa_last_error(void) { return g_last_error; }
+
+}  // extern "C"

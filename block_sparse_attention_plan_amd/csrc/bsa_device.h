@@ -1,0 +1,95 @@
+// Device-side building blocks shared by the gfx950 kernels of libbsa:
+// vector types, MFMA wrappers, bf16 packing, cross-lane reductions and the
+// LDS transpose read.  Lane layouts below were measured on gfx950.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define BSA_LDS __attribute__((address_space(3)))
+
+// D = A * B + C with 16x16x32 bf16 operands.
+// Operand layout: lane l holds row (A) / column (B) l%16 and the 8 k-values
+// 8*(l/16) .. 8*(l/16)+7.  Result: lane l holds column l%16, rows
+// 4*(l/16) + r for r = 0..3.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D = A * B + C with 32x32x16 bf16 operands.
+// Operand layout: lane l holds row (A) / column (B) l%32 and k-values
+// 8*(l/32) .. +7.  Result: lane l holds column l%32, register r holds row
+// 8*(r/4) + 4*(l/32) + r%4.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Round-to-nearest-even float -> bf16 conversion of 8 floats.
+__device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float a3,
+                                            float a4, float a5, float a6, float a7) {
+  bf16x8 r;
+  r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
+  r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
+  return r;
+}
+
+// Value of lane l ^ 16 and lane l ^ 32 combined through permlane swaps: with
+// x passed as both operands, the two results hold x of lanes {l, l^16}
+// (resp. {l, l^32}) in some order, so op(r0, r1) is the pair reduction.
+__device__ __forceinline__ float max_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// LDS transpose read of 4 bf16 values.  Inside each group of 16 lanes, lane
+// s supplies the address of a 4-element (8-byte) chunk; lane t receives
+// element t%4 of the chunks supplied by lanes 4e + t/4 (e = 0..3) of its
+// group.  With lane s = 4e' + c pointing at row (k0 + e') and columns
+// (n0 + 4c .. n0 + 4c + 3) of a row-major [k][n] tile, lane t receives
+// tile[k0 + e][n0 + t] for e = 0..3: four consecutive k of column t.
+__device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16 *lds_ptr) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BSA_LDS i16x4 *)(lds_ptr));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+}  // namespace bsa
+
+namespace bsa {
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+// D = A * B + C with 16x16x16 bf16 operands (4 k-values per lane, lane l
+// holds k = 4*(l/16) .. +3); result layout as for mfma16.
+__device__ __forceinline__ f32x4 mfma16k16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                   __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
+}
+}  // namespace bsa

@@ -1,0 +1,37 @@
+// Host-side interfaces between the C ABI layer and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bsa {
+
+// Plan buffer geometry: byte offsets of row_ptr, row_order, nnz_total, col_idx
+// and the total size.  All sections start on 256-byte boundaries.
+struct PlanGeometry {
+  size_t off_row_ptr, off_row_order, off_nnz, off_col_idx, total;
+};
+bool plan_geometry(int32_t H, int32_t Mb, int32_t Nb, PlanGeometry *g);
+
+// Largest Nb the planner handles (its per-head count histogram lives in LDS).
+constexpr int32_t kPlanMaxNb = 16384;
+
+hipError_t launch_plan(const int32_t *layout, int32_t H, int32_t Mb, int32_t Nb,
+                       int32_t *row_ptr, int32_t *row_order, int32_t *nnz_total,
+                       int32_t *col_idx, hipStream_t stream);
+
+// Returns hipErrorInvalidValue when no kernel instance matches (bs, d, f32).
+hipError_t launch_forward(const void *q, const void *k, const void *v,
+                          const int32_t *row_ptr, const int32_t *col_idx,
+                          const int32_t *row_order, int32_t B, int32_t H, int32_t Mb,
+                          int32_t Nb, int32_t bs, int32_t d, bool f32, float scale,
+                          void *out, float *lse, hipStream_t stream);
+bool forward_supported(int32_t bs, int32_t d);
+
+hipError_t launch_topk(const void *q, const void *kv, const int32_t *idx,
+                       const float *sink, int32_t B, int32_t M, int32_t N, int32_t H,
+                       int32_t d, int32_t topk, float scale, void *out,
+                       hipStream_t stream);
+bool topk_supported(int32_t H, int32_t d);
+
+}  // namespace bsa

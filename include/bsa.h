@@ -1,0 +1,164 @@
+/*
+ * bsa.h -- C ABI of libbsa.so: block-sparse attention forward and the top-k
+ * gathered sparse attention forward, for AMD Instinct MI355X (gfx950).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers marked "device" point to GPU memory owned by the caller (the
+ *   library allocates no device memory and keeps no pointer after a call
+ *   returns, except inside a caller-owned plan buffer).
+ * - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *   All compute calls are asynchronous and ordered on that stream.  Only
+ *   bsa_plan_nnz synchronises (it copies one integer to the host).
+ * - Return value: BSA_OK (0) or a negative bsa_status_t.  Host-side argument
+ *   validation runs before any HIP call, so an invalid call touches neither
+ *   the GPU nor the output buffers.  Launch failures are reported as
+ *   BSA_ERR_HIP; faults inside a kernel surface at the caller's next sync.
+ *   bsa_last_error() returns a thread-local message for the last failure.
+ * - Tensors are dense and row-major (last index fastest), with the shapes
+ *   given below.  q/k/v/kv/out must be 16-byte aligned.
+ * - Nothing throws across this boundary.
+ */
+#ifndef BSA_H_
+#define BSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BSA_OK = 0,
+  BSA_ERR_INVALID_ARG = -1,     /* null pointer, non-positive size, bad scale */
+  BSA_ERR_UNSUPPORTED = -2,     /* shape or dtype with no compiled kernel */
+  BSA_ERR_MISALIGNED = -3,      /* pointer not 16-byte aligned */
+  BSA_ERR_PLAN_MISMATCH = -4,   /* plan dims do not match the call */
+  BSA_ERR_BUFFER_TOO_SMALL = -5,/* plan buffer smaller than bsa_plan_buffer_bytes */
+  BSA_ERR_HIP = -6              /* a HIP runtime call or launch failed */
+} bsa_status_t;
+
+typedef enum { BSA_BF16 = 0, BSA_F32 = 1 } bsa_dtype_t;
+
+/*
+ * A plan: a host-side value that describes a caller-owned device buffer
+ * holding the per-row CSR of a block layout.  Filled by bsa_plan; immutable
+ * afterwards; valid for any batch size (the layout has no batch axis) and
+ * reusable across calls until the caller frees the buffer.
+ *
+ * Rows are r = h * Mb + m.  Buffer sections (each starting on a 256-byte
+ * boundary, offsets returned by bsa_plan_sections):
+ *   row_ptr   int32 [H*Mb + 1]  exclusive prefix sum of per-row live counts
+ *   row_order int32 [H*Mb]      rows head by head; inside a head by live
+ *                               count descending, ties by m ascending
+ *   nnz_total int32 [1]         number of live tiles (= row_ptr[H*Mb])
+ *   col_idx   int32 [H*Mb*Nb]   live block columns of each row, ascending;
+ *                               only the first nnz_total entries are written
+ */
+typedef struct {
+  int32_t H, Mb, Nb;
+  int32_t reserved;
+  void *dev_buf;
+  size_t dev_bytes;
+} bsa_plan_t;
+
+/* Bytes a plan buffer needs for an [H, Mb, Nb] layout (worst case: every
+ * tile live).  Returns 0 if a dimension is non-positive or H*Mb*Nb >= 2^31. */
+size_t bsa_plan_buffer_bytes(int32_t H, int32_t Mb, int32_t Nb);
+
+/* Byte offsets of the four plan sections inside the plan buffer
+ * (row_ptr, row_order, nnz_total, col_idx).  Host-only; returns
+ * BSA_ERR_INVALID_ARG for bad dimensions or a null output pointer. */
+int bsa_plan_sections(int32_t H, int32_t Mb, int32_t Nb, size_t offsets_out[4]);
+
+/*
+ * Build the plan of a block layout.
+ *
+ * Operation: the layout (DeepSpeed sparse-attention utils page, "I/O
+ * Contract") is an int32 tensor [H, Mb, Nb] in which a non-zero entry marks a
+ * live b x b tile of Q K^T.  Storing only the live tiles with their column
+ * indices is the CSR form of the next.gr "Block Sparse Attention Techniques"
+ * tutorial, section 3.2.  Per-row counts, their prefix scan and the per-row
+ * column lists follow from it; row_order adds the load-balance order.
+ *
+ *   layout    device, int32 [H, Mb, Nb], read only
+ *   dev_buf   device, caller-owned, >= bsa_plan_buffer_bytes(H, Mb, Nb) bytes,
+ *             256-byte aligned; overwritten
+ *   plan_out  host, filled on success
+ * Errors: BSA_ERR_INVALID_ARG (null pointers, dims <= 0 or H*Mb*Nb >= 2^31),
+ * BSA_ERR_MISALIGNED (dev_buf not 256-byte aligned), BSA_ERR_BUFFER_TOO_SMALL,
+ * BSA_ERR_HIP.
+ */
+int bsa_plan(const int32_t *layout, int32_t H, int32_t Mb, int32_t Nb,
+             void *dev_buf, size_t dev_bytes, bsa_plan_t *plan_out, void *stream);
+
+/* Copy nnz_total of a built plan to the host; synchronises `stream`. */
+int bsa_plan_nnz(const bsa_plan_t *plan, int64_t *nnz_host, void *stream);
+
+/*
+ * Block-sparse attention forward.
+ *
+ * Operation: for batch b, head h and query token i (query block m = i / bs),
+ *   s_ij = scale * sum_d q[b,h,i,d] k[b,h,j,d]  over key tokens j of the live
+ *          tiles (h, m, n) of the plan, -inf elsewhere;
+ *   out[b,h,i,:] = sum_j softmax_j(s_i.) v[b,h,j,:];
+ *   lse[b,h,i]   = log(sum_j exp(s_ij))  (natural log).
+ * This is the scaled dot-product attention of the next.gr tutorial
+ * (section 1) with the -inf masking of its Longformer formula, restricted to
+ * the live tiles, each tile being a dense b x b piece of work (Language AI
+ * Handbook, "Block Structure").  A row whose block row has no live tile gets
+ * out = 0 and lse = -inf.  Tiles are computed with bf16 products and fp32
+ * accumulation; fp32 inputs (BSA_F32) are rounded to bf16 (nearest-even) on
+ * load and written back as fp32.
+ *
+ *   q     device [B, H, Sq, d] of dtype
+ *   k, v  device [B, H, Sk, d] of dtype
+ *   plan  host pointer to a plan built for this layout; H must equal plan->H,
+ *         Sq must equal plan->Mb * bs and Sk plan->Nb * bs, otherwise the call
+ *         returns BSA_ERR_PLAN_MISMATCH
+ *   bs    block size: 16, 32, 64 or 128;   d: 32, 64 or 128
+ *   scale finite and > 0 (the Python binding defaults it to 1/sqrt(d))
+ *   out   device [B, H, Sq, d] of dtype, written
+ *   lse   device fp32 [B, H, Sq], written; may be NULL
+ * Errors: BSA_ERR_INVALID_ARG, BSA_ERR_UNSUPPORTED, BSA_ERR_MISALIGNED,
+ * BSA_ERR_PLAN_MISMATCH, BSA_ERR_HIP.
+ */
+int bsa_forward(const void *q, const void *k, const void *v, const bsa_plan_t *plan,
+                int32_t B, int32_t H, int32_t Sq, int32_t Sk, int32_t bs, int32_t d,
+                bsa_dtype_t dtype, float scale, void *out, float *lse, void *stream);
+
+/*
+ * Top-k gathered sparse attention forward with a per-head attention sink.
+ *
+ * Operation (DeepSeek-V4.1 "Sparse attention / Weighted row sum" page,
+ * sparse_attn_kernel and sparse_attn): for batch b and query position m, the
+ * valid slots t (idx[b,m,t] != -1) name rows of kv, the same rows for every
+ * head; for head h
+ *   s_t   = scale * q[b,m,h,:] . kv[b, idx[b,m,t], :]
+ *   out   = sum_t exp(s_t) kv[b, idx_t, :] / (sum_t exp(s_t) + exp(sink_h))
+ * The sink is an unscaled fp32 logit (NULL: no sink term).  A position with
+ * no valid slot gets out = 0.  Indices outside [0, N) are treated like -1.
+ *
+ *   q     device bf16 [B, M, H, d];  kv device bf16 [B, N, d]
+ *   idx   device int32 [B, M, topk]; attn_sink device fp32 [H] or NULL
+ *   H in [1, 64]; d = 512; topk >= 1 (no alignment needed)
+ *   out   device bf16 [B, M, H, d], written
+ * Errors: BSA_ERR_INVALID_ARG, BSA_ERR_UNSUPPORTED, BSA_ERR_MISALIGNED,
+ * BSA_ERR_HIP.
+ */
+int topk_sparse_attn(const void *q, const void *kv, const int32_t *idx,
+                     const float *attn_sink, int32_t B, int32_t M, int32_t N,
+                     int32_t H, int32_t d, int32_t topk, float scale, void *out,
+                     void *stream);
+
+/* Static text for a status code. */
+const char *bsa_status_string(int status);
+
+/* Thread-local text describing the last failed call on this thread. */
+const char *bsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BSA_H_ */

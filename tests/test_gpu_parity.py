@@ -1,0 +1,242 @@
+"""GPU parity: libbsa (through the C ABI) against the fp64 CPU oracle.
+
+Plans must match bit for bit.  Attention outputs must be within max-abs
+1.5e-2 and mean-abs 2e-3 of the oracle (bf16 I/O, fp32 accumulation), lse
+within 1e-3 where finite and exactly -inf for rows without a live tile.
+Inputs are the seeded synthetic workloads; at full size the oracle checks a
+sample of row blocks / positions, always including the heaviest and the
+lightest rows.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_plan_amd as bsa
+from block_sparse_attention_plan_amd import workloads as W
+from oracle import bsa_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 1.5e-2
+MEAN_ABS = 2e-3
+LSE_ABS = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check_plan(dev, layout: np.ndarray):
+    ref = O.plan(layout)
+    p = bsa.bsa_plan(torch.from_numpy(np.ascontiguousarray(layout, dtype=np.int32)).to(dev))
+    nnz = p.nnz()
+    assert nnz == ref.nnz_total
+    assert torch.equal(p.row_ptr.cpu(), torch.from_numpy(ref.row_ptr))
+    assert torch.equal(p.row_order.cpu(), torch.from_numpy(ref.row_order))
+    assert torch.equal(p.col_idx(nnz).cpu(), torch.from_numpy(ref.col_idx))
+    return p, ref
+
+
+def compare(out_gpu: np.ndarray, out_ref: np.ndarray, what: str):
+    assert np.isfinite(out_gpu).all(), f"{what}: non-finite output"
+    err = np.abs(out_gpu - out_ref)
+    say(f"  {what}: max_abs={err.max():.3e} mean_abs={err.mean():.3e}")
+    assert err.max() <= MAX_ABS, what
+    assert err.mean() <= MEAN_ABS, what
+
+
+def bf16_rounded(t: torch.Tensor) -> np.ndarray:
+    """fp32 inputs as the kernel multiplies them: rounded to bf16 on load."""
+    return to64(t.to(torch.bfloat16))
+
+
+def compare_lse(lse_gpu: np.ndarray, lse_ref: np.ndarray, what: str):
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse_gpu), empty), f"{what}: -inf pattern differs"
+    fin = ~empty
+    if fin.any():
+        err = np.abs(lse_gpu[fin] - lse_ref[fin]).max()
+        say(f"  {what}: lse max_abs={err:.3e}")
+        assert err <= LSE_ABS
+
+
+# ------------------------------------------------------------------ planner
+
+@pytest.mark.parametrize("case", [
+    ("empty", (2, 3, 5), 0.0), ("full", (1, 4, 4), 1.0), ("one_col", (3, 70, 1), 0.5),
+    ("wide", (2, 5, 200), 0.2), ("tall", (2, 300, 40), 0.15), ("ragged", (4, 33, 65), 0.4),
+    ("square", (8, 64, 64), 0.1)])
+def test_plan_random_layouts(gpu, case):
+    name, (H, Mb, Nb), p = case
+    say(f"[plan] {name} H={H} Mb={Mb} Nb={Nb} p={p}")
+    rng = np.random.default_rng(hash(name) % 2**32)
+    lay = (rng.random((H, Mb, Nb)) < p).astype(np.int32) * rng.integers(1, 4, (H, Mb, Nb)).astype(np.int32)
+    check_plan(gpu, lay)
+
+
+@pytest.mark.parametrize("name", [n for n, s in W.WORKLOADS.items() if s["kind"] == "bsa"])
+def test_plan_workload_layouts(gpu, name):
+    spec = W.WORKLOADS[name]
+    nb = spec["S"] // spec["bs"]
+    H = spec["H"]
+    say(f"[plan] workload {name} H={H} nb={nb}")
+    if spec["layout"] == "band":
+        lay = W.band_layout(H, nb, spec["w"])
+    elif spec["layout"] == "causal_lgs":
+        lay = W.causal_lgs_layout(H, nb, spec["window"], spec["n_global"], spec["stride"])
+    else:
+        lay = W.causal_bernoulli_layout(H, nb, spec["p"], np.random.default_rng(spec["seed"]))
+    check_plan(gpu, lay)
+
+
+# ------------------------------------------------------- block-sparse forward
+
+SMALL_CASES = []
+for bs_ in (16, 32, 64, 128):
+    for d_ in (32, 64, 128):
+        SMALL_CASES.append((bs_, d_, "bf16"))
+SMALL_CASES += [(16, 32, "f32"), (64, 128, "f32"), (128, 64, "f32")]
+
+
+@pytest.mark.parametrize("bs,d,dtype", SMALL_CASES)
+def test_forward_small_all_rows(gpu, bs, d, dtype):
+    """Several tiles per row with ragged per-row counts, an empty block row,
+    a non-square block grid; every output row is checked."""
+    Mb, Nb, H, B = 5, 7, 3, 2
+    rng = np.random.default_rng(bs * 1000 + d)
+    lay = (rng.random((H, Mb, Nb)) < 0.45).astype(np.int32)
+    lay[0, 3, :] = 0          # empty block row
+    lay[1, 0, :] = 1          # full row
+    lay[2, :, 6] = 1
+    x = W.make_bsa("small", B=B, H=H, S=Mb * bs, Sk=Nb * bs, bs=bs, d=d, dtype=dtype,
+                   layout="given", layout_array=lay, seed=bs + d)
+    say(f"[forward] small bs={bs} d={d} {dtype}")
+    plan, _ = check_plan(gpu, lay)
+    q, k, v = (t.to(gpu) for t in (x.q, x.k, x.v))
+    out, lse = bsa.bsa_forward(q, k, v, plan, x.scale)
+    torch.cuda.synchronize()
+    ref, ref_lse = O.attention_live_tiles(to64(x.q), to64(x.k), to64(x.v), lay, bs, x.scale)
+    compare(to64(out), ref, f"bs={bs} d={d} {dtype}")
+    if dtype == "f32":
+        # lse is compared with the oracle on the bf16-rounded values the
+        # kernel multiplies (fp32 I/O rounds tiles to bf16 on load).
+        _, ref_lse = O.attention_live_tiles(bf16_rounded(x.q), bf16_rounded(x.k),
+                                            bf16_rounded(x.v), lay, bs, x.scale)
+    compare_lse(lse.cpu().numpy(), ref_lse, f"bs={bs} d={d}")
+    assert torch.all(out[0, 0, 3 * bs:4 * bs] == 0)
+
+
+def test_forward_all_empty_layout(gpu):
+    lay = np.zeros((2, 3, 3), np.int32)
+    x = W.make_bsa("empty", B=1, H=2, S=48, bs=16, d=32, dtype="bf16", layout="given",
+                   layout_array=lay, seed=9)
+    say("[forward] all-empty layout")
+    plan, _ = check_plan(gpu, lay)
+    out, lse = bsa.bsa_forward(x.q.to(gpu), x.k.to(gpu), x.v.to(gpu), plan)
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+def _sample_row_blocks(layout, B, k, rng):
+    H, Mb, _ = layout.shape
+    nnz = (layout != 0).sum(-1)
+    picks = set()
+    for b in range(B):
+        h, m = np.unravel_index(np.argmax(nnz), nnz.shape)
+        picks.add((b, int(h), int(m)))
+        h, m = np.unravel_index(np.argmin(nnz), nnz.shape)
+        picks.add((b, int(h), int(m)))
+    while len(picks) < k:
+        picks.add((int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(Mb))))
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("name", [n for n, s in W.WORKLOADS.items() if s["kind"] == "bsa"])
+def test_forward_full_workloads(gpu, name):
+    """Full-size workloads in the launch configuration the benchmark times;
+    the oracle checks all rows of the two small workloads and a sample of
+    row blocks of the large ones.  Two runs must agree bit for bit."""
+    say(f"[forward] full workload {name}: generating inputs")
+    x = W.make_workload(name)
+    B = x.q.shape[0]
+    plan, _ = check_plan(gpu, x.layout)
+    q, k, v = (t.to(gpu) for t in (x.q, x.k, x.v))
+    say(f"[forward] full workload {name}: launching")
+    out, lse = bsa.bsa_forward(q, k, v, plan, x.scale)
+    out2, lse2 = bsa.bsa_forward(q, k, v, plan, x.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2), "forward is not deterministic"
+    nrows = B * x.layout.shape[0] * x.layout.shape[1]
+    rows = None if nrows <= 1024 else _sample_row_blocks(x.layout, B, 48, np.random.default_rng(0))
+    ref, ref_lse = O.attention_live_tiles(to64(x.q), to64(x.k), to64(x.v), x.layout, x.bs,
+                                          x.scale, row_blocks=rows)
+    if rows is None:
+        compare(to64(out), ref, name)
+        if x.q.dtype == torch.float32:
+            _, ref_lse = O.attention_live_tiles(bf16_rounded(x.q), bf16_rounded(x.k),
+                                                bf16_rounded(x.v), x.layout, x.bs, x.scale)
+        compare_lse(lse.cpu().numpy(), ref_lse, name)
+    else:
+        bs = x.bs
+        sel_o = np.concatenate([to64(out[b, h, m * bs:(m + 1) * bs]) for b, h, m in rows])
+        sel_r = np.concatenate([ref[b, h, m * bs:(m + 1) * bs] for b, h, m in rows])
+        compare(sel_o, sel_r, f"{name} ({len(rows)} sampled row blocks)")
+        sel_l = np.concatenate([lse[b, h, m * bs:(m + 1) * bs].cpu().numpy() for b, h, m in rows])
+        sel_rl = np.concatenate([ref_lse[b, h, m * bs:(m + 1) * bs] for b, h, m in rows])
+        compare_lse(sel_l, sel_rl, name)
+
+
+# ------------------------------------------------------------------- top-k
+
+TOPK_CASES = [
+    # H, topk, N, with_sink, drop
+    (64, 200, 300, True, 0.05),
+    (64, 64, 100, False, 0.0),
+    (16, 65, 80, True, 0.3),
+    (5, 1, 10, True, 0.0),
+    (1, 130, 500, False, 0.1),
+    (37, 127, 127, True, 0.5),
+]
+
+
+@pytest.mark.parametrize("H,topk,N,with_sink,drop", TOPK_CASES)
+def test_topk_small(gpu, H, topk, N, with_sink, drop):
+    say(f"[topk] small H={H} topk={topk} N={N} sink={with_sink} drop={drop}")
+    x = W.make_topk("topk_small", B=2, M=6, H=H, d=512, N=N, topk=topk, seed=H + topk,
+                    drop=drop, with_sink=with_sink)
+    idx = x.idx.clone()
+    idx[1, 4] = -1            # a position with no valid slot
+    out = bsa.topk_sparse_attn(x.q.to(gpu), x.kv.to(gpu), idx.to(gpu),
+                               x.sink.to(gpu) if x.sink is not None else None, x.scale)
+    torch.cuda.synchronize()
+    ref = O.topk_attention(to64(x.q), to64(x.kv), idx.numpy(),
+                           x.sink.numpy() if x.sink is not None else None, x.scale)
+    compare(to64(out), ref, f"topk H={H} topk={topk}")
+    assert torch.all(out[1, 4] == 0)
+
+
+def test_topk_full_workload(gpu):
+    name = "topk2048_m4096_h64_d512_n8192"
+    say(f"[topk] full workload {name}: generating inputs")
+    x = W.make_workload(name)
+    q, kv, idx, sink = x.q.to(gpu), x.kv.to(gpu), x.idx.to(gpu), x.sink.to(gpu)
+    say(f"[topk] full workload {name}: launching")
+    out = bsa.topk_sparse_attn(q, kv, idx, sink, x.scale)
+    out2 = bsa.topk_sparse_attn(q, kv, idx, sink, x.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "top-k is not deterministic"
+    rng = np.random.default_rng(1)
+    M = x.q.shape[1]
+    pos = sorted(set([(0, 0), (0, M - 1)] + [(0, int(m)) for m in rng.integers(0, M, 30)]))
+    ref = O.topk_attention(to64(x.q), to64(x.kv), x.idx.numpy(), x.sink.numpy(), x.scale,
+                           positions=pos)
+    sel_o = np.stack([to64(out[b, m]) for b, m in pos])
+    sel_r = np.stack([ref[b, m] for b, m in pos])
+    compare(sel_o, sel_r, f"{name} ({len(pos)} sampled positions)")
