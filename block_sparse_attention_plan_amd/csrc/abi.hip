@@ -4,7 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 
-#include "../../include/bsa.h"
+#include "bsa.h"
 #include "bsa_internal.h"
 
 namespace {

@@ -14,16 +14,21 @@
 // the eight XCDs receives one contiguous stretch of that order: consecutive
 // workgroup ids go round-robin over the XCDs, so item = (id % 8) * per + id / 8.
 //
-// Inside a workgroup of bs/16 waves, wave w owns query rows 16w .. 16w+15 of
-// the block.  For each live tile the K and V tiles are staged row-major in LDS
-// (prefetched into registers one tile ahead), then every wave computes
-//   S^T = K Q^T        (16x16x32 MFMA; Q^T stays in registers)
-//   online softmax     (lane owns one query column; exp2 with the scale and
-//                       log2(e) folded into one multiply-add)
-//   O^T += V^T P^T     (16x16x32 MFMA; P^T straight from the S^T registers,
-//                       V^T read from the row-major V tile by LDS transpose
-//                       reads)
-// so no score matrix ever leaves registers.
+// Every variant computes, per live tile, S^T = K Q^T with Q^T resident in
+// registers as the MFMA B operand, an online softmax in which each lane owns
+// one query column (exp2 with scale*log2(e) folded into one multiply-add),
+// and O^T += V^T P^T with P^T taken straight from the S^T accumulators (the
+// k-slot order of the accumulator layout is the contraction order) and V^T
+// read from a row-major V tile by LDS transpose reads.  No score matrix ever
+// leaves registers.  Variants:
+//   bsa_fwd_kernel      bs = 16: 16 query rows per wave, 16x16x32 MFMA
+//   bsa_fwd32_kernel    bs = 32 and fp32 I/O: 32 rows per wave, 32x32x16 MFMA,
+//                       register-staged tiles, two key halves per row group
+//                       when bs >= 64
+//   bsa_fwd_dma_kernel  bf16, bs >= 64: as above with tiles copied from HBM
+//                       straight into double-buffered, XOR-swizzled LDS
+#include <type_traits>
+
 #include "bsa_device.h"
 #include "bsa_internal.h"
 
@@ -33,6 +38,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kMaxFloor = -1e30f;
+constexpr float kLazy = 8.0f;  // tolerated staleness of the running max (log2 units)
 
 template <typename T> struct Io;
 template <> struct Io<__bf16> {
@@ -225,6 +231,512 @@ bsa_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__rest
   if (lh && G == 0) lh[i_row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
 }
 
+
+// Variant for bs >= 32: each wave owns 32 query rows and uses the 32x32x16
+// MFMA, which halves the LDS operand traffic per FLOP of the 16-row layout.
+// With KSPLIT = 2 (bs >= 64) the workgroup holds two waves per 32-row group:
+// wave (g, s) handles keys [s*bs/2, (s+1)*bs/2) of every live tile for rows
+// 32g .. 32g+31 with its own running max / sum / output, and the two partial
+// results are merged once at the end (the split-softmax identity
+// O = (a1 O1 + a2 O2) / (a1 l1 + a2 l2), a_k = exp(m_k - max(m1, m2))).  Two
+// waves per SIMD let one wave's softmax overlap the other's MFMA work.
+//   S^T[j][i]: lane column i = lane%32; key rows 8*(r/4) + 4*(lane/32) + r%4
+//   P^T operand for 16 keys: registers r = 8c .. 8c+7 of one 32-key block
+//   O^T[d][i]: the same result layout over d
+template <int BS, int D, typename T, int KSPLIT>
+__global__ void __launch_bounds__(BS * 2 * KSPLIT) __attribute__((amdgpu_waves_per_eu(2)))
+bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+                 const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
+                 const int32_t *__restrict__ row_order, int32_t B, int32_t H, int32_t Mb,
+                 int32_t Nb, float scale_log2, T *__restrict__ out, float *__restrict__ lse) {
+  constexpr int NRG = BS / 32;           // 32-row groups
+  constexpr int NW = NRG * KSPLIT;       // waves per workgroup
+  constexpr int NT = NW * 64;            // threads per workgroup
+  constexpr int KW = BS / KSPLIT;        // keys per wave per tile
+  constexpr int KSTR = D + 8;            // LDS row stride (elements) of the K tile
+  constexpr int VSTR = D + 16;           // LDS row stride of the V tile
+  constexpr int CPT = (BS * D / 8) / NT; // 8-element chunks per thread per tile
+  constexpr int QC = D / 16;             // 16-wide k chunks of the QK^T contraction
+  constexpr int JT = KW / 32;            // 32-key blocks per wave per tile
+  constexpr int DT = D / 32;             // 32-wide d blocks of the output
+  static_assert(CPT * NT * 8 == BS * D, "tile must split evenly over threads");
+  static_assert(JT >= 1, "each wave needs at least 32 keys per tile");
+  // merge scratch (fp32): per row group DT*16*64 output values + 2*64 (m, l)
+  constexpr int MRG = DT * 16 * 64 + 128;
+  static_assert(KSPLIT == 1 || (size_t)NRG * MRG * 4 <= (size_t)BS * (KSTR + VSTR) * 4,
+                "merge scratch must fit in the tile buffers");
+
+  // one LDS block: two K tiles, then two V tiles; reused as merge scratch
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * BS * (KSTR + VSTR)];
+  __bf16 *const Kbuf0 = smem;
+  __bf16 *const Vbuf0 = smem + 2 * BS * KSTR;
+
+  const int64_t W = (int64_t)B * H * Mb;
+  const int64_t per = (W + 7) / 8;
+  const int64_t w = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (w >= W) return;
+  const int64_t HM = (int64_t)H * Mb;
+  const int b = (int)(w / HM);
+  const int r = row_order[w % HM];
+  const int h = r / Mb;
+  const int m = r % Mb;
+  const int beg = row_ptr[r];
+  const int end = row_ptr[r + 1];
+
+  const int tid = threadIdx.x;
+  const int wid = tid / 64;
+  const int rg = wid % NRG;     // row group
+  const int ks = wid / NRG;     // key half
+  const int lane = tid % 64;
+  const int h2 = lane / 32;     // half of the wave: selects k-slots 8*h2 .. 8*h2+7
+  const int l32 = lane % 32;    // query column owned by this lane
+  const int G = lane / 16;      // 16-lane group (transpose reads)
+  const int l16 = lane % 16;
+
+  const int64_t bh = (int64_t)b * H + h;
+  const int64_t Sq = (int64_t)Mb * BS, Sk = (int64_t)Nb * BS;
+  const T *qh = q + bh * Sq * D;
+  const T *kh = k + bh * Sk * D;
+  const T *vh = v + bh * Sk * D;
+  T *oh = out + bh * Sq * D;
+  float *lh = lse ? lse + bh * Sq : nullptr;
+  const int64_t i_row = (int64_t)m * BS + 32 * rg + l32;
+
+  if (beg == end) {
+    if (ks == 0) {
+      for (int dt = 0; dt < DT; ++dt)
+        for (int a = 0; a < 4; ++a) Io<T>::store_zero4(oh + i_row * D + 32 * dt + 8 * a + 4 * h2);
+      if (lh && h2 == 0) lh[i_row] = -__builtin_inff();
+    }
+    return;
+  }
+
+  bf16x8 qf[QC];
+#pragma unroll
+  for (int c = 0; c < QC; ++c) qf[c] = Io<T>::load8(qh + i_row * D + 16 * c + 8 * h2);
+
+  // Register staging of one K tile and one V tile (16-byte pieces).
+  bf16x8 kr[CPT], vr[CPT];
+  auto load_k = [&](int n) {
+    const T *src = kh + (int64_t)n * BS * D;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int qid = c * NT + tid;
+      kr[c] = Io<T>::load8(src + (qid / (D / 8)) * D + (qid % (D / 8)) * 8);
+    }
+  };
+  auto load_v = [&](int n) {
+    const T *src = vh + (int64_t)n * BS * D;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int qid = c * NT + tid;
+      vr[c] = Io<T>::load8(src + (qid / (D / 8)) * D + (qid % (D / 8)) * 8);
+    }
+  };
+  auto store_k = [&](int buf) {
+    __bf16 *dst = Kbuf0 + buf * BS * KSTR;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int qid = c * NT + tid;
+      *reinterpret_cast<bf16x8 *>(&dst[(qid / (D / 8)) * KSTR + (qid % (D / 8)) * 8]) = kr[c];
+    }
+  };
+  auto store_v = [&](int buf) {
+    __bf16 *dst = Vbuf0 + buf * BS * VSTR;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int qid = c * NT + tid;
+      *reinterpret_cast<bf16x8 *>(&dst[(qid / (D / 8)) * VSTR + (qid % (D / 8)) * 8]) = vr[c];
+    }
+  };
+
+  const int key0 = ks * KW;
+  const int e_src = l16 / 4, c_src = l16 % 4;
+  const int koff = (key0 + l32) * KSTR + 8 * h2;
+  const int voff = (key0 + 4 * h2 + e_src) * VSTR + 16 * (G % 2) + 4 * c_src;
+
+  // S^T of this wave's keys of the tile held in K buffer `buf`.
+  auto qk = [&](int buf, f32x16 (&s)[JT]) {
+    const __bf16 *ksrc = Kbuf0 + buf * BS * KSTR + koff;
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) {
+      s[jt] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < QC; ++c) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(ksrc + 32 * jt * KSTR + 16 * c);
+        s[jt] = mfma32(a, qf[c], s[jt]);
+      }
+    }
+  };
+
+  float m_run = kMaxFloor;  // running max (log2 units); may lag the true max by < kLazy
+  float l_run = 0.f;
+  f32x16 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
+
+  // Online softmax of one tile's scores and the P V product from V buffer
+  // `buf`.  The running max is raised only when a score exceeds it by more
+  // than kLazy (log2 units): the shift cancels in out = O / l, so a stale max
+  // is exact, and the rescale of O is skipped for most tiles.
+  auto softmax_pv = [&](f32x16 (&s)[JT], int buf) {
+    float mx = s[0][0];
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[jt][e]);
+    mx = max_xor32(mx) * scale_log2;
+    if (__any(mx > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pe = fast_exp2(fmaf(s[jt][e], scale_log2, -m_run));
+        s[jt][e] = pe;
+        psum += pe;
+      }
+    l_run += psum;
+    const __bf16 *vsrc = Vbuf0 + buf * BS * VSTR + voff;
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const bf16x8 pf = to_bf16x8(s[jt][8 * c2 + 0], s[jt][8 * c2 + 1], s[jt][8 * c2 + 2],
+                                    s[jt][8 * c2 + 3], s[jt][8 * c2 + 4], s[jt][8 * c2 + 5],
+                                    s[jt][8 * c2 + 6], s[jt][8 * c2 + 7]);
+        // k-slots: keys 32jt + 16c2 + 4*h2 + e and 32jt + 16c2 + 8 + 4*h2 + e
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const __bf16 *src = vsrc + (32 * jt + 16 * c2) * VSTR + 32 * dt;
+          const bf16x8 a = cat4(lds_read_tr4(src), lds_read_tr4(src + 8 * VSTR));
+          o[dt] = mfma32(a, pf, o[dt]);
+        }
+      }
+  };
+
+  // Software pipeline over the row's live tiles u = 0 .. n-1 (tile u is
+  // column col_idx[beg + u]).  Tile u's K sits in K buffer u % 2, its V in V
+  // buffer u % 2.  At the top of iteration t: K_{t+1} and V_t are in LDS,
+  // S_t is in registers, K_{t+2} and V_{t+1} are in the staging registers.
+  // One barrier per tile; the QK^T of tile t+1 is independent of the
+  // softmax of tile t, so their MFMA and VALU work can interleave.
+  const int n = end - beg;
+  const int32_t *cols = col_idx + beg;
+  f32x16 s_cur[JT], s_next[JT];
+  load_k(cols[0]);
+  load_v(cols[0]);
+  store_k(0);
+  store_v(0);
+  if (n > 1) {
+    load_k(cols[1]);
+    store_k(1);
+  }
+  __syncthreads();
+  qk(0, s_cur);
+  if (n > 2) load_k(cols[2]);
+  if (n > 1) load_v(cols[1]);
+  // Steady state without branches: staging of tiles past the end re-loads
+  // the last tile into a buffer that is never read again, which keeps the
+  // QK^T of the next tile and the softmax of this one in one basic block.
+  for (int t = 0; t + 1 < n; ++t) {
+    __syncthreads();  // iteration t-1 is done with K buffer t%2 and V buffer (t+1)%2
+    store_k(t & 1);
+    store_v((t + 1) & 1);
+    load_k(cols[min(t + 3, n - 1)]);
+    load_v(cols[min(t + 2, n - 1)]);
+    qk((t + 1) & 1, s_next);
+    softmax_pv(s_cur, t & 1);
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) s_cur[jt] = s_next[jt];
+  }
+  __syncthreads();
+  softmax_pv(s_cur, (n - 1) & 1);
+
+  float l_tot = sum_xor32(l_run);
+  if constexpr (KSPLIT == 2) {
+    // Merge the two key halves of each row group through LDS.
+    float *mrg = reinterpret_cast<float *>(smem) + rg * MRG;
+    __syncthreads();  // every wave is done with the tile buffers
+    if (ks == 1) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mrg[(dt * 16 + e) * 64 + lane] = o[dt][e];
+      mrg[DT * 16 * 64 + lane] = m_run;
+      mrg[DT * 16 * 64 + 64 + lane] = l_tot;
+    }
+    __syncthreads();
+    if (ks == 1) return;
+    const float m2 = mrg[DT * 16 * 64 + lane];
+    const float l2 = mrg[DT * 16 * 64 + 64 + lane];
+    const float mm = fmaxf(m_run, m2);
+    const float a1 = fast_exp2(m_run - mm), a2 = fast_exp2(m2 - mm);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[dt][e] = o[dt][e] * a1 + mrg[(dt * 16 + e) * 64 + lane] * a2;
+    l_tot = l_tot * a1 + l2 * a2;
+    m_run = mm;
+  }
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      Io<T>::store4(oh + i_row * D + 32 * dt + 8 * a + 4 * h2,
+                    f32x4{o[dt][4 * a], o[dt][4 * a + 1], o[dt][4 * a + 2], o[dt][4 * a + 3]} * inv);
+  if (lh && h2 == 0) lh[i_row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
+}
+
+// bf16 variant for bs >= 64 whose K and V tiles travel from global memory
+// straight into LDS (global_load_lds_dwordx4: lane l of a wave instruction
+// writes bytes 16l .. 16l+15 of a 1 KiB LDS span), so no staging registers
+// or LDS store instructions sit in the loop.  Rows are unpadded; 16-byte
+// chunks are XOR-swizzled per row so that both read patterns are free of
+// bank conflicts:
+//   K (b128 reads, 16 consecutive rows per phase): chunk ^ (row % CPR)
+//   V (transpose reads, 4 rows x 64 B per half-wave): chunk ^ 4*f(row)
+// The work split, MFMA layouts and software pipeline match bsa_fwd32_kernel.
+template <int D> struct VSwz {
+  static __device__ __forceinline__ int f(int row) {
+    if constexpr (D == 128) return 4 * (row & 3);
+    else if constexpr (D == 64) return 4 * ((row >> 1) & 1);
+    else return 0;
+  }
+};
+
+template <int BS, int D>
+__global__ void __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2)))
+bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
+                   const __bf16 *__restrict__ v, const int32_t *__restrict__ row_ptr,
+                   const int32_t *__restrict__ col_idx, const int32_t *__restrict__ row_order,
+                   int32_t B, int32_t H, int32_t Mb, int32_t Nb, float scale_log2,
+                   __bf16 *__restrict__ out, float *__restrict__ lse) {
+  constexpr int NRG = BS / 32;           // 32-row groups
+  constexpr int NW = NRG * 2;            // waves per workgroup (two key halves)
+  constexpr int KW = BS / 2;             // keys per wave per tile
+  constexpr int CPR = D / 8;             // 16-byte chunks per row
+  constexpr int TILE = BS * D;           // elements per K or V tile
+  constexpr int NI = TILE * 2 / 1024;    // 1 KiB load instructions per tile
+  constexpr int IPW = NI / NW;           // load instructions per wave per tile
+  constexpr int RPI = 64 / CPR;          // rows per load instruction
+  constexpr int QC = D / 16;
+  constexpr int JT = KW / 32;
+  constexpr int DT = D / 32;
+  constexpr int MRG = DT * 16 * 64 + 128;
+  static_assert(NI % NW == 0 && IPW >= 1, "tile loads must split evenly over waves");
+  static_assert(NW % 4 == 0 || CPR <= RPI, "per-wave K swizzle must be lane-constant");
+  static_assert((size_t)NRG * MRG * 4 <= (size_t)4 * TILE * 2, "merge scratch must fit");
+
+  __shared__ __attribute__((aligned(1024))) __bf16 smem[4 * TILE];  // K0 K1 V0 V1
+  __bf16 *const Kbuf0 = smem;
+  __bf16 *const Vbuf0 = smem + 2 * TILE;
+
+  const int64_t W = (int64_t)B * H * Mb;
+  const int64_t per = (W + 7) / 8;
+  const int64_t w = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (w >= W) return;
+  const int64_t HM = (int64_t)H * Mb;
+  const int b = (int)(w / HM);
+  const int r = row_order[w % HM];
+  const int h = r / Mb;
+  const int m = r % Mb;
+  const int beg = row_ptr[r];
+  const int end = row_ptr[r + 1];
+
+  const int tid = threadIdx.x;
+  const int wid = tid / 64;
+  const int rg = wid % NRG;
+  const int ks = wid / NRG;
+  const int lane = tid % 64;
+  const int h2 = lane / 32;
+  const int l32 = lane % 32;
+  const int G = lane / 16;
+  const int l16 = lane % 16;
+
+  const int64_t bh = (int64_t)b * H + h;
+  const int64_t Sq = (int64_t)Mb * BS, Sk = (int64_t)Nb * BS;
+  const __bf16 *qh = q + bh * Sq * D;
+  const __bf16 *kh = k + bh * Sk * D;
+  const __bf16 *vh = v + bh * Sk * D;
+  __bf16 *oh = out + bh * Sq * D;
+  float *lh = lse ? lse + bh * Sq : nullptr;
+  const int64_t i_row = (int64_t)m * BS + 32 * rg + l32;
+
+  if (beg == end) {
+    if (ks == 0) {
+      for (int dt = 0; dt < DT; ++dt)
+        for (int a = 0; a < 4; ++a) Io<__bf16>::store_zero4(oh + i_row * D + 32 * dt + 8 * a + 4 * h2);
+      if (lh && h2 == 0) lh[i_row] = -__builtin_inff();
+    }
+    return;
+  }
+
+  bf16x8 qf[QC];
+#pragma unroll
+  for (int c = 0; c < QC; ++c) qf[c] = Io<__bf16>::load8(qh + i_row * D + 16 * c + 8 * h2);
+
+  // Load instruction j of this wave covers tile rows RPI*(wid + NW*j) ..;
+  // lane l writes physical chunk l % CPR of row RPI*i + l / CPR.
+  const int lrow = lane / CPR, lph = lane % CPR;
+  const int row0 = RPI * wid + lrow;  // row % CPR and f(row) are the same for every j
+  const int k_src = lrow * D + (lph ^ (row0 & (CPR - 1))) * 8;
+  const int v_src = lrow * D + (lph ^ VSwz<D>::f(row0)) * 8;
+  auto dma = [&](const __bf16 *src_tile, const int src_off, __bf16 *dst_tile) {
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      const int i = wid + NW * j;
+      __builtin_amdgcn_global_load_lds(
+          (__attribute__((address_space(1))) void *)(src_tile + src_off + i * RPI * D),
+          (__attribute__((address_space(3))) void *)(dst_tile + i * 512), 16, 0, 0);
+    }
+  };
+  auto load_k = [&](int n, int buf) { dma(kh + (int64_t)n * TILE, k_src, Kbuf0 + buf * TILE); };
+  auto load_v = [&](int n, int buf) { dma(vh + (int64_t)n * TILE, v_src, Vbuf0 + buf * TILE); };
+
+  // Per-lane element offsets of the K operand reads (one per k chunk).
+  const int key0 = ks * KW;
+  int koff[QC];
+#pragma unroll
+  for (int c = 0; c < QC; ++c)
+    koff[c] = (key0 + l32) * D + (((2 * c + h2) ^ (l32 & (CPR - 1))) * 8);
+  // V^T operand: transpose-read source row and chunk of this lane
+  const int e_src = l16 / 4, c_src = l16 % 4;
+  const int vrow = key0 + 4 * h2 + e_src;   // + 32jt + 16c2 (+8) leaves f(row) unchanged
+  const int vsw = VSwz<D>::f(vrow);
+
+  auto qk = [&](int buf, f32x16 (&s)[JT]) {
+    const __bf16 *kb = Kbuf0 + buf * TILE;
+    __builtin_amdgcn_iglp_opt(0);  // interleave LDS reads with MFMAs
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) {
+      s[jt] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < QC; ++c) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kb + koff[c] + 32 * jt * D);
+        s[jt] = mfma32(a, qf[c], s[jt]);
+      }
+    }
+  };
+
+  float m_run = kMaxFloor;
+  float l_run = 0.f;
+  f32x16 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
+
+  auto softmax_pv = [&](f32x16 (&s)[JT], int buf) {
+    float mx = s[0][0];
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[jt][e]);
+    mx = max_xor32(mx) * scale_log2;
+    if (__any(mx > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pe = fast_exp2(fmaf(s[jt][e], scale_log2, -m_run));
+        s[jt][e] = pe;
+        psum += pe;
+      }
+    l_run += psum;
+    const __bf16 *vb = Vbuf0 + buf * TILE;
+    __builtin_amdgcn_iglp_opt(0);
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const bf16x8 pf = to_bf16x8(s[jt][8 * c2 + 0], s[jt][8 * c2 + 1], s[jt][8 * c2 + 2],
+                                    s[jt][8 * c2 + 3], s[jt][8 * c2 + 4], s[jt][8 * c2 + 5],
+                                    s[jt][8 * c2 + 6], s[jt][8 * c2 + 7]);
+        const int row = vrow + 32 * jt + 16 * c2;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          // logical 8-byte piece (dt, G%2, c_src) of rows `row` and `row + 8`
+          const int lc = 4 * dt + 2 * (G % 2) + c_src / 2;  // 16-byte chunk
+          const int pc = lc ^ vsw;
+          const __bf16 *src = vb + row * D + pc * 8 + 4 * (c_src % 2);
+          const bf16x8 a = cat4(lds_read_tr4(src), lds_read_tr4(src + 8 * D));
+          o[dt] = mfma32(a, pf, o[dt]);
+        }
+      }
+  };
+
+  const int n = end - beg;
+  const int32_t *cols = col_idx + beg;
+  f32x16 s_cur[JT], s_next[JT];
+  load_k(cols[0], 0);
+  load_v(cols[0], 0);
+  if (n > 1) load_k(cols[1], 1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  qk(0, s_cur);
+  for (int t = 0; t + 1 < n; ++t) {
+    __syncthreads();  // DMA of iteration t-1 visible; K buffer t%2, V buffer (t+1)%2 free
+    load_k(cols[min(t + 2, n - 1)], t & 1);
+    load_v(cols[t + 1], (t + 1) & 1);
+    qk((t + 1) & 1, s_next);
+    softmax_pv(s_cur, t & 1);
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) s_cur[jt] = s_next[jt];
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA done before the next barrier
+  }
+  __syncthreads();
+  softmax_pv(s_cur, (n - 1) & 1);
+
+  float l_tot = sum_xor32(l_run);
+  {
+    float *mrg = reinterpret_cast<float *>(smem) + rg * MRG;
+    __syncthreads();
+    if (ks == 1) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mrg[(dt * 16 + e) * 64 + lane] = o[dt][e];
+      mrg[DT * 16 * 64 + lane] = m_run;
+      mrg[DT * 16 * 64 + 64 + lane] = l_tot;
+    }
+    __syncthreads();
+    if (ks == 1) return;
+    const float m2 = mrg[DT * 16 * 64 + lane];
+    const float l2 = mrg[DT * 16 * 64 + 64 + lane];
+    const float mm = fmaxf(m_run, m2);
+    const float a1 = fast_exp2(m_run - mm), a2 = fast_exp2(m2 - mm);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[dt][e] = o[dt][e] * a1 + mrg[(dt * 16 + e) * 64 + lane] * a2;
+    l_tot = l_tot * a1 + l2 * a2;
+    m_run = mm;
+  }
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      Io<__bf16>::store4(oh + i_row * D + 32 * dt + 8 * a + 4 * h2,
+                         f32x4{o[dt][4 * a], o[dt][4 * a + 1], o[dt][4 * a + 2], o[dt][4 * a + 3]} * inv);
+  if (lh && h2 == 0) lh[i_row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
+}
+
 template <int BS, int D, typename T>
 hipError_t launch_one(const void *q, const void *k, const void *v, const int32_t *row_ptr,
                       const int32_t *col_idx, const int32_t *row_order, int32_t B, int32_t H,
@@ -234,9 +746,20 @@ hipError_t launch_one(const void *q, const void *k, const void *v, const int32_t
   const int64_t per = (W + 7) / 8;
   const int64_t grid = per * 8;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((bsa_fwd_kernel<BS, D, T>), dim3((unsigned)grid), dim3(BS * 4), 0, stream,
-                     (const T *)q, (const T *)k, (const T *)v, row_ptr, col_idx, row_order, B, H,
-                     Mb, Nb, scale * kLog2e, (T *)out, lse);
+  if constexpr (BS == 16) {
+    hipLaunchKernelGGL((bsa_fwd_kernel<BS, D, T>), dim3((unsigned)grid), dim3(BS * 4), 0, stream,
+                       (const T *)q, (const T *)k, (const T *)v, row_ptr, col_idx, row_order, B, H,
+                       Mb, Nb, scale * kLog2e, (T *)out, lse);
+  } else if constexpr (BS >= 64 && std::is_same<T, __bf16>::value) {
+    hipLaunchKernelGGL((bsa_fwd_dma_kernel<BS, D>), dim3((unsigned)grid), dim3(BS * 4), 0, stream,
+                       (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, row_ptr, col_idx,
+                       row_order, B, H, Mb, Nb, scale * kLog2e, (__bf16 *)out, lse);
+  } else {
+    constexpr int KSPLIT = BS >= 64 ? 2 : 1;
+    hipLaunchKernelGGL((bsa_fwd32_kernel<BS, D, T, KSPLIT>), dim3((unsigned)grid),
+                       dim3(BS * 2 * KSPLIT), 0, stream, (const T *)q, (const T *)k, (const T *)v,
+                       row_ptr, col_idx, row_order, B, H, Mb, Nb, scale * kLog2e, (T *)out, lse);
+  }
   return hipGetLastError();
 }
 
