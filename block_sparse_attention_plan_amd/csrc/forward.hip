@@ -39,6 +39,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kMaxFloor = -1e30f;
 constexpr float kLazy = 8.0f;  // tolerated staleness of the running max (log2 units)
+#ifndef BSA_DMA_KEY_SPLIT
+#define BSA_DMA_KEY_SPLIT 2
+#endif
+constexpr int kDmaKeySplit = BSA_DMA_KEY_SPLIT;  // waves per 32-row group in the bf16 kernel
 
 template <typename T> struct Io;
 template <> struct Io<__bf16> {
@@ -513,16 +517,16 @@ template <int D> struct VSwz {
   }
 };
 
-template <int BS, int D>
-__global__ void __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2)))
+template <int BS, int D, int KSPLIT>
+__global__ void __launch_bounds__(BS * 2 * KSPLIT) __attribute__((amdgpu_waves_per_eu(KSPLIT)))
 bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
                    const __bf16 *__restrict__ v, const int32_t *__restrict__ row_ptr,
                    const int32_t *__restrict__ col_idx, const int32_t *__restrict__ row_order,
                    int32_t B, int32_t H, int32_t Mb, int32_t Nb, float scale_log2,
                    __bf16 *__restrict__ out, float *__restrict__ lse) {
   constexpr int NRG = BS / 32;           // 32-row groups
-  constexpr int NW = NRG * 2;            // waves per workgroup (two key halves)
-  constexpr int KW = BS / 2;             // keys per wave per tile
+  constexpr int NW = NRG * KSPLIT;       // waves per workgroup
+  constexpr int KW = BS / KSPLIT;        // keys per wave per tile
   constexpr int CPR = D / 8;             // 16-byte chunks per row
   constexpr int TILE = BS * D;           // elements per K or V tile
   constexpr int NI = TILE * 2 / 1024;    // 1 KiB load instructions per tile
@@ -531,14 +535,17 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   constexpr int QC = D / 16;
   constexpr int JT = KW / 32;
   constexpr int DT = D / 32;
-  constexpr int MRG = DT * 16 * 64 + 128;
+  constexpr int HALF = DT * 8 * 64;      // merge floats per row group and buffer
   static_assert(NI % NW == 0 && IPW >= 1, "tile loads must split evenly over waves");
-  static_assert(NW % 4 == 0 || CPR <= RPI, "per-wave K swizzle must be lane-constant");
-  static_assert((size_t)NRG * MRG * 4 <= (size_t)4 * TILE * 2, "merge scratch must fit");
+  static_assert(NRG * HALF * 4 == TILE * 2, "merge halves fill one tile buffer each");
+  static_assert((RPI * NW) % CPR == 0, "per-wave K swizzle must be lane-constant");
 
-  __shared__ __attribute__((aligned(1024))) __bf16 smem[4 * TILE];  // K0 K1 V0 V1
-  __bf16 *const Kbuf0 = smem;
-  __bf16 *const Vbuf0 = smem + 2 * TILE;
+  // Four distinct LDS objects, so that the compiler can tell the tile being
+  // read from the tile being filled and need not wait for the copy in flight.
+  __shared__ __attribute__((aligned(1024))) __bf16 K0[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 K1[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 V0[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 V1[TILE];
 
   const int64_t W = (int64_t)B * H * Mb;
   const int64_t per = (W + 7) / 8;
@@ -599,8 +606,8 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
           (__attribute__((address_space(3))) void *)(dst_tile + i * 512), 16, 0, 0);
     }
   };
-  auto load_k = [&](int n, int buf) { dma(kh + (int64_t)n * TILE, k_src, Kbuf0 + buf * TILE); };
-  auto load_v = [&](int n, int buf) { dma(vh + (int64_t)n * TILE, v_src, Vbuf0 + buf * TILE); };
+  auto load_k = [&](int n, __bf16 *dst) { dma(kh + (int64_t)n * TILE, k_src, dst); };
+  auto load_v = [&](int n, __bf16 *dst) { dma(vh + (int64_t)n * TILE, v_src, dst); };
 
   // Per-lane element offsets of the K operand reads (one per k chunk).
   const int key0 = ks * KW;
@@ -613,8 +620,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   const int vrow = key0 + 4 * h2 + e_src;   // + 32jt + 16c2 (+8) leaves f(row) unchanged
   const int vsw = VSwz<D>::f(vrow);
 
-  auto qk = [&](int buf, f32x16 (&s)[JT]) {
-    const __bf16 *kb = Kbuf0 + buf * TILE;
+  auto qk = [&](const __bf16 *kb, f32x16 (&s)[JT]) {
     __builtin_amdgcn_iglp_opt(0);  // interleave LDS reads with MFMAs
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt) {
@@ -633,7 +639,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
 
-  auto softmax_pv = [&](f32x16 (&s)[JT], int buf) {
+  auto softmax_pv = [&](f32x16 (&s)[JT], const __bf16 *vb) {
     float mx = s[0][0];
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt)
@@ -658,7 +664,6 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
         psum += pe;
       }
     l_run += psum;
-    const __bf16 *vb = Vbuf0 + buf * TILE;
     __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt)
@@ -672,58 +677,89 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
         for (int dt = 0; dt < DT; ++dt) {
           // logical 8-byte piece (dt, G%2, c_src) of rows `row` and `row + 8`
           const int lc = 4 * dt + 2 * (G % 2) + c_src / 2;  // 16-byte chunk
-          const int pc = lc ^ vsw;
-          const __bf16 *src = vb + row * D + pc * 8 + 4 * (c_src % 2);
+          const __bf16 *src = vb + row * D + (lc ^ vsw) * 8 + 4 * (c_src % 2);
           const bf16x8 a = cat4(lds_read_tr4(src), lds_read_tr4(src + 8 * D));
           o[dt] = mfma32(a, pf, o[dt]);
         }
       }
   };
 
+  // Software pipeline over the row's live tiles u = 0 .. n-1: tile u's K
+  // sits in K0 (u even) or K1 (u odd), its V likewise in V0 / V1.  At the top
+  // of iteration t, K_{t+1} and V_t are in LDS and S_t is in registers; the
+  // iteration starts the copies of K_{t+2} and V_{t+1} into the buffers freed
+  // by iteration t-1, computes the QK^T of tile t+1 beside the softmax of
+  // tile t, and waits for its own copies before the next barrier.  The loop is
+  // unrolled by two so every buffer is a compile-time object.
   const int n = end - beg;
   const int32_t *cols = col_idx + beg;
-  f32x16 s_cur[JT], s_next[JT];
-  load_k(cols[0], 0);
-  load_v(cols[0], 0);
-  if (n > 1) load_k(cols[1], 1);
+  f32x16 s_a[JT], s_b[JT];
+  load_k(cols[0], K0);
+  load_v(cols[0], V0);
+  if (n > 1) load_k(cols[1], K1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  qk(0, s_cur);
-  for (int t = 0; t + 1 < n; ++t) {
-    __syncthreads();  // DMA of iteration t-1 visible; K buffer t%2, V buffer (t+1)%2 free
-    load_k(cols[min(t + 2, n - 1)], t & 1);
-    load_v(cols[t + 1], (t + 1) & 1);
-    qk((t + 1) & 1, s_next);
-    softmax_pv(s_cur, t & 1);
-#pragma unroll
-    for (int jt = 0; jt < JT; ++jt) s_cur[jt] = s_next[jt];
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA done before the next barrier
+  qk(K0, s_a);
+  int t = 0;
+  for (; t + 2 < n; t += 2) {
+    __syncthreads();  // DMA of the previous iteration visible; K0 and V1 free
+    load_k(cols[t + 2], K0);
+    load_v(cols[t + 1], V1);
+    qk(K1, s_b);
+    softmax_pv(s_a, V0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // K1 and V0 free
+    load_k(cols[min(t + 3, n - 1)], K1);
+    load_v(cols[t + 2], V0);
+    qk(K0, s_a);
+    softmax_pv(s_b, V1);
+    __builtin_amdgcn_s_waitcnt(0);
   }
-  __syncthreads();
-  softmax_pv(s_cur, (n - 1) & 1);
+  if (t + 1 < n) {  // one more steady step: tile t (even) with V0, K_{t+1} in K1
+    __syncthreads();
+    load_v(cols[t + 1], V1);
+    qk(K1, s_b);
+    softmax_pv(s_a, V0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    softmax_pv(s_b, V1);
+  } else {
+    __syncthreads();
+    softmax_pv(s_a, V0);
+  }
 
   float l_tot = sum_xor32(l_run);
-  {
-    float *mrg = reinterpret_cast<float *>(smem) + rg * MRG;
+  if constexpr (KSPLIT == 2) {
+    // merge the two key halves: O halves through K0 / K1, (m, l) through V0
+    float *h0 = reinterpret_cast<float *>(K0) + rg * HALF;
+    float *h1 = reinterpret_cast<float *>(K1) + rg * HALF;
+    float *ml = reinterpret_cast<float *>(V0) + rg * 128;
     __syncthreads();
     if (ks == 1) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mrg[(dt * 16 + e) * 64 + lane] = o[dt][e];
-      mrg[DT * 16 * 64 + lane] = m_run;
-      mrg[DT * 16 * 64 + 64 + lane] = l_tot;
+        for (int e = 0; e < 16; ++e) {
+          const int f = (dt * 16 + e) * 64 + lane;
+          if (f < HALF) h0[f] = o[dt][e]; else h1[f - HALF] = o[dt][e];
+        }
+      ml[lane] = m_run;
+      ml[64 + lane] = l_tot;
     }
     __syncthreads();
     if (ks == 1) return;
-    const float m2 = mrg[DT * 16 * 64 + lane];
-    const float l2 = mrg[DT * 16 * 64 + 64 + lane];
+    const float m2 = ml[lane];
+    const float l2 = ml[64 + lane];
     const float mm = fmaxf(m_run, m2);
     const float a1 = fast_exp2(m_run - mm), a2 = fast_exp2(m2 - mm);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[dt][e] = o[dt][e] * a1 + mrg[(dt * 16 + e) * 64 + lane] * a2;
+      for (int e = 0; e < 16; ++e) {
+        const int f = (dt * 16 + e) * 64 + lane;
+        const float other = f < HALF ? h0[f] : h1[f - HALF];
+        o[dt][e] = o[dt][e] * a1 + other * a2;
+      }
     l_tot = l_tot * a1 + l2 * a2;
     m_run = mm;
   }
@@ -751,7 +787,8 @@ hipError_t launch_one(const void *q, const void *k, const void *v, const int32_t
                        (const T *)q, (const T *)k, (const T *)v, row_ptr, col_idx, row_order, B, H,
                        Mb, Nb, scale * kLog2e, (T *)out, lse);
   } else if constexpr (BS >= 64 && std::is_same<T, __bf16>::value) {
-    hipLaunchKernelGGL((bsa_fwd_dma_kernel<BS, D>), dim3((unsigned)grid), dim3(BS * 4), 0, stream,
+    constexpr int KS = BS == 128 ? kDmaKeySplit : 2;
+    hipLaunchKernelGGL((bsa_fwd_dma_kernel<BS, D, KS>), dim3((unsigned)grid), dim3(BS * 2 * KS), 0, stream,
                        (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, row_ptr, col_idx,
                        row_order, B, H, Mb, Nb, scale * kLog2e, (__bf16 *)out, lse);
   } else {

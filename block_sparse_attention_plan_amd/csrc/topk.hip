@@ -10,15 +10,22 @@
 // [0, N)) contribute nothing; the running maximum starts at a finite floor so
 // a position without a valid slot produces zeros instead of NaN.
 //
-// Work item = (batch, position); one workgroup of four waves.  Wave w owns
-// heads 16w .. 16w+15.  Slots are processed in chunks of 64: each wave
-// gathers 16 of the chunk's rows (one 1 KiB row per wave instruction) into a
-// register prefetch buffer one chunk ahead; the chunk is then staged
-// row-major in LDS and every wave computes
+// Work item = (batch, position); one workgroup of four waves, wave w owning
+// heads 16w .. 16w+15 over all of d.  Slots are processed in chunks of 32
+// whose rows are copied straight from HBM into LDS (one
+// global_load_lds_dwordx4 per 1 KiB row; slots without a valid index get a
+// zero row), one chunk ahead into the other of two buffers, so the one
+// gather serves all heads of the position.  Every wave computes
 //   S^T = KV Q^T       (16x16x32 MFMA, Q^T resident in registers)
-//   online softmax     (lane owns one head column)
+//   online softmax     (lane owns one head column; the running maximum may
+//                      lag the true one by a bounded amount before the
+//                      accumulator is rescaled)
 //   O^T += KV^T P^T    (16x16x32 MFMA, KV^T by LDS transpose reads)
-// so the one gather serves all heads of the position.
+// The two buffers (2 x 33 KiB with rows padded by 32 bytes against bank
+// conflicts) let two workgroups share a CU, so each SIMD interleaves the
+// waves of two positions.  The buffers are distinct LDS objects and the
+// chunk loop is unrolled by two, so the compiler never waits for a copy
+// into the buffer it is not reading.
 #include "bsa_device.h"
 #include "bsa_internal.h"
 
@@ -27,23 +34,22 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMaxFloor = -1e30f;
+constexpr float kLazy = 8.0f;  // tolerated staleness of the running max (log2 units)
 
 template <int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
             const int32_t *__restrict__ idx, const float *__restrict__ sink, int32_t M,
             int32_t N, int32_t H, int32_t topk, float scale_log2, __bf16 *__restrict__ out) {
-  constexpr int T = 64;               // slots per chunk
+  constexpr int T = 32;               // slots per chunk
   constexpr int STR = D + 16;         // LDS row stride (elements)
   constexpr int RPW = T / 4;          // rows gathered per wave per chunk
-  constexpr int LPR = D / 8;          // lanes per row (16-byte pieces)
-  constexpr int RPI = 64 / LPR;       // rows per wave instruction
-  constexpr int CPT = RPW / RPI;      // 16-byte pieces per thread per chunk
-  constexpr int QC = D / 32;
-  constexpr int DT = D / 16;
-  static_assert(LPR <= 64 && 64 % LPR == 0 && RPW % RPI == 0, "row split");
+  constexpr int QC = D / 32;          // 32-wide k steps of S^T
+  constexpr int DT = D / 16;          // 16-wide d tiles of O^T
+  static_assert(D == 512, "one wave instruction copies one 1 KiB row");
 
-  __shared__ __attribute__((aligned(16))) __bf16 KVs[T * STR];
+  __shared__ __attribute__((aligned(16))) __bf16 C0[T * STR];
+  __shared__ __attribute__((aligned(16))) __bf16 C1[T * STR];
 
   const int64_t pos = blockIdx.x;  // b * M + m
   const int64_t b = pos / M;
@@ -65,33 +71,25 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
       qf[c] = bf16x8{};
   }
 
-  // Gather of one chunk into registers: wave wid fetches rows wid*RPW ..
-  // (wid+1)*RPW-1 of the chunk; invalid slots load zeros.
-  bf16x8 gr[CPT];
-  uint64_t vmask_next = 0;
-  auto gather = [&](int t0) -> uint64_t {
-    const int slot = t0 + lane;
-    int my = -1;
-    if (slot < topk) my = ib[slot];
-    const bool valid = slot < topk && my >= 0 && my < N;
-    const uint64_t vm = __ballot(valid);
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int row = wid * RPW + c * RPI + lane / LPR;
-      const int src = __shfl(my, row, 64);
-      const bool ok = (vm >> row) & 1ull;
-      if (ok)
-        gr[c] = *reinterpret_cast<const bf16x8 *>(kvb + (int64_t)src * D + (lane % LPR) * 8);
-      else
-        gr[c] = bf16x8{};
-    }
-    return vm;
+  // Lane j < 32 holds slot j of chunk ch: its row index if valid, else -1.
+  auto chunk_idx = [&](int ch) -> int {
+    const int slot = ch * T + lane;
+    const int my = (lane < T && slot < topk) ? ib[slot] : -1;
+    return (my >= 0 && my < N) ? my : -1;
   };
-  auto stage = [&]() {
+  // Copy rows wid*RPW .. wid*RPW+RPW-1 of a chunk into `dst`.
+  auto gather = [&](int my, __bf16 *dst) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int row = wid * RPW + c * RPI + lane / LPR;
-      *reinterpret_cast<bf16x8 *>(&KVs[row * STR + (lane % LPR) * 8]) = gr[c];
+    for (int j = 0; j < RPW; ++j) {
+      const int row = wid * RPW + j;
+      const int src = __shfl(my, row, 64);
+      if (src >= 0) {
+        __builtin_amdgcn_global_load_lds(
+            (__attribute__((address_space(1))) void *)(kvb + (int64_t)src * D + lane * 8),
+            (__attribute__((address_space(3))) void *)(dst + row * STR), 16, 0, 0);
+      } else {
+        *reinterpret_cast<bf16x8 *>(dst + row * STR + lane * 8) = bf16x8{};
+      }
     }
   };
 
@@ -100,66 +98,77 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nchunks = (topk + T - 1) / T;
-  vmask_next = gather(0);
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const uint64_t vmask = vmask_next;
-    __syncthreads();
-    stage();
-    __syncthreads();
-    if (ch + 1 < nchunks) vmask_next = gather((ch + 1) * T);
-    if (!wave_active) continue;
-
-    f32x4 s[T / 16];
+  const int e_src = li / 4, c_src = li % 4;
+  auto compute = [&](const __bf16 *kb, uint64_t vmask) {
+    f32x4 s[2];
 #pragma unroll
-    for (int jt = 0; jt < T / 16; ++jt) {
+    for (int jt = 0; jt < 2; ++jt) {
       s[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < QC; ++c) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&KVs[(16 * jt + li) * STR + 32 * c + 8 * G]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kb + (16 * jt + li) * STR + 32 * c + 8 * G);
         s[jt] = mfma16(a, qf[c], s[jt]);
       }
     }
     float mx = -__builtin_inff();
 #pragma unroll
-    for (int jt = 0; jt < T / 16; ++jt)
+    for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = 16 * jt + 4 * G + e;
         if (!((vmask >> j) & 1ull)) s[jt][e] = -__builtin_inff();
         mx = fmaxf(mx, s[jt][e]);
       }
-    mx = max_xor32(max_xor16(mx));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
+    mx = max_xor32(max_xor16(mx)) * scale_log2;
+    if (__any(mx > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+    }
     float psum = 0.f;
 #pragma unroll
-    for (int jt = 0; jt < T / 16; ++jt)
+    for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = fast_exp2(fmaf(s[jt][e], scale_log2, -m_new));
+        const float p = fast_exp2(fmaf(s[jt][e], scale_log2, -m_run));
         s[jt][e] = p;
         psum += p;
       }
-    l_run = l_run * alpha + psum;
+    l_run += psum;
+    // k order of P^T: slots 4G+e (e < 4) then 16+4G+e, matching the rows of
+    // the two transpose reads below.
+    const bf16x8 pf = to_bf16x8(s[0][0], s[0][1], s[0][2], s[0][3], s[1][0], s[1][1], s[1][2], s[1][3]);
+    const __bf16 *rows = kb + (4 * G + e_src) * STR + 4 * c_src;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+    for (int dt = 0; dt < DT; ++dt) {
+      const bf16x8 a = cat4(lds_read_tr4(rows + 16 * dt), lds_read_tr4(rows + 16 * STR + 16 * dt));
+      acc[dt] = mfma16(a, pf, acc[dt]);
+    }
+  };
+  auto step = [&](int ch, int nchunks, int &my_cur, int &my_next, const __bf16 *cur, __bf16 *nxt) {
+    const uint64_t vmask = __ballot(my_cur >= 0);
+    if (ch + 1 < nchunks) {
+      gather(my_next, nxt);
+      my_cur = my_next;
+      if (ch + 2 < nchunks) my_next = chunk_idx(ch + 2);
+    }
+    if (wave_active && vmask != 0) compute(cur, vmask);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // next chunk visible; this chunk's buffer free
+  };
 
-    bf16x8 pf[T / 32];
-#pragma unroll
-    for (int kc = 0; kc < T / 32; ++kc)
-      pf[kc] = to_bf16x8(s[2 * kc][0], s[2 * kc][1], s[2 * kc][2], s[2 * kc][3],
-                         s[2 * kc + 1][0], s[2 * kc + 1][1], s[2 * kc + 1][2], s[2 * kc + 1][3]);
-    const int e_src = li / 4, c_src = li % 4;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int kc = 0; kc < T / 32; ++kc) {
-        const __bf16 *src = &KVs[(32 * kc + 4 * G + e_src) * STR + 16 * dt + 4 * c_src];
-        const bf16x8 a = cat4(lds_read_tr4(src), lds_read_tr4(src + 16 * STR));
-        acc[dt] = mfma16(a, pf[kc], acc[dt]);
-      }
+  const int nchunks = (topk + T - 1) / T;
+  int my_cur = chunk_idx(0);
+  gather(my_cur, C0);
+  int my_next = nchunks > 1 ? chunk_idx(1) : -1;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int ch = 0; ch < nchunks; ch += 2) {
+    step(ch, nchunks, my_cur, my_next, C0, C1);
+    if (ch + 1 < nchunks) step(ch + 1, nchunks, my_cur, my_next, C1, C0);
   }
   if (!wave_active) return;
 
