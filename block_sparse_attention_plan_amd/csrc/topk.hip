@@ -53,7 +53,8 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
 
   const int64_t pos = blockIdx.x;  // b * M + m
   const int64_t b = pos / M;
-  const int tid = threadIdx.x, wid = tid / 64, lane = tid % 64;
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wid = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform, kept in SGPRs
   const int G = lane / 16, li = lane % 16;
   const int h = 16 * wid + li;
   const bool wave_active = 16 * wid < H;
@@ -71,18 +72,21 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
       qf[c] = bf16x8{};
   }
 
-  // Lane j < 32 holds slot j of chunk ch: its row index if valid, else -1.
+  // Lane j < 32 loads slot j of chunk ch (-1 past the end); `valid` maps an
+  // entry to its row, or to -1 when it names no row.  The two are kept apart
+  // so that the load of a later chunk's indices is not waited for (which
+  // would also wait for the row copies issued before it) until it is used.
   auto chunk_idx = [&](int ch) -> int {
     const int slot = ch * T + lane;
-    const int my = (lane < T && slot < topk) ? ib[slot] : -1;
-    return (my >= 0 && my < N) ? my : -1;
+    return (lane < T && slot < topk) ? ib[slot] : -1;
   };
+  auto valid = [&](int my) -> int { return (my >= 0 && my < N) ? my : -1; };
   // Copy rows wid*RPW .. wid*RPW+RPW-1 of a chunk into `dst`.
   auto gather = [&](int my, __bf16 *dst) {
 #pragma unroll
     for (int j = 0; j < RPW; ++j) {
       const int row = wid * RPW + j;
-      const int src = __shfl(my, row, 64);
+      const int src = __builtin_amdgcn_readlane(my, row);
       if (src >= 0) {
         __builtin_amdgcn_global_load_lds(
             (__attribute__((address_space(1))) void *)(kvb + (int64_t)src * D + lane * 8),
@@ -100,16 +104,14 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
 
   const int e_src = li / 4, c_src = li % 4;
   auto compute = [&](const __bf16 *kb, uint64_t vmask) {
-    f32x4 s[2];
+    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt) {
-      s[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < QC; ++c)
 #pragma unroll
-      for (int c = 0; c < QC; ++c) {
+      for (int jt = 0; jt < 2; ++jt) {
         const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kb + (16 * jt + li) * STR + 32 * c + 8 * G);
         s[jt] = mfma16(a, qf[c], s[jt]);
       }
-    }
     float mx = -__builtin_inff();
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt)
@@ -148,20 +150,24 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
       acc[dt] = mfma16(a, pf, acc[dt]);
     }
   };
-  auto step = [&](int ch, int nchunks, int &my_cur, int &my_next, const __bf16 *cur, __bf16 *nxt) {
+  // my_cur: validated rows of chunk ch; raw_next: unvalidated entries of
+  // chunk ch + 1.
+  auto step = [&](int ch, int nchunks, int &my_cur, int &raw_next, const __bf16 *cur, __bf16 *nxt) {
     const uint64_t vmask = __ballot(my_cur >= 0);
+    int my_following = -1;
     if (ch + 1 < nchunks) {
-      gather(my_next, nxt);
-      my_cur = my_next;
-      if (ch + 2 < nchunks) my_next = chunk_idx(ch + 2);
+      my_following = valid(raw_next);
+      gather(my_following, nxt);
+      if (ch + 2 < nchunks) raw_next = chunk_idx(ch + 2);
     }
     if (wave_active && vmask != 0) compute(cur, vmask);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // next chunk visible; this chunk's buffer free
+    my_cur = my_following;
   };
 
   const int nchunks = (topk + T - 1) / T;
-  int my_cur = chunk_idx(0);
+  int my_cur = valid(chunk_idx(0));
   gather(my_cur, C0);
   int my_next = nchunks > 1 ? chunk_idx(1) : -1;
   __builtin_amdgcn_s_waitcnt(0);
