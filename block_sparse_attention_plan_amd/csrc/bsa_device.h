@@ -70,6 +70,22 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // group.  With lane s = 4e' + c pointing at row (k0 + e') and columns
 // (n0 + 4c .. n0 + 4c + 3) of a row-major [k][n] tile, lane t receives
 // tile[k0 + e][n0 + t] for e = 0..3: four consecutive k of column t.
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 untyped access);
+// reads at or past `bytes` return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
+// Copy 16 bytes per lane from rsrc + voff + soff straight into LDS at
+// lds_base + 16 * lane (buffer_load_dwordx4 ... lds; lds_base is
+// wave-uniform).  Unlike the global_load_lds form, the compiler accounts
+// for this copy on the vector-memory counter alone, so LDS reads issued
+// while it is in flight can be waited for one by one.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rs, void *lds_base,
+                                              uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (BSA_LDS void *)lds_base, 16, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16 *lds_ptr) {
   i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BSA_LDS i16x4 *)(lds_ptr));
   return __builtin_bit_cast(bf16x4, r);

@@ -42,7 +42,15 @@ constexpr float kLazy = 8.0f;  // tolerated staleness of the running max (log2 u
 #ifndef BSA_DMA_KEY_SPLIT
 #define BSA_DMA_KEY_SPLIT 2
 #endif
-constexpr int kDmaKeySplit = BSA_DMA_KEY_SPLIT;  // waves per 32-row group in the bf16 kernel
+constexpr int kDmaKeySplit = BSA_DMA_KEY_SPLIT;
+#ifndef BSA_READ_AHEAD_K
+#define BSA_READ_AHEAD_K 4
+#endif
+#ifndef BSA_READ_AHEAD_V
+#define BSA_READ_AHEAD_V 6
+#endif
+constexpr int kReadAheadK = BSA_READ_AHEAD_K;  // K operand reads issued before the first QK MFMA
+constexpr int kReadAheadV = BSA_READ_AHEAD_V;  // V transpose reads issued before the first PV MFMA  // waves per 32-row group in the bf16 kernel
 
 template <typename T> struct Io;
 template <> struct Io<__bf16> {
@@ -509,6 +517,25 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
 //   K (b128 reads, 16 consecutive rows per phase): chunk ^ (row % CPR)
 //   V (transpose reads, 4 rows x 64 B per half-wave): chunk ^ 4*f(row)
 // The work split, MFMA layouts and software pipeline match bsa_fwd32_kernel.
+// Schedule pattern for one straight-line region: N MFMAs, each followed by
+// V VALU instructions and R LDS reads, with P reads issued ahead of the
+// first MFMA (reads beyond the total are simply not matched).
+template <int I, int N, int R, int V>
+__device__ __forceinline__ void sched_steps() {
+  if constexpr (I < N) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(0x002, V, 0);  // VALU
+    if constexpr (R > 0) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);  // LDS read
+    sched_steps<I + 1, N, R, V>();
+  }
+}
+template <int N, int TOTAL_READS, int P, int V>
+__device__ __forceinline__ void sched_interleave() {
+  constexpr int R = (TOTAL_READS + N - 1) / N;
+  if constexpr (P > 0) __builtin_amdgcn_sched_group_barrier(0x100, P, 0);
+  sched_steps<0, N, R, V>();
+}
+
 template <int D> struct VSwz {
   static __device__ __forceinline__ int f(int row) {
     if constexpr (D == 128) return 4 * (row & 3);
@@ -560,7 +587,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   const int end = row_ptr[r + 1];
 
   const int tid = threadIdx.x;
-  const int wid = tid / 64;
+  const int wid = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform, kept in SGPRs
   const int rg = wid % NRG;
   const int ks = wid / NRG;
   const int lane = tid % 64;
@@ -598,12 +625,11 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   const int k_src = lrow * D + (lph ^ (row0 & (CPR - 1))) * 8;
   const int v_src = lrow * D + (lph ^ VSwz<D>::f(row0)) * 8;
   auto dma = [&](const __bf16 *src_tile, const int src_off, __bf16 *dst_tile) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src_tile, TILE * 2);
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
       const int i = wid + NW * j;
-      __builtin_amdgcn_global_load_lds(
-          (__attribute__((address_space(1))) void *)(src_tile + src_off + i * RPI * D),
-          (__attribute__((address_space(3))) void *)(dst_tile + i * 512), 16, 0, 0);
+      copy16_to_lds(rs, dst_tile + i * 512, (uint32_t)(src_off * 2), (uint32_t)(i * RPI * D * 2));
     }
   };
   auto load_k = [&](int n, __bf16 *dst) { dma(kh + (int64_t)n * TILE, k_src, dst); };
@@ -621,16 +647,15 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   const int vsw = VSwz<D>::f(vrow);
 
   auto qk = [&](const __bf16 *kb, f32x16 (&s)[JT]) {
-    __builtin_amdgcn_iglp_opt(0);  // interleave LDS reads with MFMAs
 #pragma unroll
-    for (int jt = 0; jt < JT; ++jt) {
-      s[jt] = f32x16{};
+    for (int jt = 0; jt < JT; ++jt) s[jt] = f32x16{};
 #pragma unroll
-      for (int c = 0; c < QC; ++c) {
+    for (int c = 0; c < QC; ++c)
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt) {
         const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kb + koff[c] + 32 * jt * D);
         s[jt] = mfma32(a, qf[c], s[jt]);
       }
-    }
   };
 
   float m_run = kMaxFloor;
@@ -639,13 +664,18 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
 
-  auto softmax_pv = [&](f32x16 (&s)[JT], const __bf16 *vb) {
+  // Row maximum of a score tile in log2 units (lane column = query row).
+  auto tile_max = [&](const f32x16 (&s)[JT]) -> float {
     float mx = s[0][0];
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[jt][e]);
-    mx = max_xor32(mx) * scale_log2;
+    return max_xor32(mx) * scale_log2;
+  };
+  // Move the running max only when a row's tile max exceeds it by more than
+  // kLazy; the accumulators are rescaled on those (rare) tiles alone.
+  auto rescale = [&](float mx) {
     if (__any(mx > m_run + kLazy)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = fast_exp2(m_run - m_new);
@@ -654,24 +684,29 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
     }
-    float psum = 0.f;
-#pragma unroll
-    for (int jt = 0; jt < JT; ++jt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pe = fast_exp2(fmaf(s[jt][e], scale_log2, -m_run));
-        s[jt][e] = pe;
-        psum += pe;
-      }
-    l_run += psum;
-    __builtin_amdgcn_iglp_opt(0);
+  };
+  // P = exp2(S * scale - m) packed to bf16 in the k order of the PV operand.
+  auto exp_pack = [&](const f32x16 (&s)[JT], bf16x8 (&pf)[2 * JT]) {
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
-        const bf16x8 pf = to_bf16x8(s[jt][8 * c2 + 0], s[jt][8 * c2 + 1], s[jt][8 * c2 + 2],
-                                    s[jt][8 * c2 + 3], s[jt][8 * c2 + 4], s[jt][8 * c2 + 5],
-                                    s[jt][8 * c2 + 6], s[jt][8 * c2 + 7]);
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = fast_exp2(fmaf(s[jt][8 * c2 + e], scale_log2, -m_run));
+          ps[e % 4] += p[e];
+        }
+        pf[2 * jt + c2] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+      }
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  };
+  auto pv = [&](const bf16x8 (&pf)[2 * JT], const __bf16 *vb) {
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
         const int row = vrow + 32 * jt + 16 * c2;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
@@ -679,53 +714,93 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
           const int lc = 4 * dt + 2 * (G % 2) + c_src / 2;  // 16-byte chunk
           const __bf16 *src = vb + row * D + (lc ^ vsw) * 8 + 4 * (c_src % 2);
           const bf16x8 a = cat4(lds_read_tr4(src), lds_read_tr4(src + 8 * D));
-          o[dt] = mfma32(a, pf, o[dt]);
+          o[dt] = mfma32(a, pf[2 * jt + c2], o[dt]);
         }
       }
+  };
+  // One steady step: QK^T of the next tile beside the exponentials of this
+  // one, then this tile's PV beside the next tile's row max.  The schedule
+  // barriers interleave each MFMA with the VALU and LDS work that hides it.
+  auto step = [&](const __bf16 *kb_next, f32x16 (&s_next)[JT], f32x16 (&s_cur)[JT],
+                  const __bf16 *vb, float &mx_next) {
+    bf16x8 pf[2 * JT];
+    qk(kb_next, s_next);
+    exp_pack(s_cur, pf);
+    pv(pf, vb);
+    mx_next = tile_max(s_next);
+    sched_interleave<JT * QC, JT * QC, kReadAheadK, 3 * 16 * JT / (JT * QC) + 1>();
+    sched_interleave<JT * 2 * DT, 4 * JT * DT, kReadAheadV, 1>();
+  };
+  auto last = [&](f32x16 (&s_cur)[JT], const __bf16 *vb) {
+    bf16x8 pf[2 * JT];
+    exp_pack(s_cur, pf);
+    pv(pf, vb);
   };
 
   // Software pipeline over the row's live tiles u = 0 .. n-1: tile u's K
   // sits in K0 (u even) or K1 (u odd), its V likewise in V0 / V1.  At the top
-  // of iteration t, K_{t+1} and V_t are in LDS and S_t is in registers; the
-  // iteration starts the copies of K_{t+2} and V_{t+1} into the buffers freed
-  // by iteration t-1, computes the QK^T of tile t+1 beside the softmax of
-  // tile t, and waits for its own copies before the next barrier.  The loop is
-  // unrolled by two so every buffer is a compile-time object.
+  // of iteration t, K_{t+1} and V_t are in LDS, S_t is in registers and its
+  // row max is known; the iteration starts the copies of K_{t+2} and V_{t+1}
+  // into the buffers freed by iteration t-1, computes the QK^T of tile t+1
+  // beside the softmax of tile t, and waits for its own copies before the
+  // next barrier.  The loop is unrolled by two so every buffer is a
+  // compile-time object.
   const int n = end - beg;
   const int32_t *cols = col_idx + beg;
+  // Column indices of the next step's copies travel through a vector load
+  // (lane 0: next K tile, lane 1: next V tile) issued one step ahead: a
+  // scalar load in flight would force every LDS wait in between to drain
+  // completely, since scalar loads may return out of order.
+  auto fetch_cols = [&](int kpos, int vpos) -> int { return cols[lane == 0 ? kpos : vpos]; };
   f32x16 s_a[JT], s_b[JT];
+  float mx_a, mx_b;
   load_k(cols[0], K0);
   load_v(cols[0], V0);
   if (n > 1) load_k(cols[1], K1);
+  int cv = fetch_cols(min(2, n - 1), min(1, n - 1));
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   qk(K0, s_a);
+  mx_a = tile_max(s_a);
   int t = 0;
   for (; t + 2 < n; t += 2) {
     __syncthreads();  // DMA of the previous iteration visible; K0 and V1 free
-    load_k(cols[t + 2], K0);
-    load_v(cols[t + 1], V1);
-    qk(K1, s_b);
-    softmax_pv(s_a, V0);
+    {
+      const int kc = __builtin_amdgcn_readlane(cv, 0), vc = __builtin_amdgcn_readlane(cv, 1);
+      cv = fetch_cols(min(t + 3, n - 1), t + 2);  // ahead of the copies: waits for it skip them
+      load_k(kc, K0);  // tile t + 2
+      load_v(vc, V1);  // tile t + 1
+    }
+    rescale(mx_a);
+    step(K1, s_b, s_a, V0, mx_b);
     __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_sched_barrier(0);  // keep the compute regions between the barriers
     __syncthreads();  // K1 and V0 free
-    load_k(cols[min(t + 3, n - 1)], K1);
-    load_v(cols[t + 2], V0);
-    qk(K0, s_a);
-    softmax_pv(s_b, V1);
+    {
+      const int kc = __builtin_amdgcn_readlane(cv, 0), vc = __builtin_amdgcn_readlane(cv, 1);
+      cv = fetch_cols(min(t + 4, n - 1), min(t + 3, n - 1));
+      load_k(kc, K1);  // tile min(t + 3, n - 1)
+      load_v(vc, V0);  // tile t + 2
+    }
+    rescale(mx_b);
+    step(K0, s_a, s_b, V1, mx_a);
     __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_sched_barrier(0);  // keep the compute regions between the barriers
   }
   if (t + 1 < n) {  // one more steady step: tile t (even) with V0, K_{t+1} in K1
     __syncthreads();
-    load_v(cols[t + 1], V1);
-    qk(K1, s_b);
-    softmax_pv(s_a, V0);
+    load_v(__builtin_amdgcn_readlane(cv, 1), V1);  // tile t + 1
+    rescale(mx_a);
+    step(K1, s_b, s_a, V0, mx_b);
     __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_sched_barrier(0);  // keep the compute regions between the barriers
     __syncthreads();
-    softmax_pv(s_b, V1);
+    rescale(mx_b);
+    last(s_b, V1);
   } else {
     __syncthreads();
-    softmax_pv(s_a, V0);
+    rescale(mx_a);
+    last(s_a, V0);
   }
 
   float l_tot = sum_xor32(l_run);
