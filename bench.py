@@ -17,8 +17,13 @@ tile per head per batch item + 4*d*H per valid top-k index) / step time.
 
 Flags: --gpus N (only 1 is supported), --steps K, --warmup W,
 --no-cpu-baseline (skip the oracle timing), --cpu-seconds S (oracle sample
-budget per kernel), --copy-calibration (also run one plain device copy of
-known size, for HBM counter scaling under a profiler).
+budget per kernel), --copy-calibration (also run one plain elementwise copy
+of 1 GiB, for HBM counter scaling under a profiler).
+
+--summarize-counters FETCH_CSV WRITE_CSV (no GPU needed) turns the counter
+files of two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of
+`bench.py --copy-calibration` into profiles/hbm_traffic.json: HBM bytes per
+launch of each kernel, scaled by what the same counters read for the copy.
 """
 
 from __future__ import annotations
@@ -152,7 +157,60 @@ def cpu_baseline(fwd, topk_in, budget_s: float):
     }
 
 
+CALIBRATION_BYTES = float(1 << 30)   # read and written by the calibration copy
+KERNEL_MATCH = {"bsa_forward": "bsa_fwd", "topk_sparse_attn": "topk_kernel"}
+
+
+def _counter_means(path: str, counter: str):
+    """Mean value (KiB) of `counter` per dispatch, by kernel name."""
+    import csv
+    acc = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            acc.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, out_path: str = TRAFFIC_FILE) -> dict:
+    """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE counter runs, each
+    scaled so that the calibration copy reads and writes exactly 1 GiB."""
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+    cal_f = [v for k, v in fetch.items() if "neg_kernel" in k]
+    cal_w = [v for k, v in write.items() if "neg_kernel" in k]
+    if not cal_f or not cal_w:
+        raise SystemExit("summarize-counters: calibration copy (neg_kernel) not found in the counter files")
+    f_scale = CALIBRATION_BYTES / (cal_f[0] * 1024.0)
+    w_scale = CALIBRATION_BYTES / (cal_w[0] * 1024.0)
+    out = {"_calibration": {"kernel": "elementwise neg over 1 GiB fp32 (reads 1 GiB, writes 1 GiB)",
+                            "fetch_kib": cal_f[0], "write_kib": cal_w[0],
+                            "fetch_scale": f_scale, "write_scale": w_scale}}
+    for kernel, pat in KERNEL_MATCH.items():
+        fk = [v for k, v in fetch.items() if pat in k]
+        wk = [v for k, v in write.items() if pat in k]
+        if not fk or not wk:
+            continue
+        rd, wr = fk[0] * 1024.0 * f_scale, wk[0] * 1024.0 * w_scale
+        out[kernel] = {"fetch_kib": fk[0], "write_kib": wk[0], "read_bytes": rd, "write_bytes": wr,
+                       "bytes_per_launch": rd + wr,
+                       "source_sha": source_hash(KERNEL_SOURCES[kernel])}
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    return out
+
+
 def main(argv=None) -> int:
+    if argv is None:
+        argv = sys.argv[1:]
+    if argv and argv[0] == "--summarize-counters":
+        if len(argv) != 3:
+            print("usage: bench.py --summarize-counters FETCH_CSV WRITE_CSV", file=sys.stderr)
+            return 2
+        print(json.dumps(summarize_counters(argv[1], argv[2]), indent=1))
+        return 0
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
@@ -230,11 +288,13 @@ def main(argv=None) -> int:
     ms_per_step = wall * 1e3 / args.steps
 
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # one full-grid elementwise kernel that reads 1 GiB and writes 1 GiB
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)
         torch.cuda.synchronize()
-        log("[bench] copy calibration: 1 GiB device-to-device copy issued")
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: elementwise neg over 1 GiB issued")
 
     fwd_tflops = f_flops / (t_fwd * 1e-3) / 1e12
     topk_tflops = t_flops / (t_topk * 1e-3) / 1e12

@@ -70,6 +70,15 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // group.  With lane s = 4e' + c pointing at row (k0 + e') and columns
 // (n0 + 4c .. n0 + 4c + 3) of a row-major [k][n] tile, lane t receives
 // tile[k0 + e][n0 + t] for e = 0..3: four consecutive k of column t.
+// acc + x[2i] + x[2i+1] for a packed bf16 pair of x (v_dot2c_f32_bf16 with
+// a ones vector: products are exact, the sum is taken in fp32).
+__device__ __forceinline__ float sum2_bf16(bf16x8 x, int i, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t pair = {x[2 * i], x[2 * i + 1]};
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(pair, ones, acc, false);
+}
+
 // Raw buffer resource over `bytes` bytes at `base` (gfx9 untyped access);
 // reads at or past `bytes` return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -108,4 +117,23 @@ __device__ __forceinline__ f32x4 mfma16k16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
                                                    __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
 }
+// Schedule pattern for one straight-line region: N MFMAs, each followed by
+// V VALU instructions and R LDS reads, with P reads issued ahead of the
+// first MFMA (reads beyond the total are simply not matched).
+template <int I, int N, int R, int V>
+__device__ __forceinline__ void sched_steps() {
+  if constexpr (I < N) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(0x002, V, 0);  // VALU
+    if constexpr (R > 0) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);  // LDS read
+    sched_steps<I + 1, N, R, V>();
+  }
+}
+template <int N, int TOTAL_READS, int P, int V>
+__device__ __forceinline__ void sched_interleave() {
+  constexpr int R = (TOTAL_READS + N - 1) / N;
+  if constexpr (P > 0) __builtin_amdgcn_sched_group_barrier(0x100, P, 0);
+  sched_steps<0, N, R, V>();
+}
+
 }  // namespace bsa

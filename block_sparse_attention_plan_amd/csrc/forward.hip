@@ -42,7 +42,7 @@ constexpr float kLazy = 8.0f;  // tolerated staleness of the running max (log2 u
 #ifndef BSA_DMA_KEY_SPLIT
 #define BSA_DMA_KEY_SPLIT 2
 #endif
-constexpr int kDmaKeySplit = BSA_DMA_KEY_SPLIT;
+constexpr int kDmaKeySplit = BSA_DMA_KEY_SPLIT;  // waves per 32-row group in the bf16 bs=128 kernel
 #ifndef BSA_READ_AHEAD_K
 #define BSA_READ_AHEAD_K 4
 #endif
@@ -50,7 +50,7 @@ constexpr int kDmaKeySplit = BSA_DMA_KEY_SPLIT;
 #define BSA_READ_AHEAD_V 6
 #endif
 constexpr int kReadAheadK = BSA_READ_AHEAD_K;  // K operand reads issued before the first QK MFMA
-constexpr int kReadAheadV = BSA_READ_AHEAD_V;  // V transpose reads issued before the first PV MFMA  // waves per 32-row group in the bf16 kernel
+constexpr int kReadAheadV = BSA_READ_AHEAD_V;  // V transpose reads issued before the first PV MFMA
 
 template <typename T> struct Io;
 template <> struct Io<__bf16> {
@@ -509,33 +509,16 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
 }
 
 // bf16 variant for bs >= 64 whose K and V tiles travel from global memory
-// straight into LDS (global_load_lds_dwordx4: lane l of a wave instruction
-// writes bytes 16l .. 16l+15 of a 1 KiB LDS span), so no staging registers
-// or LDS store instructions sit in the loop.  Rows are unpadded; 16-byte
-// chunks are XOR-swizzled per row so that both read patterns are free of
-// bank conflicts:
+// straight into LDS (buffer_load_dwordx4 ... lds: lane l of a wave
+// instruction writes bytes 16l .. 16l+15 of a 1 KiB LDS span), so no staging
+// registers or LDS store instructions sit in the loop.  Rows are unpadded;
+// 16-byte chunks are XOR-swizzled per row so that both read patterns are
+// free of bank conflicts:
 //   K (b128 reads, 16 consecutive rows per phase): chunk ^ (row % CPR)
 //   V (transpose reads, 4 rows x 64 B per half-wave): chunk ^ 4*f(row)
-// The work split, MFMA layouts and software pipeline match bsa_fwd32_kernel.
-// Schedule pattern for one straight-line region: N MFMAs, each followed by
-// V VALU instructions and R LDS reads, with P reads issued ahead of the
-// first MFMA (reads beyond the total are simply not matched).
-template <int I, int N, int R, int V>
-__device__ __forceinline__ void sched_steps() {
-  if constexpr (I < N) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(0x002, V, 0);  // VALU
-    if constexpr (R > 0) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);  // LDS read
-    sched_steps<I + 1, N, R, V>();
-  }
-}
-template <int N, int TOTAL_READS, int P, int V>
-__device__ __forceinline__ void sched_interleave() {
-  constexpr int R = (TOTAL_READS + N - 1) / N;
-  if constexpr (P > 0) __builtin_amdgcn_sched_group_barrier(0x100, P, 0);
-  sched_steps<0, N, R, V>();
-}
-
+// The work split and MFMA layouts match bsa_fwd32_kernel; the pipeline (two
+// phases per tile, each copy given one and a half tiles to land) and the
+// instruction schedule are described at the loop.
 template <int D> struct VSwz {
   static __device__ __forceinline__ int f(int row) {
     if constexpr (D == 128) return 4 * (row & 3);
@@ -694,11 +677,11 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
       for (int c2 = 0; c2 < 2; ++c2) {
         float p[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = fast_exp2(fmaf(s[jt][8 * c2 + e], scale_log2, -m_run));
-          ps[e % 4] += p[e];
-        }
+        for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(s[jt][8 * c2 + e], scale_log2, -m_run));
         pf[2 * jt + c2] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+        // the denominator sums the same bf16 weights that multiply V
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ps[e] = sum2_bf16(pf[2 * jt + c2], e, ps[e]);
       }
     l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
   };
@@ -718,90 +701,94 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
         }
       }
   };
-  // One steady step: QK^T of the next tile beside the exponentials of this
-  // one, then this tile's PV beside the next tile's row max.  The schedule
-  // barriers interleave each MFMA with the VALU and LDS work that hides it.
-  auto step = [&](const __bf16 *kb_next, f32x16 (&s_next)[JT], f32x16 (&s_cur)[JT],
-                  const __bf16 *vb, float &mx_next) {
-    bf16x8 pf[2 * JT];
-    qk(kb_next, s_next);
-    exp_pack(s_cur, pf);
-    pv(pf, vb);
-    mx_next = tile_max(s_next);
-    sched_interleave<JT * QC, JT * QC, kReadAheadK, 3 * 16 * JT / (JT * QC) + 1>();
-    sched_interleave<JT * 2 * DT, 4 * JT * DT, kReadAheadV, 1>();
-  };
-  auto last = [&](f32x16 (&s_cur)[JT], const __bf16 *vb) {
-    bf16x8 pf[2 * JT];
-    exp_pack(s_cur, pf);
-    pv(pf, vb);
-  };
-
   // Software pipeline over the row's live tiles u = 0 .. n-1: tile u's K
-  // sits in K0 (u even) or K1 (u odd), its V likewise in V0 / V1.  At the top
-  // of iteration t, K_{t+1} and V_t are in LDS, S_t is in registers and its
-  // row max is known; the iteration starts the copies of K_{t+2} and V_{t+1}
-  // into the buffers freed by iteration t-1, computes the QK^T of tile t+1
-  // beside the softmax of tile t, and waits for its own copies before the
-  // next barrier.  The loop is unrolled by two so every buffer is a
-  // compile-time object.
+  // sits in K0 (u even) or K1 (u odd), its V likewise in V0 / V1.  Step t
+  // has two phases separated by block barriers:
+  //   S_t: K_{t+1} has landed; copy V_{t+1} into the V buffer PV(t-1) freed;
+  //        then QK^T of tile t+1 beside the exponentials of tile t.
+  //   M_t: V_t has landed; copy K_{t+3} into the K buffer QK(t+1) freed;
+  //        then PV of tile t beside the row max of tile t+1.
+  // Each copy thus has one and a half steps to land.  Every phase issues the
+  // same vector-memory instructions (S: one column fetch + IPW copies, M: IPW
+  // copies; indices past the row's end are clamped, so the last copies are
+  // redundant but harmless), so waiting until at most 2*IPW+1 are in flight
+  // is exactly "the copy this phase needs has landed".  Column indices come
+  // from a vector load two steps ahead (lane 0: K column for M_{t+2}, lane 1:
+  // V column for S_{t+2}); a scalar load in flight would force every LDS wait
+  // in between to drain completely.
   const int n = end - beg;
   const int32_t *cols = col_idx + beg;
-  // Column indices of the next step's copies travel through a vector load
-  // (lane 0: next K tile, lane 1: next V tile) issued one step ahead: a
-  // scalar load in flight would force every LDS wait in between to drain
-  // completely, since scalar loads may return out of order.
-  auto fetch_cols = [&](int kpos, int vpos) -> int { return cols[lane == 0 ? kpos : vpos]; };
+  auto col_at = [&](int u) -> int { return cols[min(u, n - 1)]; };
+  auto fetch_cols = [&](int kpos, int vpos) -> int { return col_at(lane == 0 ? kpos : vpos); };
+  constexpr int kVmInFlight = 2 * IPW + 1;
+  constexpr int kVmWait = (kVmInFlight & 15) | (7 << 4) | (15 << 8) | ((kVmInFlight >> 4) << 14);
+  static_assert(kVmInFlight < 64, "vmcnt holds 6 bits");
+  // Block barrier without the release fence of __syncthreads(), which would
+  // drain every copy in flight; the explicit vmcnt waits above provide the
+  // ordering, and the memory clobber keeps LDS accesses on their side.
+  auto block_barrier = []() { asm volatile("s_barrier" ::: "memory"); };
+
   f32x16 s_a[JT], s_b[JT];
-  float mx_a, mx_b;
-  load_k(cols[0], K0);
-  load_v(cols[0], V0);
-  if (n > 1) load_k(cols[1], K1);
-  int cv = fetch_cols(min(2, n - 1), min(1, n - 1));
+  float mx_a = 0.f, mx_b = 0.f;
+  int cv0 = fetch_cols(3, 1);  // for S_0 / M_0
+  int cv1 = fetch_cols(4, 2);  // for S_1 / M_1
+  load_k(col_at(0), K0);
+  load_v(col_at(0), V0);
+  load_k(col_at(1), K1);
+  const int k2 = col_at(2);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   qk(K0, s_a);
   mx_a = tile_max(s_a);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();  // M_{-1}: K0 free
+  load_k(k2, K0);
+
+  // One step; Kq is K[(t+1)%2], Vn is V[(t+1)%2], Vc is V[t%2].  MORE:
+  // tile t+1 exists (every step but the row's last).
+  auto step = [&](auto more_tag, int t, __bf16 *Kq, __bf16 *Vn, const __bf16 *Vc,
+                  f32x16 (&s_cur)[JT], f32x16 (&s_nxt)[JT], float &mx_cur, float &mx_nxt,
+                  int &cv) {
+    constexpr bool MORE = decltype(more_tag)::value;
+    __builtin_amdgcn_s_waitcnt(kVmWait);  // K_{t+1} landed (this wave's part)
+    __builtin_amdgcn_sched_barrier(0);
+    block_barrier();
+    const int kcol = __builtin_amdgcn_readlane(cv, 0);  // column of tile t+3
+    const int vcol = __builtin_amdgcn_readlane(cv, 1);  // column of tile t+1
+    cv = fetch_cols(t + 5, t + 3);
+    load_v(vcol, Vn);
+    rescale(mx_cur);
+    bf16x8 pf[2 * JT];
+    if constexpr (MORE) qk(Kq, s_nxt);
+    exp_pack(s_cur, pf);
+    if constexpr (MORE) sched_interleave<JT * QC, JT * QC, kReadAheadK, 3 * 16 * JT / (JT * QC) + 1>();
+    __builtin_amdgcn_s_waitcnt(kVmWait);  // V_t landed
+    __builtin_amdgcn_sched_barrier(0);
+    block_barrier();
+    load_k(kcol, Kq);
+    pv(pf, Vc);
+    if constexpr (MORE) {
+      mx_nxt = tile_max(s_nxt);
+      sched_interleave<JT * 2 * DT, 4 * JT * DT, kReadAheadV, 1>();
+    } else {
+      sched_interleave<JT * 2 * DT, 4 * JT * DT, kReadAheadV, 0>();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using More = std::true_type;
+  using Last = std::false_type;
   int t = 0;
   for (; t + 2 < n; t += 2) {
-    __syncthreads();  // DMA of the previous iteration visible; K0 and V1 free
-    {
-      const int kc = __builtin_amdgcn_readlane(cv, 0), vc = __builtin_amdgcn_readlane(cv, 1);
-      cv = fetch_cols(min(t + 3, n - 1), t + 2);  // ahead of the copies: waits for it skip them
-      load_k(kc, K0);  // tile t + 2
-      load_v(vc, V1);  // tile t + 1
-    }
-    rescale(mx_a);
-    step(K1, s_b, s_a, V0, mx_b);
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_sched_barrier(0);  // keep the compute regions between the barriers
-    __syncthreads();  // K1 and V0 free
-    {
-      const int kc = __builtin_amdgcn_readlane(cv, 0), vc = __builtin_amdgcn_readlane(cv, 1);
-      cv = fetch_cols(min(t + 4, n - 1), min(t + 3, n - 1));
-      load_k(kc, K1);  // tile min(t + 3, n - 1)
-      load_v(vc, V0);  // tile t + 2
-    }
-    rescale(mx_b);
-    step(K0, s_a, s_b, V1, mx_a);
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_sched_barrier(0);  // keep the compute regions between the barriers
+    step(More{}, t, K1, V1, V0, s_a, s_b, mx_a, mx_b, cv0);
+    step(More{}, t + 1, K0, V0, V1, s_b, s_a, mx_b, mx_a, cv1);
   }
-  if (t + 1 < n) {  // one more steady step: tile t (even) with V0, K_{t+1} in K1
-    __syncthreads();
-    load_v(__builtin_amdgcn_readlane(cv, 1), V1);  // tile t + 1
-    rescale(mx_a);
-    step(K1, s_b, s_a, V0, mx_b);
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_sched_barrier(0);  // keep the compute regions between the barriers
-    __syncthreads();
-    rescale(mx_b);
-    last(s_b, V1);
+  if (t + 1 < n) {
+    step(More{}, t, K1, V1, V0, s_a, s_b, mx_a, mx_b, cv0);
+    step(Last{}, t + 1, K0, V0, V1, s_b, s_a, mx_b, mx_a, cv1);
   } else {
-    __syncthreads();
-    rescale(mx_a);
-    last(s_a, V0);
+    step(Last{}, t, K1, V1, V0, s_a, s_b, mx_a, mx_b, cv0);
   }
+  __builtin_amdgcn_s_waitcnt(0);  // no copy may still be landing in the buffers reused below
 
   float l_tot = sum_xor32(l_run);
   if constexpr (KSPLIT == 2) {

@@ -13,7 +13,7 @@
 // Work item = (batch, position); one workgroup of four waves, wave w owning
 // heads 16w .. 16w+15 over all of d.  Slots are processed in chunks of 32
 // whose rows are copied straight from HBM into LDS (one
-// global_load_lds_dwordx4 per 1 KiB row; slots without a valid index get a
+// buffer_load_dwordx4 ... lds per 1 KiB row; slots without a valid index get a
 // zero row), one chunk ahead into the other of two buffers, so the one
 // gather serves all heads of the position.  Every wave computes
 //   S^T = KV Q^T       (16x16x32 MFMA, Q^T resident in registers)
@@ -35,6 +35,8 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMaxFloor = -1e30f;
 constexpr float kLazy = 8.0f;  // tolerated staleness of the running max (log2 units)
+constexpr int kReadAheadS = 6;   // KV row reads issued before the first score MFMA
+constexpr int kReadAheadV = 12;  // KV transpose reads issued before the first PV MFMA
 
 template <int D>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
@@ -82,15 +84,14 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
   };
   auto valid = [&](int my) -> int { return (my >= 0 && my < N) ? my : -1; };
   // Copy rows wid*RPW .. wid*RPW+RPW-1 of a chunk into `dst`.
+  const __amdgpu_buffer_rsrc_t kv_rs = make_rsrc(kvb, (uint32_t)((int64_t)N * D * 2));
   auto gather = [&](int my, __bf16 *dst) {
 #pragma unroll
     for (int j = 0; j < RPW; ++j) {
       const int row = wid * RPW + j;
       const int src = __builtin_amdgcn_readlane(my, row);
       if (src >= 0) {
-        __builtin_amdgcn_global_load_lds(
-            (__attribute__((address_space(1))) void *)(kvb + (int64_t)src * D + lane * 8),
-            (__attribute__((address_space(3))) void *)(dst + row * STR), 16, 0, 0);
+        copy16_to_lds(kv_rs, dst + row * STR, (uint32_t)(lane * 16), (uint32_t)src * (uint32_t)(D * 2));
       } else {
         *reinterpret_cast<bf16x8 *>(dst + row * STR + lane * 8) = bf16x8{};
       }
@@ -112,6 +113,7 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
         const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kb + (16 * jt + li) * STR + 32 * c + 8 * G);
         s[jt] = mfma16(a, qf[c], s[jt]);
       }
+    sched_interleave<2 * QC, 2 * QC, kReadAheadS, 0>();
     float mx = -__builtin_inff();
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt)
@@ -149,6 +151,7 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
       const bf16x8 a = cat4(lds_read_tr4(rows + 16 * dt), lds_read_tr4(rows + 16 * STR + 16 * dt));
       acc[dt] = mfma16(a, pf, acc[dt]);
     }
+    sched_interleave<DT, 2 * DT, kReadAheadV, 0>();
   };
   // my_cur: validated rows of chunk ch; raw_next: unvalidated entries of
   // chunk ch + 1.
