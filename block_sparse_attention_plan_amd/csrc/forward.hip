@@ -641,26 +641,29 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
       }
   };
 
-  float m_run = kMaxFloor;
+  float m_run = kMaxFloor;  // running max (log2 units)
   float l_run = 0.f;
   f32x16 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
 
-  // Row maximum of a score tile in log2 units (lane column = query row).
+  // This lane's maximum of a raw score tile.  The cross-lane step of the row
+  // maximum is only needed when the running max moves, so it sits inside
+  // the rescale branch; the test itself is a wave vote.
   auto tile_max = [&](const f32x16 (&s)[JT]) -> float {
     float mx = s[0][0];
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[jt][e]);
-    return max_xor32(mx) * scale_log2;
+    return mx;
   };
-  // Move the running max only when a row's tile max exceeds it by more than
-  // kLazy; the accumulators are rescaled on those (rare) tiles alone.
+  // The running max moves only when some score of a tile exceeds it by more
+  // than kLazy (log2 units); O and l are rescaled on those (rare) tiles alone.
+  // The first tile always moves it off the finite floor (alpha = 0 there).
   auto rescale = [&](float mx) {
-    if (__any(mx > m_run + kLazy)) {
-      const float m_new = fmaxf(m_run, mx);
+    if (__any(mx * scale_log2 > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, max_xor32(mx) * scale_log2);
       const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
@@ -668,7 +671,6 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
       for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
     }
   };
-  // P = exp2(S * scale - m) packed to bf16 in the k order of the PV operand.
   auto exp_pack = [&](const f32x16 (&s)[JT], bf16x8 (&pf)[2 * JT]) {
     float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -761,7 +763,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     bf16x8 pf[2 * JT];
     if constexpr (MORE) qk(Kq, s_nxt);
     exp_pack(s_cur, pf);
-    if constexpr (MORE) sched_interleave<JT * QC, JT * QC, kReadAheadK, 3 * 16 * JT / (JT * QC) + 1>();
+    if constexpr (MORE) sched_interleave<JT * QC, JT * QC, kReadAheadK, 3 * 16 * JT / (JT * QC)>();
     __builtin_amdgcn_s_waitcnt(kVmWait);  // V_t landed
     __builtin_amdgcn_sched_barrier(0);
     block_barrier();
