@@ -268,3 +268,51 @@ def test_forward_growing_scores(gpu, bs, d):
     err = np.abs(lse.cpu().numpy()[fin] - ref_lse[fin]) / np.maximum(1.0, np.abs(ref_lse[fin]))
     say(f"  lse rel err {err.max():.2e}")
     assert err.max() <= 1e-3
+
+
+# ------------------------------------------------------------- edge cases
+
+def test_plan_widest_row(gpu):
+    """Block rows as wide as the planner accepts (16384 columns), a few ragged
+    densities, one row empty and one full."""
+    H, Mb, Nb = 2, 3, 16384
+    rng = np.random.default_rng(11)
+    lay = (rng.random((H, Mb, Nb)) < np.array([0.001, 0.3, 0.9])[None, :, None]).astype(np.int32)
+    lay[0, 0, :] = 0
+    lay[1, 2, :] = 1
+    say(f"[plan] widest rows H={H} Mb={Mb} Nb={Nb}")
+    check_plan(gpu, lay)
+
+
+def test_topk_out_of_range_indices_act_as_missing(gpu):
+    """Entries outside [0, N) other than -1 are documented to contribute
+    nothing, exactly as -1 does: the result equals the oracle's on the same
+    input with those entries replaced by -1."""
+    x = W.make_topk("topk_oob", B=1, M=5, H=24, d=512, N=90, topk=70, seed=21, drop=0.1)
+    idx = x.idx.clone()
+    idx[0, 0, 3] = 90            # == N
+    idx[0, 1, 0] = 1 << 30
+    idx[0, 2, 69] = -7
+    idx[0, 3, :40] = -2          # a leading run of bad entries
+    say("[topk] out-of-range entries")
+    out = bsa.topk_sparse_attn(x.q.to(gpu), x.kv.to(gpu), idx.to(gpu), x.sink.to(gpu), x.scale)
+    torch.cuda.synchronize()
+    clean = idx.numpy().copy()
+    clean[(clean < 0) | (clean >= 90)] = -1
+    ref = O.topk_attention(to64(x.q), to64(x.kv), clean, x.sink.numpy(), x.scale)
+    compare(to64(out), ref, "topk out-of-range entries")
+
+
+def test_topk_duplicates_and_late_valid_slots(gpu):
+    """Repeated rows count once per slot; a position whose first chunks hold
+    no valid slot starts its running max from a later chunk."""
+    x = W.make_topk("topk_dup", B=2, M=4, H=64, d=512, N=50, topk=50, seed=22, drop=0.0)  # q, kv, sink
+    rng = np.random.default_rng(23)
+    idx = torch.from_numpy(rng.integers(0, 50, (2, 4, 160)).astype(np.int32))  # with repeats
+    idx[0, 1, :130] = -1         # only the last chunk holds valid slots
+    idx[1, 2, :] = 7             # one row, 160 times
+    say("[topk] duplicates and late valid slots")
+    out = bsa.topk_sparse_attn(x.q.to(gpu), x.kv.to(gpu), idx.to(gpu), x.sink.to(gpu), x.scale)
+    torch.cuda.synchronize()
+    ref = O.topk_attention(to64(x.q), to64(x.kv), idx.numpy(), x.sink.numpy(), x.scale)
+    compare(to64(out), ref, "topk duplicates")
