@@ -710,19 +710,23 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   //        then QK^T of tile t+1 beside the exponentials of tile t.
   //   M_t: V_t has landed; copy K_{t+3} into the K buffer QK(t+1) freed;
   //        then PV of tile t beside the row max of tile t+1.
-  // Each copy thus has one and a half steps to land.  Every phase issues the
-  // same vector-memory instructions (S: one column fetch + IPW copies, M: IPW
-  // copies; indices past the row's end are clamped, so the last copies are
-  // redundant but harmless), so waiting until at most 2*IPW+1 are in flight
-  // is exactly "the copy this phase needs has landed".  Column indices come
-  // from a vector load two steps ahead (lane 0: K column for M_{t+2}, lane 1:
-  // V column for S_{t+2}); a scalar load in flight would force every LDS wait
-  // in between to drain completely.
+  // Each copy thus has one and a half steps to land.  Every phase issues
+  // IPW copies (indices past the row's end are clamped, so the last copies
+  // are redundant but harmless) and S_t also a column fetch, so the copy a
+  // phase needs is followed by 2*IPW copies and at most two fetches: waiting
+  // until at most 2*IPW vector-memory loads are in flight proves it has
+  // landed, since loads complete in issue order.  (The count leaves the
+  // fetches out because the compiler deletes those whose result is dead, in
+  // a row's last steps; a spill store in between cannot loosen the wait, as
+  // it only adds to the count.)  Column indices come from a vector load two
+  // steps ahead (lane 0: K column for M_{t+2}, lane 1: V column for S_{t+2});
+  // a scalar load in flight would force every LDS wait in between to drain
+  // completely.
   const int n = end - beg;
   const int32_t *cols = col_idx + beg;
   auto col_at = [&](int u) -> int { return cols[min(u, n - 1)]; };
   auto fetch_cols = [&](int kpos, int vpos) -> int { return col_at(lane == 0 ? kpos : vpos); };
-  constexpr int kVmInFlight = 2 * IPW + 1;
+  constexpr int kVmInFlight = 2 * IPW;
   constexpr int kVmWait = (kVmInFlight & 15) | (7 << 4) | (15 << 8) | ((kVmInFlight >> 4) << 14);
   static_assert(kVmInFlight < 64, "vmcnt holds 6 bits");
   // Block barrier without the release fence of __syncthreads(), which would
