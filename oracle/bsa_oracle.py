@@ -22,6 +22,10 @@ Sources (web pages; cite by title and section):
 * "Block-Sparse Attention" (Language AI Handbook), "Block Structure" -- each
   b x b block pair is a dense piece of work; its create_block_sparse_mask example
   expands a block pattern into a token-level boolean mask.
+* "ejkernel: BlockSparseAttention" (ejkernel operations page), the operation's
+  arguments -- ``softmax_aux`` (values added to the scores for attention sinks),
+  ``logits_soft_cap`` (tanh capping of the logits, Gemma-2 style), ``causal``
+  (causal masking) and ``kv_num_heads`` for keys and values (grouped heads).
 * DeepSeek-V4.1 "Sparse attention / Weighted row sum" page, code excerpt of
   sparse_attn_kernel and sparse_attn -- per query position the top-k KV rows are
   gathered by index (the same rows for every head, -1 marks an unused slot),
@@ -34,7 +38,15 @@ Readings where the pages are silent (each is listed in the design notes):
 
 * A query row whose block row holds no live tile has out = 0 and lse = -inf.
 * lse is the natural logarithm of the softmax denominator, sum_j exp(s_ij).
-* Causality lives only in the layout (no mask inside a tile).
+* Causality lives in the layout unless ``causal`` is set; then, in addition,
+  key position j is masked for query position i whenever j > i (positions
+  counted from 0 in both sequences).
+* The soft cap maps the scaled score s to cap * tanh(s / cap), before masking.
+* A block-sparse sink is one logit per query head that adds exp(sink_h) to the
+  denominator, like the top-k sink (not scaled, not capped); lse includes it,
+  so a row with no live key then has out = 0 and lse = sink_h.
+* With kv_heads = H / g, query head h reads key/value head h // g (groups of
+  g consecutive query heads share one K/V head).
 * Sequence lengths are multiples of the block size.
 * An absent sink (None) is the same as a sink of -infinity.
 * Duplicate top-k indices count once per occurrence.
@@ -140,30 +152,58 @@ def _as64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def attention_dense_masked(q, k, v, layout, bs: int, scale: float
+def _kv_head(H: int, Hkv: int):
+    """Map query head -> key/value head for grouped heads (h // (H / Hkv))."""
+    if Hkv <= 0 or H % Hkv:
+        raise ValueError("the number of query heads must be a multiple of the K/V heads")
+    g = H // Hkv
+    return lambda h: h // g
+
+
+def _cap(s: np.ndarray, soft_cap: Optional[float]) -> np.ndarray:
+    return s if not soft_cap else soft_cap * np.tanh(s / soft_cap)
+
+
+def attention_dense_masked(q, k, v, layout, bs: int, scale: float, *, sink=None,
+                           soft_cap: Optional[float] = None, causal: bool = False
                            ) -> Tuple[np.ndarray, np.ndarray]:
     """Dense definition with non-live tiles masked to -inf.
 
-    q: [B, H, Sq, d]; k, v: [B, H, Sk, d]; layout [H, Sq/bs, Sk/bs].
-    Returns out [B, H, Sq, d] and lse [B, H, Sq] (natural log).
+    q: [B, H, Sq, d]; k, v: [B, Hkv, Sk, d] with H a multiple of Hkv; layout
+    [H, Sq/bs, Sk/bs].  Returns out [B, H, Sq, d] and lse [B, H, Sq] (natural
+    log).
 
     Scores s = scale * q k^T (next.gr tutorial, "Scaled Dot-Product Attention"),
-    entries outside the layout set to -inf (its Longformer formula), then one
-    softmax across the whole key axis of each row and a product with v.  Rows
-    with no live key give out = 0 and lse = -inf.
+    optionally capped to soft_cap * tanh(s / soft_cap), entries outside the
+    layout (and, when causal, above the diagonal) set to -inf (its Longformer
+    formula), then one softmax across the whole key axis of each row -- whose
+    denominator also holds exp(sink_h) when a sink is given -- and a product
+    with v.  Rows with no live key give out = 0 and lse = -inf (sink_h with a
+    sink).
     """
     q, k, v = _as64(q), _as64(k), _as64(v)
     B, H, Sq, d = q.shape
+    Sk = k.shape[2]
+    kvh = _kv_head(H, k.shape[1])
+    k = k[:, [kvh(h) for h in range(H)]]
+    v = v[:, [kvh(h) for h in range(H)]]
     mask = token_mask(layout, bs)
-    if mask.shape != (H, Sq, k.shape[2]):
+    if mask.shape != (H, Sq, Sk):
         raise ValueError("layout does not match q/k shapes")
-    s = scale * np.matmul(q, np.swapaxes(k, -1, -2))
+    if causal:
+        mask = mask & (np.arange(Sk)[None, None, :] <= np.arange(Sq)[None, :, None])
+    s = _cap(scale * np.matmul(q, np.swapaxes(k, -1, -2)), soft_cap)
     s = np.where(mask[None], s, -np.inf)
     row_max = s.max(axis=-1, keepdims=True)
+    sk = None if sink is None else _as64(sink)[None, :, None, None]
+    if sk is not None:
+        row_max = np.maximum(row_max, sk)
     has_live = np.isfinite(row_max)
     shift = np.where(has_live, row_max, 0.0)
     e = np.exp(s - shift)  # exp(-inf) == 0 exactly
     den = e.sum(axis=-1, keepdims=True)
+    if sk is not None:
+        den = den + np.exp(sk - shift)
     with np.errstate(invalid="ignore", divide="ignore"):
         p = np.where(has_live, e / np.where(has_live, den, 1.0), 0.0)
         lse = np.where(has_live[..., 0], shift[..., 0] + np.log(np.where(has_live, den, 1.0))[..., 0],
@@ -173,23 +213,27 @@ def attention_dense_masked(q, k, v, layout, bs: int, scale: float
 
 
 def attention_live_tiles(q, k, v, layout, bs: int, scale: float,
-                         row_blocks: Optional[Iterable[Tuple[int, int, int]]] = None
+                         row_blocks: Optional[Iterable[Tuple[int, int, int]]] = None, *,
+                         sink=None, soft_cap: Optional[float] = None, causal: bool = False
                          ) -> Tuple[np.ndarray, np.ndarray]:
     """Same definition evaluated over the live tiles of each row only.
 
     Because exp(-inf) is exactly zero, dropping the masked keys leaves the
     softmax of every row unchanged; this form touches n*k*b score entries
-    instead of n^2 (Language AI Handbook, "Block Structure").
+    instead of n^2 (Language AI Handbook, "Block Structure").  The options have
+    the meaning given in attention_dense_masked.
 
     ``row_blocks`` optionally restricts the work to a list of (b, h, m) query
     blocks; rows not computed are left as NaN in the returned arrays.
     """
     q, k, v = _as64(q), _as64(k), _as64(v)
     B, H, Sq, d = q.shape
+    kvh = _kv_head(H, k.shape[1])
     lay = np.asarray(layout) != 0
     Mb = Sq // bs
     if lay.shape[0] != H or lay.shape[1] != Mb or lay.shape[2] * bs != k.shape[2]:
         raise ValueError("layout does not match q/k shapes")
+    sk = None if sink is None else _as64(sink)
     out = np.full((B, H, Sq, v.shape[3]), np.nan)
     lse = np.full((B, H, Sq), np.nan)
     if row_blocks is None:
@@ -198,19 +242,24 @@ def attention_live_tiles(q, k, v, layout, bs: int, scale: float,
     for (b, h, m) in row_blocks:
         rows = slice(m * bs, (m + 1) * bs)
         cols = np.flatnonzero(lay[h, m])
-        if cols.size == 0:
-            out[b, h, rows] = 0.0
-            lse[b, h, rows] = -np.inf
-            continue
         tok = (cols[:, None] * bs + offs[None, :]).reshape(-1)
-        kk = k[b, h, tok]
-        vv = v[b, h, tok]
-        s = scale * (q[b, h, rows] @ kk.T)
-        mx = s.max(axis=1, keepdims=True)
-        e = np.exp(s - mx)
-        den = e.sum(axis=1, keepdims=True)
-        out[b, h, rows] = (e @ vv) / den
-        lse[b, h, rows] = mx[:, 0] + np.log(den[:, 0])
+        s = _cap(scale * (q[b, h, rows] @ k[b, kvh(h), tok].T), soft_cap)   # [bs, T]
+        if causal:
+            qpos = m * bs + offs
+            s = np.where(tok[None, :] <= qpos[:, None], s, -np.inf)
+        mx = s.max(axis=1) if tok.size else np.full(bs, -np.inf)
+        if sk is not None:
+            mx = np.maximum(mx, sk[h])
+        live = np.isfinite(mx)
+        shift = np.where(live, mx, 0.0)
+        e = np.exp(s - shift[:, None])
+        den = e.sum(axis=1)
+        if sk is not None:
+            den = den + np.exp(sk[h] - shift)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            o = (e @ v[b, kvh(h), tok]) / np.where(live, den, 1.0)[:, None]
+            out[b, h, rows] = np.where(live[:, None], o, 0.0)
+            lse[b, h, rows] = np.where(live, shift + np.log(np.where(live, den, 1.0)), -np.inf)
     return out, lse
 
 

@@ -457,3 +457,148 @@ def test_band_layout_count_closed_form():
     p = O.plan(lay)
     assert p.nnz_total == 8 * (nb * (2 * w + 1) - w * (w + 1)) == 8 * 556
     assert round(100 * (1 - 556 / nb ** 2), 2) == 86.43
+
+
+# ------------------------------------------- forward options (sink, cap, causal, GQA)
+
+BOTH = (O.attention_dense_masked, O.attention_live_tiles)
+
+
+def test_causal_full_layout_is_causal_sdpa():
+    """causal with every tile live is torch's causal scaled dot-product
+    attention; so is causal with the lower-triangular block layout, since the
+    tiles above the diagonal are fully masked anyway."""
+    B, H, S, d, bs, scale = 2, 2, 48, 8, 16, 0.41
+    q, k, v = rnd((B, H, S, d), 61), rnd((B, H, S, d), 62), rnd((B, H, S, d), 63)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=scale).numpy()
+    full = np.ones((H, S // bs, S // bs), np.int32)
+    lower = np.tril(full)
+    for fn in BOTH:
+        for lay in (full, lower):
+            out, lse = fn(q, k, v, lay, bs, scale, causal=True)
+            np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    # row 0 of every head sees only key 0: its output is v[.., 0, :]
+    out, lse = O.attention_live_tiles(q, k, v, lower, bs, scale, causal=True)
+    np.testing.assert_allclose(out[:, :, 0], v[:, :, 0], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse[:, :, 0], scale * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0]),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_causal_masks_tiles_above_the_diagonal():
+    """A block row whose only live tiles lie above the diagonal has no
+    visible key under causal: zeros and -inf, as for an empty row."""
+    B, H, S, d, bs = 1, 1, 32, 4, 8
+    q, k, v = rnd((B, H, S, d), 64), rnd((B, H, S, d), 65), rnd((B, H, S, d), 66)
+    lay = np.zeros((H, 4, 4), np.int32)
+    lay[0, 1, 2:] = 1            # strictly above the diagonal
+    lay[0, 2, :3] = 1
+    for fn in BOTH:
+        out, lse = fn(q, k, v, lay, bs, 0.5, causal=True)
+        assert np.all(out[0, 0, bs:2 * bs] == 0) and np.all(np.isneginf(lse[0, 0, bs:2 * bs]))
+        assert np.all(np.isfinite(lse[0, 0, 2 * bs:3 * bs]))
+
+
+def test_grouped_heads_match_repeated_heads_and_sdpa():
+    """kv_heads = H / g: query head h reads K/V head h // g.  Equal to the
+    ungrouped oracle with every K/V head repeated g times in a row, and to
+    torch's scaled dot-product attention with enable_gqa."""
+    B, H, Hkv, S, d, bs, scale = 1, 6, 2, 32, 8, 8, 0.3
+    q, k, v = rnd((B, H, S, d), 67), rnd((B, Hkv, S, d), 68), rnd((B, Hkv, S, d), 69)
+    lay = np.ones((H, S // bs, S // bs), np.int32)
+    kr, vr = np.repeat(k, H // Hkv, axis=1), np.repeat(v, H // Hkv, axis=1)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale, enable_gqa=True).numpy()
+    for fn in BOTH:
+        out, lse = fn(q, k, v, lay, bs, scale)
+        rep, rep_lse = fn(q, kr, vr, lay, bs, scale)
+        np.testing.assert_allclose(out, rep, rtol=0, atol=0)
+        np.testing.assert_allclose(lse, rep_lse, rtol=0, atol=0)
+        np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    with pytest.raises(ValueError):
+        O.attention_live_tiles(q, rnd((B, 4, S, d), 1), rnd((B, 4, S, d), 2), lay, bs, scale)
+
+
+def test_sink_closed_form_with_zero_queries():
+    """q = 0 makes every visible score 0: out = (sum of visible v) /
+    (n + e^sink) and lse = ln(n + e^sink); the sink only lowers the total
+    weight on the real keys (DeepSeek-V4.1 sink term)."""
+    B, H, S, d, bs = 1, 3, 32, 4, 8
+    q = np.zeros((B, H, S, d))
+    k, v = rnd((B, H, S, d), 70), rnd((B, H, S, d), 71)
+    rng = np.random.default_rng(72)
+    lay = (rng.random((H, 4, 4)) < 0.5).astype(np.int32)
+    lay[:, :, 0] = 1
+    sink = np.array([-1.0, 0.5, 3.0])
+    mask = token_mask_by_lookup(lay, bs)
+    n = mask.sum(-1)                                     # [H, S]
+    vsum = np.einsum("hij,bhjd->bhid", mask.astype(float), v)
+    ref = vsum / (n + np.exp(sink)[:, None])[None, :, :, None]
+    for fn in BOTH:
+        out, lse = fn(q, k, v, lay, bs, 0.7, sink=sink)
+        np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse[0], np.log(n + np.exp(sink)[:, None]), rtol=1e-12)
+
+
+def test_sink_limits():
+    """A sink of -1e9 is no sink; with a sink, a row without a visible key
+    has out = 0 and lse = sink_h."""
+    B, H, S, d, bs = 2, 2, 24, 4, 8
+    q, k, v = rnd((B, H, S, d), 73), rnd((B, H, S, d), 74), rnd((B, H, S, d), 75)
+    lay = np.ones((H, 3, 3), np.int32)
+    lay[1, 2, :] = 0
+    sink = np.array([0.25, -0.75])
+    for fn in BOTH:
+        base, base_lse = fn(q, k, v, lay, bs, 0.6)
+        off, off_lse = fn(q, k, v, lay, bs, 0.6, sink=np.full(H, -1e9))
+        np.testing.assert_allclose(off, base, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(off_lse[np.isfinite(base_lse)], base_lse[np.isfinite(base_lse)], rtol=1e-12)
+        out, lse = fn(q, k, v, lay, bs, 0.6, sink=sink)
+        assert np.all(out[:, 1, 2 * bs:] == 0)
+        np.testing.assert_allclose(lse[:, 1, 2 * bs:], -0.75)
+        live = np.isfinite(base_lse)
+        assert np.all(lse[live] > base_lse[live])        # the denominator only grows
+
+
+def test_soft_cap_limits():
+    """A huge cap changes nothing; with scores driven to +-infinity the capped
+    logits saturate at +-cap, so two visible keys get weights
+    e^(+-cap) / (e^cap + e^-cap) (tanh capping, Gemma-2 style)."""
+    B, H, S, d, bs = 1, 2, 16, 4, 8
+    q, k, v = rnd((B, H, S, d), 76), rnd((B, H, S, d), 77), rnd((B, H, S, d), 78)
+    lay = np.ones((H, 2, 2), np.int32)
+    for fn in BOTH:
+        a, la = fn(q, k, v, lay, bs, 0.5)
+        b_, lb = fn(q, k, v, lay, bs, 0.5, soft_cap=1e8)
+        np.testing.assert_allclose(b_, a, rtol=1e-10, atol=1e-10)
+        np.testing.assert_allclose(lb, la, rtol=1e-10)
+    # saturation: one query row, two keys with scores +-1e6
+    q1 = np.zeros((1, 1, 2, 2)); q1[..., 0] = 1.0
+    k1 = np.zeros((1, 1, 2, 2)); k1[0, 0, 0, 0] = 1e6; k1[0, 0, 1, 0] = -1e6
+    v1 = np.array([[[[1.0, 0.0], [0.0, 1.0]]]])
+    lay1 = np.ones((1, 1, 1), np.int32)
+    cap = 1.5
+    for fn in BOTH:
+        out, lse = fn(q1, k1, v1, lay1, 2, 0.5, soft_cap=cap)   # capping after scaling
+        w = np.exp(cap) / (np.exp(cap) + np.exp(-cap))
+        np.testing.assert_allclose(out[0, 0, 0], [w, 1 - w], rtol=1e-12)
+        np.testing.assert_allclose(lse[0, 0, 0], np.log(np.exp(cap) + np.exp(-cap)), rtol=1e-12)
+        assert np.all(np.abs(lse) <= cap + np.log(2) + 1e-12)
+
+
+def test_options_dense_and_live_tile_forms_agree():
+    """All options together on random layouts, grouped heads and a ragged
+    block grid: the dense and the live-tile forms give the same result."""
+    B, H, Hkv, bs, d = 2, 4, 2, 8, 6
+    Mb, Nb = 5, 5
+    rng = np.random.default_rng(79)
+    q = rnd((B, H, Mb * bs, d), 80)
+    k, v = rnd((B, Hkv, Nb * bs, d), 81), rnd((B, Hkv, Nb * bs, d), 82)
+    lay = (rng.random((H, Mb, Nb)) < 0.5).astype(np.int32)
+    lay[0, 2] = 0
+    sink = rnd((H,), 83)
+    kw = dict(sink=sink, soft_cap=2.5, causal=True)
+    a, la = O.attention_dense_masked(q, k, v, lay, bs, 0.45, **kw)
+    b_, lb = O.attention_live_tiles(q, k, v, lay, bs, 0.45, **kw)
+    np.testing.assert_allclose(b_, a, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lb, la, rtol=1e-12)
