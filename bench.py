@@ -15,10 +15,16 @@ average duration.
 Prints ONE JSON line.  `value` = live-tile FLOPs of the step (4*b^2*d per live
 tile per head per batch item + 4*d*H per valid top-k index) / step time.
 
+After the timed steps, the forward with all of its optional terms (causal
+mask, per-head sink, tanh logit cap 50, eight K/V heads shared by the 32
+query heads) is timed on the same workload and reported beside the plain
+forward under kernels.bsa_forward_options; it is not part of `value`.
+
 Flags: --gpus N (only 1 is supported), --steps K, --warmup W,
 --no-cpu-baseline (skip the oracle timing), --cpu-seconds S (oracle sample
 budget per kernel), --copy-calibration (also run one plain elementwise copy
-of 1 GiB, for HBM counter scaling under a profiler).
+of 1 GiB, for HBM counter scaling under a profiler), --option-steps N (launches
+of the forward with options; 0 skips that leg).
 
 --summarize-counters FETCH_CSV WRITE_CSV (no GPU needed) turns the counter
 files of two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of
@@ -49,6 +55,7 @@ KERNEL_SOURCES = {
     "bsa_forward": os.path.join(REPO, "block_sparse_attention_plan_amd", "csrc", "forward.hip"),
     "topk_sparse_attn": os.path.join(REPO, "block_sparse_attention_plan_amd", "csrc", "topk.hip"),
 }
+KERNEL_SOURCES["bsa_forward_options"] = KERNEL_SOURCES["bsa_forward"]
 
 
 def log(*a):
@@ -158,7 +165,13 @@ def cpu_baseline(fwd, topk_in, budget_s: float):
 
 
 CALIBRATION_BYTES = float(1 << 30)   # read and written by the calibration copy
-KERNEL_MATCH = {"bsa_forward": "bsa_fwd", "topk_sparse_attn": "topk_kernel"}
+# Kernel-name tests; the forward's plain instances carry template argument
+# `false` (mangled Lb0E) for its options flag, the instances with options `true`.
+KERNEL_MATCH = {
+    "bsa_forward": lambda n: "bsa_fwd" in n and "Lb0E" in n,
+    "bsa_forward_options": lambda n: "bsa_fwd" in n and "Lb1E" in n,
+    "topk_sparse_attn": lambda n: "topk_kernel" in n,
+}
 
 
 def _counter_means(path: str, counter: str):
@@ -187,9 +200,9 @@ def summarize_counters(fetch_csv: str, write_csv: str, out_path: str = TRAFFIC_F
     out = {"_calibration": {"kernel": "elementwise neg over 1 GiB fp32 (reads 1 GiB, writes 1 GiB)",
                             "fetch_kib": cal_f[0], "write_kib": cal_w[0],
                             "fetch_scale": f_scale, "write_scale": w_scale}}
-    for kernel, pat in KERNEL_MATCH.items():
-        fk = [v for k, v in fetch.items() if pat in k]
-        wk = [v for k, v in write.items() if pat in k]
+    for kernel, match in KERNEL_MATCH.items():
+        fk = [v for k, v in fetch.items() if match(k)]
+        wk = [v for k, v in write.items() if match(k)]
         if not fk or not wk:
             continue
         rd, wr = fk[0] * 1024.0 * f_scale, wk[0] * 1024.0 * w_scale
@@ -218,6 +231,7 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--option-steps", type=int, default=20)
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
@@ -287,6 +301,33 @@ def main(argv=None) -> int:
     t_step_ev = sum(e[0].elapsed_time(e[3]) for e in events) / args.steps
     ms_per_step = wall * 1e3 / args.steps
 
+    opt_leg = None
+    if args.option_steps > 0:
+        # same q and layout; K/V = the first 8 heads of k, v, shared by groups of 4
+        hkv = 8
+        k8, v8 = k[:, :hkv].contiguous(), v[:, :hkv].contiguous()
+        sink = W.sink_logits(H, 3.0, 6).to(dev)
+        plan = bsa.bsa_plan(layout, buf=pbuf)
+        kw = dict(out=out, lse=lse, attn_sink=sink, soft_cap=50.0, causal=True)
+        for _ in range(3):
+            bsa.bsa_forward(q, k8, v8, plan, fwd.scale, **kw)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.option_steps):
+            bsa.bsa_forward(q, k8, v8, plan, fwd.scale, **kw)
+        e1.record()
+        torch.cuda.synchronize()
+        t_opt = e0.elapsed_time(e1) / args.option_steps
+        opt_tflops = f_flops / (t_opt * 1e-3) / 1e12
+        opt_leg = {"avg_ms": round(t_opt, 5), "launches": args.option_steps,
+                   "options": {"causal": True, "attn_sink": "N(3,1) per head", "soft_cap": 50.0,
+                               "kv_heads": hkv},
+                   "tflops": round(opt_tflops, 2),
+                   "pct_bf16_peak": round(100 * opt_tflops / PEAK_BF16_TFLOPS, 2),
+                   "traffic": measured_traffic("bsa_forward_options")}
+        log(f"[bench] forward with options: {t_opt:.4f} ms")
+
     if args.copy_calibration:
         # one full-grid elementwise kernel that reads 1 GiB and writes 1 GiB
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -312,6 +353,8 @@ def main(argv=None) -> int:
             "algorithmic_bytes": t_bytes, "algorithmic_gbs": round(topk_gbs, 1),
             "pct_hbm_peak": round(100 * topk_gbs / PEAK_HBM_GBS, 2)},
     }
+    if opt_leg is not None:
+        kernels["bsa_forward_options"] = opt_leg
     # dominant kernel of the step and its roofline
     if t_fwd >= t_topk:
         roof = {"kernel": "bsa_forward", "bound": "mfma", "achieved": round(fwd_tflops, 2),

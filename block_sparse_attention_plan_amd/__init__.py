@@ -7,7 +7,8 @@ memory and the current stream.  There is no CPU fallback: if the library is
 missing, every call raises.
 
     bsa_plan(layout)                      -> Plan   (per-row CSR of live tiles)
-    bsa_forward(q, k, v, plan, scale)     -> (out, lse)
+    bsa_forward(q, k, v, plan, scale, *, attn_sink, soft_cap, causal)
+                                          -> (out, lse)
     topk_sparse_attn(q, kv, idx, attn_sink, scale) -> out
 """
 
@@ -87,6 +88,9 @@ def load_library():
     lib.bsa_forward.argtypes = [vp, vp, vp, ctypes.POINTER(_PlanT), i32, i32, i32, i32, i32, i32,
                                 ctypes.c_int, f32, vp, vp, vp]
     lib.bsa_forward.restype = ctypes.c_int
+    lib.bsa_forward_ex.argtypes = [vp, vp, vp, ctypes.POINTER(_PlanT), i32, i32, i32, i32, i32,
+                                   i32, i32, f32, ctypes.POINTER(_FwdOptsT), vp, vp, vp]
+    lib.bsa_forward_ex.restype = ctypes.c_int
     lib.topk_sparse_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp]
     lib.topk_sparse_attn.restype = ctypes.c_int
     lib.bsa_status_string.argtypes = [ctypes.c_int]
@@ -115,6 +119,15 @@ def _require_gpu(name: str, t: torch.Tensor) -> None:
         raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+class _FwdOptsT(ctypes.Structure):
+    _fields_ = [
+        ("attn_sink", ctypes.c_void_p),
+        ("soft_cap", ctypes.c_float),
+        ("causal", ctypes.c_int32),
+        ("kv_heads", ctypes.c_int32),
+    ]
 
 
 class Plan:
@@ -194,13 +207,18 @@ def bsa_plan_nnz(plan: Plan) -> int:
 
 def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
                 scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                lse: Optional[torch.Tensor] = None, want_lse: bool = True
-                ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                lse: Optional[torch.Tensor] = None, want_lse: bool = True, *,
+                attn_sink: Optional[torch.Tensor] = None, soft_cap: Optional[float] = None,
+                causal: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Block-sparse attention forward.
 
-    q: [B, H, Sq, d], k/v: [B, H, Sk, d], bf16 or fp32, with Sq = Mb*bs and
+    q: [B, H, Sq, d], k/v: [B, Hkv, Sk, d] with H % Hkv == 0 (query head h
+    reads K/V head h // (H // Hkv)), bf16 or fp32, with Sq = Mb*bs and
     Sk = Nb*bs for the plan's layout.  Returns (out [B, H, Sq, d] of q's dtype,
-    lse [B, H, Sq] fp32 or None).  scale defaults to 1/sqrt(d).
+    lse [B, H, Sq] fp32 or None).  scale defaults to 1/sqrt(d).  attn_sink
+    (fp32 [H]) adds exp(attn_sink[h]) to each softmax denominator; soft_cap
+    caps the scaled scores to soft_cap * tanh(s / soft_cap); causal also masks
+    key tokens after the query token.
     """
     for name, t in (("q", q), ("k", k), ("v", v)):
         _require_gpu(name, t)
@@ -209,8 +227,16 @@ def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("q, k, v must share dtype bf16 or fp32")
     B, H, Sq, d = (int(x) for x in q.shape)
-    if tuple(k.shape) != tuple(v.shape) or k.shape[0] != B or k.shape[1] != H or k.shape[3] != d:
-        raise ValueError("k and v must be [B, H, Sk, d] matching q")
+    Hkv = int(k.shape[1])
+    if (tuple(k.shape) != tuple(v.shape) or k.shape[0] != B or k.shape[3] != d or Hkv < 1
+            or H % Hkv != 0):
+        raise ValueError("k and v must be [B, Hkv, Sk, d] matching q, with Hkv dividing H")
+    if attn_sink is not None:
+        _require_gpu("attn_sink", attn_sink)
+        if attn_sink.dtype != torch.float32 or tuple(attn_sink.shape) != (H,):
+            raise ValueError("attn_sink must be fp32 [H]")
+    if soft_cap is not None and not (math.isfinite(soft_cap) and soft_cap > 0):
+        raise ValueError("soft_cap must be finite and > 0")
     Sk = int(k.shape[2])
     if Sq % plan.Mb != 0:
         raise ValueError("Sq must be a multiple of the layout's block rows")
@@ -230,11 +256,19 @@ def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
         if tuple(lse.shape) != (B, H, Sq) or lse.dtype != torch.float32:
             raise ValueError("lse must be fp32 [B, H, Sq]")
     dtype = BSA_BF16 if q.dtype == torch.bfloat16 else BSA_F32
-    _check(load_library().bsa_forward(
+    lse_ptr = ctypes.c_void_p(lse.data_ptr() if lse is not None else 0)
+    if attn_sink is None and soft_cap is None and not causal and Hkv == H:
+        _check(load_library().bsa_forward(
+            ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+            ctypes.c_void_p(v.data_ptr()), ctypes.byref(plan._raw), B, H, Sq, Sk, bs, d, dtype,
+            float(scale), ctypes.c_void_p(out.data_ptr()), lse_ptr, _stream(q)))
+        return out, lse
+    opts = _FwdOptsT(ctypes.c_void_p(attn_sink.data_ptr() if attn_sink is not None else 0),
+                     float(soft_cap or 0.0), 1 if causal else 0, Hkv)
+    _check(load_library().bsa_forward_ex(
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
         ctypes.c_void_p(v.data_ptr()), ctypes.byref(plan._raw), B, H, Sq, Sk, bs, d, dtype,
-        float(scale), ctypes.c_void_p(out.data_ptr()),
-        ctypes.c_void_p(lse.data_ptr() if lse is not None else 0), _stream(q)))
+        float(scale), ctypes.byref(opts), ctypes.c_void_p(out.data_ptr()), lse_ptr, _stream(q)))
     return out, lse
 
 

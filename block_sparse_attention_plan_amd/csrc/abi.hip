@@ -105,9 +105,10 @@ int bsa_plan_nnz(const bsa_plan_t *plan, int64_t *nnz_host, void *stream) {
   return BSA_OK;
 }
 
-int bsa_forward(const void *q, const void *k, const void *v, const bsa_plan_t *plan, int32_t B,
-                int32_t H, int32_t Sq, int32_t Sk, int32_t bs, int32_t d, bsa_dtype_t dtype,
-                float scale, void *out, float *lse, void *stream) {
+int bsa_forward_ex(const void *q, const void *k, const void *v, const bsa_plan_t *plan,
+                   int32_t B, int32_t H, int32_t Sq, int32_t Sk, int32_t bs, int32_t d,
+                   bsa_dtype_t dtype, float scale, const bsa_forward_opts_t *opts, void *out,
+                   float *lse, void *stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
     return fail(BSA_ERR_INVALID_ARG, "bsa_forward: NULL tensor pointer");
   bsa::PlanGeometry g;
@@ -130,12 +131,43 @@ int bsa_forward(const void *q, const void *k, const void *v, const bsa_plan_t *p
     return fail(BSA_ERR_MISALIGNED, "bsa_forward: tensors must be 16-byte aligned");
   const int64_t work = (int64_t)B * plan->H * plan->Mb;
   if (work > 0x7ffffff0LL) return fail(BSA_ERR_UNSUPPORTED, "bsa_forward: problem too large");
+  bsa::FwdOptions fo{nullptr, 0.f, 0.f, 0, 1};
+  if (opts != nullptr) {
+    const int32_t hkv = opts->kv_heads == 0 ? H : opts->kv_heads;
+    if (hkv < 1 || H % hkv != 0)
+      return fail(BSA_ERR_INVALID_ARG, "bsa_forward: kv_heads=%d must divide H=%d",
+                  (int)opts->kv_heads, (int)H);
+    if (!(std::isfinite(opts->soft_cap) && opts->soft_cap >= 0.f))
+      return fail(BSA_ERR_INVALID_ARG, "bsa_forward: soft_cap must be finite and >= 0");
+    if (opts->attn_sink != nullptr && !aligned(opts->attn_sink, 4))
+      return fail(BSA_ERR_MISALIGNED, "bsa_forward: attn_sink must be 4-byte aligned");
+    fo.sink = opts->attn_sink;
+    if (opts->soft_cap > 0.f) {
+      // tanh(x) = 1 - 2 / (exp(2x) + 1) with x = scale * s / cap, evaluated
+      // as exp2(s * cap_k); the kernel multiplies the result by cap_b and
+      // later by scale, so that the capped score is cap * tanh(x).
+      fo.cap_k = (float)(2.0 * (double)scale * 1.4426950408889634 / (double)opts->soft_cap);
+      fo.cap_b = (float)((double)opts->soft_cap / (double)scale);
+      if (!(std::isfinite(fo.cap_k) && std::isfinite(fo.cap_b) && fo.cap_b > 0.f))
+        return fail(BSA_ERR_INVALID_ARG, "bsa_forward: soft_cap %g out of range for scale %g",
+                    (double)opts->soft_cap, (double)scale);
+    }
+    fo.causal = opts->causal != 0;
+    fo.kv_group = H / hkv;
+  }
   hipError_t e = bsa::launch_forward(
       q, k, v, at<int32_t>(plan->dev_buf, g.off_row_ptr), at<int32_t>(plan->dev_buf, g.off_col_idx),
       at<int32_t>(plan->dev_buf, g.off_row_order), B, plan->H, plan->Mb, plan->Nb, bs, d,
-      dtype == BSA_F32, scale, out, lse, (hipStream_t)stream);
+      dtype == BSA_F32, scale, fo, out, lse, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "bsa_forward launch");
   return BSA_OK;
+}
+
+int bsa_forward(const void *q, const void *k, const void *v, const bsa_plan_t *plan, int32_t B,
+                int32_t H, int32_t Sq, int32_t Sk, int32_t bs, int32_t d, bsa_dtype_t dtype,
+                float scale, void *out, float *lse, void *stream) {
+  return bsa_forward_ex(q, k, v, plan, B, H, Sq, Sk, bs, d, dtype, scale, nullptr, out, lse,
+                        stream);
 }
 
 int topk_sparse_attn(const void *q, const void *kv, const int32_t *idx, const float *attn_sink,

@@ -79,6 +79,25 @@ __device__ __forceinline__ float sum2_bf16(bf16x8 x, int i, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(pair, ones, acc, false);
 }
 
+// The tanh logit cap applied to a raw score s (before scaling): returns
+// s' with scale * s' = cap * tanh(scale * s / cap), given k2 =
+// 2 * scale * log2(e) / cap and b = cap / scale; tanh(y) = 1 - 2 / (e^(2y) + 1)
+// saturates cleanly at +-1 when e^(2y) over- or underflows.
+__device__ __forceinline__ float capped_score(float s, float k2, float b) {
+  const float e = __builtin_amdgcn_exp2f(s * k2);
+  return b * fmaf(-2.f, __builtin_amdgcn_rcpf(e + 1.f), 1.f);
+}
+
+// Folds a sink logit (log2 units) into a row's running max m and sum l and
+// returns the factor by which the row's unnormalised output must be scaled.
+__device__ __forceinline__ float fold_sink(float &m, float &l, float sink_l2) {
+  const float mm = fmaxf(m, sink_l2);
+  const float a = __builtin_amdgcn_exp2f(m - mm);
+  l = l * a + __builtin_amdgcn_exp2f(sink_l2 - mm);
+  m = mm;
+  return a;
+}
+
 // Raw buffer resource over `bytes` bytes at `base` (gfx9 untyped access);
 // reads at or past `bytes` return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {

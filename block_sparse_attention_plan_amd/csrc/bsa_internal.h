@@ -20,12 +20,21 @@ hipError_t launch_plan(const int32_t *layout, int32_t H, int32_t Mb, int32_t Nb,
                        int32_t *row_ptr, int32_t *row_order, int32_t *nnz_total,
                        int32_t *col_idx, hipStream_t stream);
 
+// Per-call options of the forward kernels (already validated).
+struct FwdOptions {
+  const float *sink;  // [H] per-head sink logits, or nullptr
+  float cap_k;        // 2*scale*log2(e)/cap for the tanh logit cap, 0 without one
+  float cap_b;        // cap/scale
+  int32_t causal;     // nonzero: key token j > query token i is masked too
+  int32_t kv_group;   // query heads per K/V head (1 without grouping)
+};
+
 // Returns hipErrorInvalidValue when no kernel instance matches (bs, d, f32).
 hipError_t launch_forward(const void *q, const void *k, const void *v,
                           const int32_t *row_ptr, const int32_t *col_idx,
                           const int32_t *row_order, int32_t B, int32_t H, int32_t Mb,
                           int32_t Nb, int32_t bs, int32_t d, bool f32, float scale,
-                          void *out, float *lse, hipStream_t stream);
+                          const FwdOptions &opt, void *out, float *lse, hipStream_t stream);
 bool forward_supported(int32_t bs, int32_t d);
 
 hipError_t launch_topk(const void *q, const void *kv, const int32_t *idx,

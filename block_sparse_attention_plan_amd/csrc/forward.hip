@@ -27,6 +27,13 @@
 //                       when bs >= 64
 //   bsa_fwd_dma_kernel  bf16, bs >= 64: as above with tiles copied from HBM
 //                       straight into double-buffered, XOR-swizzled LDS
+//
+// Optional terms, from the arguments of the ejkernel BlockSparseAttention
+// operation: grouped K/V heads (query head h reads K/V head h / kv_group), a
+// per-head sink logit folded into the denominator after the loop, and -- in
+// the MASK instances only, so that the plain instances keep their code -- a
+// tanh cap on the scaled scores and an element-level causal mask on tiles
+// that reach past the diagonal.
 #include <type_traits>
 
 #include "bsa_device.h"
@@ -81,12 +88,12 @@ template <> struct Io<float> {
   }
 };
 
-template <int BS, int D, typename T>
+template <int BS, int D, typename T, bool MASK>
 __global__ void __launch_bounds__(BS * 4)
 bsa_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
                const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
                const int32_t *__restrict__ row_order, int32_t B, int32_t H, int32_t Mb,
-               int32_t Nb, float scale_log2, T *__restrict__ out, float *__restrict__ lse) {
+               int32_t Nb, float scale_log2, T *__restrict__ out, float *__restrict__ lse, const FwdOptions opt) {
   constexpr int NW = BS / 16;            // waves per workgroup
   constexpr int NT = NW * 64;            // threads per workgroup
   constexpr int KSTR = D + 8;            // LDS row stride (elements) of the K tile
@@ -121,15 +128,16 @@ bsa_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__rest
   const int64_t bh = (int64_t)b * H + h;
   const int64_t Sq = (int64_t)Mb * BS, Sk = (int64_t)Nb * BS;
   const T *qh = q + bh * Sq * D;
-  const T *kh = k + bh * Sk * D;
-  const T *vh = v + bh * Sk * D;
+  const int64_t bkv = (int64_t)b * (H / opt.kv_group) + h / opt.kv_group;  // K/V head
+  const T *kh = k + bkv * Sk * D;
+  const T *vh = v + bkv * Sk * D;
   T *oh = out + bh * Sq * D;
   float *lh = lse ? lse + bh * Sq : nullptr;
   const int64_t i_row = (int64_t)m * BS + 16 * wid + li;  // this lane's query row
 
-  if (beg == end) {  // no live tile: zero output, lse = -inf
+  if (beg == end) {  // no live tile: zero output, lse = -inf (the sink logit with a sink)
     for (int dt = 0; dt < DT; ++dt) Io<T>::store_zero4(oh + i_row * D + 16 * dt + 4 * G);
-    if (lh && G == 0) lh[i_row] = -__builtin_inff();
+    if (lh && G == 0) lh[i_row] = opt.sink ? opt.sink[h] : -__builtin_inff();
     return;
   }
 
@@ -185,6 +193,23 @@ bsa_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__rest
         s[jt] = mfma16(a, qf[c], s[jt]);
       }
     }
+    // Options (MASK instances only): tanh logit cap, then the causal mask on
+    // tiles that reach past the diagonal (key row 16jt + 4G + e, query row
+    // 16 wid + li).
+    if (MASK && opt.cap_k != 0.f) {
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[jt][e] = capped_score(s[jt][e], opt.cap_k, opt.cap_b);
+    }
+    if (MASK && opt.causal && col_idx[t] >= m) {
+      const int dq = (m - col_idx[t]) * BS + 16 * wid + li;  // query minus key offset
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (16 * jt + 4 * G + e > dq) s[jt][e] = -__builtin_inff();
+    }
     // Online softmax over this tile's keys for query column li.
     float mx = s[0][0];
 #pragma unroll
@@ -236,8 +261,10 @@ bsa_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__rest
     }
   }
 
-  const float l_tot = sum_xor32(sum_xor16(l_run));
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  float l_tot = sum_xor32(sum_xor16(l_run));
+  float o_scale = 1.f;
+  if (opt.sink) o_scale = fold_sink(m_run, l_tot, opt.sink[h] * kLog2e);
+  const float inv = l_tot > 0.f ? o_scale / l_tot : 0.f;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) Io<T>::store4(oh + i_row * D + 16 * dt + 4 * G, acc[dt] * inv);
   if (lh && G == 0) lh[i_row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
@@ -255,12 +282,12 @@ bsa_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__rest
 //   S^T[j][i]: lane column i = lane%32; key rows 8*(r/4) + 4*(lane/32) + r%4
 //   P^T operand for 16 keys: registers r = 8c .. 8c+7 of one 32-key block
 //   O^T[d][i]: the same result layout over d
-template <int BS, int D, typename T, int KSPLIT>
+template <int BS, int D, typename T, int KSPLIT, bool MASK>
 __global__ void __launch_bounds__(BS * 2 * KSPLIT) __attribute__((amdgpu_waves_per_eu(2)))
 bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
                  const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
                  const int32_t *__restrict__ row_order, int32_t B, int32_t H, int32_t Mb,
-                 int32_t Nb, float scale_log2, T *__restrict__ out, float *__restrict__ lse) {
+                 int32_t Nb, float scale_log2, T *__restrict__ out, float *__restrict__ lse, const FwdOptions opt) {
   constexpr int NRG = BS / 32;           // 32-row groups
   constexpr int NW = NRG * KSPLIT;       // waves per workgroup
   constexpr int NT = NW * 64;            // threads per workgroup
@@ -308,8 +335,9 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
   const int64_t bh = (int64_t)b * H + h;
   const int64_t Sq = (int64_t)Mb * BS, Sk = (int64_t)Nb * BS;
   const T *qh = q + bh * Sq * D;
-  const T *kh = k + bh * Sk * D;
-  const T *vh = v + bh * Sk * D;
+  const int64_t bkv = (int64_t)b * (H / opt.kv_group) + h / opt.kv_group;  // K/V head
+  const T *kh = k + bkv * Sk * D;
+  const T *vh = v + bkv * Sk * D;
   T *oh = out + bh * Sq * D;
   float *lh = lse ? lse + bh * Sq : nullptr;
   const int64_t i_row = (int64_t)m * BS + 32 * rg + l32;
@@ -318,7 +346,7 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
     if (ks == 0) {
       for (int dt = 0; dt < DT; ++dt)
         for (int a = 0; a < 4; ++a) Io<T>::store_zero4(oh + i_row * D + 32 * dt + 8 * a + 4 * h2);
-      if (lh && h2 == 0) lh[i_row] = -__builtin_inff();
+      if (lh && h2 == 0) lh[i_row] = opt.sink ? opt.sink[h] : -__builtin_inff();
     }
     return;
   }
@@ -378,6 +406,27 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
         const bf16x8 a = *reinterpret_cast<const bf16x8 *>(ksrc + 32 * jt * KSTR + 16 * c);
         s[jt] = mfma32(a, qf[c], s[jt]);
       }
+    }
+  };
+
+  // Options on a fresh score tile of column ncol (MASK instances only): tanh
+  // logit cap, then the causal mask when the tile reaches past the diagonal
+  // (key row key0 + 32jt + 8(e/4) + 4h2 + e%4, query row 32rg + l32).
+  auto apply_opts = [&](f32x16 (&s)[JT], int ncol) {
+    if constexpr (!MASK) return;
+    if (opt.cap_k != 0.f) {
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[jt][e] = capped_score(s[jt][e], opt.cap_k, opt.cap_b);
+    }
+    if (opt.causal && ncol >= m) {
+      const int dq = (m - ncol) * BS + 32 * rg + l32 - key0 - 4 * h2;
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (32 * jt + 8 * (e / 4) + (e % 4) > dq) s[jt][e] = -__builtin_inff();
     }
   };
 
@@ -453,6 +502,7 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
   }
   __syncthreads();
   qk(0, s_cur);
+  apply_opts(s_cur, cols[0]);
   if (n > 2) load_k(cols[2]);
   if (n > 1) load_v(cols[1]);
   // Steady state without branches: staging of tiles past the end re-loads
@@ -465,6 +515,7 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
     load_k(cols[min(t + 3, n - 1)]);
     load_v(cols[min(t + 2, n - 1)]);
     qk((t + 1) & 1, s_next);
+    apply_opts(s_next, cols[t + 1]);
     softmax_pv(s_cur, t & 1);
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt) s_cur[jt] = s_next[jt];
@@ -498,7 +549,9 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
     l_tot = l_tot * a1 + l2 * a2;
     m_run = mm;
   }
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  float o_scale = 1.f;
+  if (opt.sink) o_scale = fold_sink(m_run, l_tot, opt.sink[h] * kLog2e);
+  const float inv = l_tot > 0.f ? o_scale / l_tot : 0.f;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -527,13 +580,13 @@ template <int D> struct VSwz {
   }
 };
 
-template <int BS, int D, int KSPLIT>
+template <int BS, int D, int KSPLIT, bool MASK>
 __global__ void __launch_bounds__(BS * 2 * KSPLIT) __attribute__((amdgpu_waves_per_eu(KSPLIT)))
 bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
                    const __bf16 *__restrict__ v, const int32_t *__restrict__ row_ptr,
                    const int32_t *__restrict__ col_idx, const int32_t *__restrict__ row_order,
                    int32_t B, int32_t H, int32_t Mb, int32_t Nb, float scale_log2,
-                   __bf16 *__restrict__ out, float *__restrict__ lse) {
+                   __bf16 *__restrict__ out, float *__restrict__ lse, const FwdOptions opt) {
   constexpr int NRG = BS / 32;           // 32-row groups
   constexpr int NW = NRG * KSPLIT;       // waves per workgroup
   constexpr int KW = BS / KSPLIT;        // keys per wave per tile
@@ -582,8 +635,9 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   const int64_t bh = (int64_t)b * H + h;
   const int64_t Sq = (int64_t)Mb * BS, Sk = (int64_t)Nb * BS;
   const __bf16 *qh = q + bh * Sq * D;
-  const __bf16 *kh = k + bh * Sk * D;
-  const __bf16 *vh = v + bh * Sk * D;
+  const int64_t bkv = (int64_t)b * (H / opt.kv_group) + h / opt.kv_group;  // K/V head
+  const __bf16 *kh = k + bkv * Sk * D;
+  const __bf16 *vh = v + bkv * Sk * D;
   __bf16 *oh = out + bh * Sq * D;
   float *lh = lse ? lse + bh * Sq : nullptr;
   const int64_t i_row = (int64_t)m * BS + 32 * rg + l32;
@@ -592,7 +646,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     if (ks == 0) {
       for (int dt = 0; dt < DT; ++dt)
         for (int a = 0; a < 4; ++a) Io<__bf16>::store_zero4(oh + i_row * D + 32 * dt + 8 * a + 4 * h2);
-      if (lh && h2 == 0) lh[i_row] = -__builtin_inff();
+      if (lh && h2 == 0) lh[i_row] = opt.sink ? opt.sink[h] : -__builtin_inff();
     }
     return;
   }
@@ -641,6 +695,27 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
       }
   };
 
+  // Options on a fresh score tile of column ncol (MASK instances only): tanh
+  // logit cap, then the causal mask when the tile reaches past the diagonal
+  // (key row key0 + 32jt + 8(e/4) + 4h2 + e%4, query row 32rg + l32).
+  auto apply_opts = [&](f32x16 (&s)[JT], int ncol) {
+    if constexpr (!MASK) return;
+    if (opt.cap_k != 0.f) {
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[jt][e] = capped_score(s[jt][e], opt.cap_k, opt.cap_b);
+    }
+    if (opt.causal && ncol >= m) {
+      const int dq = (m - ncol) * BS + 32 * rg + l32 - key0 - 4 * h2;
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (32 * jt + 8 * (e / 4) + (e % 4) > dq) s[jt][e] = -__builtin_inff();
+    }
+  };
+
   float m_run = kMaxFloor;  // running max (log2 units)
   float l_run = 0.f;
   f32x16 o[DT];
@@ -681,9 +756,9 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(s[jt][8 * c2 + e], scale_log2, -m_run));
         pf[2 * jt + c2] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-        // the denominator sums the same bf16 weights that multiply V
+        // the denominator sums the fp32 weights, so lse carries no bf16 rounding
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ps[e] = sum2_bf16(pf[2 * jt + c2], e, ps[e]);
+        for (int e = 0; e < 8; ++e) ps[e % 4] += p[e];
       }
     l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
   };
@@ -745,6 +820,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   qk(K0, s_a);
+  apply_opts(s_a, col_at(0));
   mx_a = tile_max(s_a);
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();  // M_{-1}: K0 free
@@ -774,6 +850,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     load_k(kcol, Kq);
     pv(pf, Vc);
     if constexpr (MORE) {
+      apply_opts(s_nxt, vcol);
       mx_nxt = tile_max(s_nxt);
       sched_interleave<JT * 2 * DT, 4 * JT * DT, kReadAheadV, 1>();
     } else {
@@ -831,7 +908,9 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     l_tot = l_tot * a1 + l2 * a2;
     m_run = mm;
   }
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  float o_scale = 1.f;
+  if (opt.sink) o_scale = fold_sink(m_run, l_tot, opt.sink[h] * kLog2e);
+  const float inv = l_tot > 0.f ? o_scale / l_tot : 0.f;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -841,29 +920,30 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   if (lh && h2 == 0) lh[i_row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
 }
 
-template <int BS, int D, typename T>
+template <int BS, int D, typename T, bool MASK>
 hipError_t launch_one(const void *q, const void *k, const void *v, const int32_t *row_ptr,
                       const int32_t *col_idx, const int32_t *row_order, int32_t B, int32_t H,
-                      int32_t Mb, int32_t Nb, float scale, void *out, float *lse,
-                      hipStream_t stream) {
+                      int32_t Mb, int32_t Nb, float scale, const FwdOptions &opt, void *out,
+                      float *lse, hipStream_t stream) {
   const int64_t W = (int64_t)B * H * Mb;
   const int64_t per = (W + 7) / 8;
   const int64_t grid = per * 8;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if constexpr (BS == 16) {
-    hipLaunchKernelGGL((bsa_fwd_kernel<BS, D, T>), dim3((unsigned)grid), dim3(BS * 4), 0, stream,
-                       (const T *)q, (const T *)k, (const T *)v, row_ptr, col_idx, row_order, B, H,
-                       Mb, Nb, scale * kLog2e, (T *)out, lse);
+    hipLaunchKernelGGL((bsa_fwd_kernel<BS, D, T, MASK>), dim3((unsigned)grid), dim3(BS * 4), 0,
+                       stream, (const T *)q, (const T *)k, (const T *)v, row_ptr, col_idx,
+                       row_order, B, H, Mb, Nb, scale * kLog2e, (T *)out, lse, opt);
   } else if constexpr (BS >= 64 && std::is_same<T, __bf16>::value) {
     constexpr int KS = BS == 128 ? kDmaKeySplit : 2;
-    hipLaunchKernelGGL((bsa_fwd_dma_kernel<BS, D, KS>), dim3((unsigned)grid), dim3(BS * 2 * KS), 0, stream,
-                       (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, row_ptr, col_idx,
-                       row_order, B, H, Mb, Nb, scale * kLog2e, (__bf16 *)out, lse);
+    hipLaunchKernelGGL((bsa_fwd_dma_kernel<BS, D, KS, MASK>), dim3((unsigned)grid),
+                       dim3(BS * 2 * KS), 0, stream, (const __bf16 *)q, (const __bf16 *)k,
+                       (const __bf16 *)v, row_ptr, col_idx, row_order, B, H, Mb, Nb,
+                       scale * kLog2e, (__bf16 *)out, lse, opt);
   } else {
     constexpr int KSPLIT = BS >= 64 ? 2 : 1;
-    hipLaunchKernelGGL((bsa_fwd32_kernel<BS, D, T, KSPLIT>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((bsa_fwd32_kernel<BS, D, T, KSPLIT, MASK>), dim3((unsigned)grid),
                        dim3(BS * 2 * KSPLIT), 0, stream, (const T *)q, (const T *)k, (const T *)v,
-                       row_ptr, col_idx, row_order, B, H, Mb, Nb, scale * kLog2e, (T *)out, lse);
+                       row_ptr, col_idx, row_order, B, H, Mb, Nb, scale * kLog2e, (T *)out, lse, opt);
   }
   return hipGetLastError();
 }
@@ -871,10 +951,17 @@ hipError_t launch_one(const void *q, const void *k, const void *v, const int32_t
 template <typename T>
 hipError_t dispatch(int32_t bs, int32_t d, const void *q, const void *k, const void *v,
                     const int32_t *rp, const int32_t *ci, const int32_t *ro, int32_t B, int32_t H,
-                    int32_t Mb, int32_t Nb, float scale, void *out, float *lse, hipStream_t s) {
+                    int32_t Mb, int32_t Nb, float scale, const FwdOptions &opt, void *out,
+                    float *lse, hipStream_t s) {
+  // Score-changing options (cap, causal) select their own kernel instances,
+  // so the plain forward keeps the code it has without them.
+  const bool mask = opt.cap_k != 0.f || opt.causal != 0;
 #define BSA_CASE(BS_, D_)                                                                   \
   if (bs == BS_ && d == D_)                                                                 \
-    return launch_one<BS_, D_, T>(q, k, v, rp, ci, ro, B, H, Mb, Nb, scale, out, lse, s);
+    return mask ? launch_one<BS_, D_, T, true>(q, k, v, rp, ci, ro, B, H, Mb, Nb, scale, opt, \
+                                               out, lse, s)                                 \
+                : launch_one<BS_, D_, T, false>(q, k, v, rp, ci, ro, B, H, Mb, Nb, scale, opt, \
+                                                out, lse, s);
   BSA_CASE(16, 32) BSA_CASE(16, 64) BSA_CASE(16, 128)
   BSA_CASE(32, 32) BSA_CASE(32, 64) BSA_CASE(32, 128)
   BSA_CASE(64, 32) BSA_CASE(64, 64) BSA_CASE(64, 128)
@@ -892,12 +979,13 @@ bool forward_supported(int32_t bs, int32_t d) {
 hipError_t launch_forward(const void *q, const void *k, const void *v, const int32_t *row_ptr,
                           const int32_t *col_idx, const int32_t *row_order, int32_t B, int32_t H,
                           int32_t Mb, int32_t Nb, int32_t bs, int32_t d, bool f32, float scale,
-                          void *out, float *lse, hipStream_t stream) {
+                          const FwdOptions &opt, void *out, float *lse, hipStream_t stream) {
+  if (opt.kv_group < 1 || H % opt.kv_group != 0) return hipErrorInvalidValue;
   if (f32)
-    return dispatch<float>(bs, d, q, k, v, row_ptr, col_idx, row_order, B, H, Mb, Nb, scale, out,
-                           lse, stream);
-  return dispatch<__bf16>(bs, d, q, k, v, row_ptr, col_idx, row_order, B, H, Mb, Nb, scale, out,
-                          lse, stream);
+    return dispatch<float>(bs, d, q, k, v, row_ptr, col_idx, row_order, B, H, Mb, Nb, scale, opt,
+                           out, lse, stream);
+  return dispatch<__bf16>(bs, d, q, k, v, row_ptr, col_idx, row_order, B, H, Mb, Nb, scale, opt,
+                          out, lse, stream);
 }
 
 }  // namespace bsa

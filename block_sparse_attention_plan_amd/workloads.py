@@ -42,13 +42,14 @@ __all__ = [
 class BsaInputs:
     name: str
     q: torch.Tensor          # CPU [B, H, S, d], bf16 or fp32
-    k: torch.Tensor
+    k: torch.Tensor          # CPU [B, Hkv, Sk, d]
     v: torch.Tensor
     layout: np.ndarray       # int32 [H, Mb, Nb]
     bs: int
     scale: float
     seed: int
     params: Dict = field(default_factory=dict)
+    sink: Optional[torch.Tensor] = None  # CPU fp32 [H] or None
 
 
 @dataclass
@@ -105,16 +106,22 @@ def causal_bernoulli_layout(H: int, nb: int, p: float, rng: np.random.Generator)
 
 
 def make_bsa(name: str, B: int, H: int, S: int, bs: int, d: int, dtype: str, layout: str,
-             seed: int, std: float = 1.0, Sk: Optional[int] = None, **kw) -> BsaInputs:
+             seed: int, std: float = 1.0, Sk: Optional[int] = None, Hkv: Optional[int] = None,
+             sink_mean: Optional[float] = None, **kw) -> BsaInputs:
     """Draw q, k, v and a layout.  ``layout`` names a family above, or
-    ``"given"`` with ``kw['layout_array']``."""
+    ``"given"`` with ``kw['layout_array']``.  ``Hkv`` (default H) is the
+    number of K/V heads; with ``sink_mean`` a per-head sink logit
+    N(sink_mean, 1) is drawn last, so the other draws do not depend on it."""
     Sk = S if Sk is None else Sk
+    Hkv = H if Hkv is None else Hkv
     if S % bs or Sk % bs:
         raise ValueError("sequence lengths must be multiples of the block size")
+    if Hkv < 1 or H % Hkv:
+        raise ValueError("Hkv must divide H")
     rng = np.random.default_rng(seed)
     q = _tensor(_normal(rng, (B, H, S, d), std), dtype)
-    k = _tensor(_normal(rng, (B, H, Sk, d), std), dtype)
-    v = _tensor(_normal(rng, (B, H, Sk, d), std), dtype)
+    k = _tensor(_normal(rng, (B, Hkv, Sk, d), std), dtype)
+    v = _tensor(_normal(rng, (B, Hkv, Sk, d), std), dtype)
     mb, nb = S // bs, Sk // bs
     if layout == "band":
         if mb != nb:
@@ -133,10 +140,20 @@ def make_bsa(name: str, B: int, H: int, S: int, bs: int, d: int, dtype: str, lay
         raise ValueError(layout)
     if lay.shape != (H, mb, nb):
         raise ValueError("layout shape mismatch")
-    params = dict(B=B, H=H, S=S, Sk=Sk, bs=bs, d=d, dtype=dtype, layout=layout, std=std, **{
-        k2: v2 for k2, v2 in kw.items() if k2 != "layout_array"})
+    sink = None
+    if sink_mean is not None:
+        sink = torch.from_numpy((rng.standard_normal(H) + sink_mean).astype(np.float32))
+    params = dict(B=B, H=H, Hkv=Hkv, S=S, Sk=Sk, bs=bs, d=d, dtype=dtype, layout=layout,
+                  std=std, sink_mean=sink_mean,
+                  **{k2: v2 for k2, v2 in kw.items() if k2 != "layout_array"})
     return BsaInputs(name=name, q=q, k=k, v=v, layout=lay, bs=bs, scale=1.0 / np.sqrt(d),
-                     seed=seed, params=params)
+                     seed=seed, params=params, sink=sink)
+
+
+def sink_logits(H: int, mean: float, seed: int) -> torch.Tensor:
+    """Per-head sink logits N(mean, 1), fp32 [H] on the CPU."""
+    rng = np.random.default_rng(seed)
+    return torch.from_numpy((rng.standard_normal(H) + mean).astype(np.float32))
 
 
 def make_topk(name: str, B: int, M: int, H: int, d: int, N: int, topk: int, seed: int,

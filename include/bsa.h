@@ -128,6 +128,41 @@ int bsa_forward(const void *q, const void *k, const void *v, const bsa_plan_t *p
                 int32_t B, int32_t H, int32_t Sq, int32_t Sk, int32_t bs, int32_t d,
                 bsa_dtype_t dtype, float scale, void *out, float *lse, void *stream);
 
+/* Options of bsa_forward_ex.  A zeroed struct (or a NULL pointer) gives the
+ * plain bsa_forward. */
+typedef struct {
+  const float *attn_sink; /* device fp32 [H], 4-byte aligned, or NULL */
+  float soft_cap;         /* > 0: tanh logit cap; 0: none */
+  int32_t causal;         /* nonzero: also mask key token j > query token i */
+  int32_t kv_heads;       /* K/V heads Hkv (H % Hkv == 0); 0 means H */
+} bsa_forward_opts_t;
+
+/*
+ * Block-sparse attention forward with the optional terms of the ejkernel
+ * BlockSparseAttention operation ("ejkernel: BlockSparseAttention" page,
+ * arguments softmax_aux, logits_soft_cap, causal and the key/value head
+ * count).  With opts zeroed it computes exactly what bsa_forward computes.
+ * Otherwise, in the notation of bsa_forward:
+ *   soft_cap > 0:  s_ij <- soft_cap * tanh(s_ij / soft_cap), applied to the
+ *                  scaled score before any masking (Gemma-2 style capping);
+ *   causal:        s_ij = -inf also where j > i (token positions counted from
+ *                  0 in both q and k), on top of the layout's mask;
+ *   attn_sink:     the softmax denominator of head h also holds
+ *                  exp(attn_sink[h]) (the sink logit is neither scaled nor
+ *                  capped), so lse includes it and a row with no live key gets
+ *                  out = 0 and lse = attn_sink[h];
+ *   kv_heads:      k and v are [B, Hkv, Sk, d]; query head h reads K/V head
+ *                  h / (H / Hkv) (grouped-query attention).
+ * Arguments, layouts and ownership as for bsa_forward; opts is a host pointer
+ * read during the call.  Errors as for bsa_forward, plus BSA_ERR_INVALID_ARG
+ * for kv_heads < 0 or not dividing H, or a soft_cap that is negative or not
+ * finite, and BSA_ERR_MISALIGNED for an attn_sink not 4-byte aligned.
+ */
+int bsa_forward_ex(const void *q, const void *k, const void *v, const bsa_plan_t *plan,
+                   int32_t B, int32_t H, int32_t Sq, int32_t Sk, int32_t bs, int32_t d,
+                   bsa_dtype_t dtype, float scale, const bsa_forward_opts_t *opts, void *out,
+                   float *lse, void *stream);
+
 /*
  * Top-k gathered sparse attention forward with a per-head attention sink.
  *

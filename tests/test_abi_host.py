@@ -112,6 +112,34 @@ def test_bsa_forward_validation(lib):
     assert call(plan=ctypes.byref(nobuf)) == INVALID
 
 
+def test_bsa_forward_ex_validation(lib):
+    """Option checks of bsa_forward_ex; every call here fails before a launch."""
+    f = ctypes.c_void_p(0x10000)
+    p = _plan_struct(lib=lib)
+    P = ctypes.byref(p)
+
+    def call(sink=None, soft_cap=0.0, causal=0, kv_heads=0, opts=True, **kw):
+        a = dict(B=1, H=2, Sq=64, Sk=64, bs=16, d=32, dtype=0, scale=0.5)
+        a.update(kw)
+        o = bsa._FwdOptsT(sink, soft_cap, causal, kv_heads)
+        return lib.bsa_forward_ex(f, f, f, P, a["B"], a["H"], a["Sq"], a["Sk"], a["bs"],
+                                  a["d"], a["dtype"], a["scale"],
+                                  ctypes.byref(o) if opts else None, f, None, None)
+
+    assert call(kv_heads=3) == INVALID          # does not divide H = 2
+    assert call(kv_heads=-1) == INVALID
+    assert call(kv_heads=4) == INVALID
+    assert call(soft_cap=-1.0) == INVALID
+    assert call(soft_cap=float("inf")) == INVALID
+    assert call(soft_cap=float("nan")) == INVALID
+    assert call(soft_cap=1e-44) == INVALID      # 2*scale*log2(e)/cap overflows fp32
+    assert call(sink=0x10002) == MISALIGNED
+    # the plain checks still run first with options present
+    assert call(kv_heads=1, H=3) == MISMATCH
+    assert call(opts=False, d=48) == UNSUPPORTED
+    assert call(causal=1, bs=8, Sq=32, Sk=32) == UNSUPPORTED
+
+
 def test_topk_validation(lib):
     f = ctypes.c_void_p(0x10000)
 
