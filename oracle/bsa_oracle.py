@@ -1,4 +1,4 @@
-"""Reference oracle for block-sparse attention forward and the top-k gathered variant.
+"""Reference oracle for block-sparse attention (forward and backward) and the top-k gathered variant.
 
 TEST INFRASTRUCTURE ONLY.  This module is a plain, slow, obviously correct CPU
 implementation in float64 NumPy of what the GPU library computes.  It exists to
@@ -69,6 +69,10 @@ __all__ = [
     "token_mask",
     "attention_dense_masked",
     "attention_live_tiles",
+    "PlanColsRef",
+    "plan_columns",
+    "attention_backward_dense",
+    "attention_backward_live_tiles",
     "topk_attention",
 ]
 
@@ -261,6 +265,213 @@ def attention_live_tiles(q, k, v, layout, bs: int, scale: float,
             out[b, h, rows] = np.where(live[:, None], o, 0.0)
             lse[b, h, rows] = np.where(live, shift + np.log(np.where(live, den, 1.0)), -np.inf)
     return out, lse
+
+
+# --------------------------------------------------------------------------
+# Backward: gradients of the block-sparse forward
+# --------------------------------------------------------------------------
+#
+# The next.gr tutorial ("Gradient Propagation in Block Sparse Attention", and
+# the block-structured Jacobian under "Mathematical Formulation") fixes only
+# that gradients flow through the live blocks of the pattern: the gradient of
+# query block i sums over the blocks attending to it, and the Jacobian of an
+# output row with respect to an input row is zero outside the row's
+# neighbourhood.  The pages print no formula for the softmax step, so the
+# oracle is the chain rule of the forward definition above written out.  With
+# c_ij the (capped) scaled score, Z_i = sum_j exp(c_ij) + exp(sink_h),
+# P_ij = exp(c_ij) / Z_i and out_i = sum_j P_ij v_j, an upstream gradient dO
+# gives
+#   dv_j    = sum_i P_ij dO_i
+#   dP_ij   = dO_i . v_j,      D_i = sum_j P_ij dP_ij = dO_i . out_i
+#   dc_ij   = P_ij (dP_ij - D_i)
+#   ds_ij   = dc_ij (1 - tanh^2(s_ij / cap))      (dc_ij without a cap)
+#   dq_i    = scale sum_j ds_ij k_j,   dk_j = scale sum_i ds_ij q_i
+#   dsink_h = -sum_i exp(sink_h) / Z_i * D_i       (over every batch item and row)
+# with masked entries contributing nothing (P_ij = 0 there) and, under grouped
+# heads, dk and dv of a K/V head summed over the query heads that read it.
+
+
+@dataclass
+class PlanColsRef:
+    """Per-column CSR (the transposed plan) of a block layout, for the
+    backward's key-block work items.
+
+    Column c = h * Nb + n.  ``col_ptr[c]:col_ptr[c+1]`` delimits the query
+    blocks m with (h, m, n) live, ascending, in ``row_idx``.  ``col_order``
+    lists the key-block work items w = kvh * Nb + n (one per K/V head and key
+    block), K/V head by K/V head, and inside each K/V head by the number of
+    live tiles the item visits -- summed over the query heads of its group --
+    descending, ties by n ascending.
+    """
+
+    H: int
+    Hkv: int
+    Mb: int
+    Nb: int
+    col_ptr: np.ndarray    # int32 [H*Nb+1]
+    row_idx: np.ndarray    # int32 [nnz_total]
+    col_order: np.ndarray  # int32 [Hkv*Nb]
+    nnz_total: int
+
+
+def plan_columns(layout: np.ndarray, kv_heads: Optional[int] = None) -> PlanColsRef:
+    """Transposed CSR of a block layout [H, Mb, Nb] and the order of the
+    backward's key-block work items (see PlanColsRef)."""
+    lay = np.asarray(layout)
+    if lay.ndim != 3:
+        raise ValueError("layout must be [H, Mb, Nb]")
+    H, Mb, Nb = lay.shape
+    Hkv = H if kv_heads is None else kv_heads
+    if Hkv <= 0 or H % Hkv:
+        raise ValueError("kv_heads must divide H")
+    g = H // Hkv
+    live_t = np.swapaxes(lay != 0, 1, 2)                     # [H, Nb, Mb]
+    cnt = live_t.reshape(H * Nb, Mb).sum(axis=1).astype(np.int64)
+    col_ptr = np.zeros(H * Nb + 1, dtype=np.int64)
+    col_ptr[1:] = np.cumsum(cnt)
+    _, rows = np.nonzero(live_t.reshape(H * Nb, Mb))         # m ascending per column
+    order = []
+    for kvh in range(Hkv):
+        work = cnt.reshape(H, Nb)[kvh * g:(kvh + 1) * g].sum(axis=0)
+        n = np.arange(Nb)
+        order.append(kvh * Nb + np.lexsort((n, -work)))
+    col_order = np.concatenate(order) if order else np.zeros(0, np.int64)
+    return PlanColsRef(H=H, Hkv=Hkv, Mb=Mb, Nb=Nb, col_ptr=col_ptr.astype(np.int32),
+                       row_idx=rows.astype(np.int32), col_order=col_order.astype(np.int32),
+                       nnz_total=int(col_ptr[-1]))
+
+
+def _cap_slope(s: np.ndarray, soft_cap: Optional[float]) -> np.ndarray:
+    """d cap(s) / d s = 1 - tanh^2(s / cap) (1 without a cap)."""
+    if not soft_cap:
+        return np.ones_like(s)
+    t = np.tanh(s / soft_cap)
+    return 1.0 - t * t
+
+
+def attention_backward_dense(q, k, v, dout, layout, bs: int, scale: float, *, sink=None,
+                             soft_cap: Optional[float] = None, causal: bool = False):
+    """Gradients of attention_dense_masked's ``out`` for the upstream gradient
+    ``dout`` [B, H, Sq, d]: returns dq [B, H, Sq, d], dk and dv [B, Hkv, Sk, d],
+    and dsink [H] (None without a sink).  Dense S x S form of the formulas
+    above; the options mean what they mean in the forward."""
+    q, k, v, dout = _as64(q), _as64(k), _as64(v), _as64(dout)
+    B, H, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    kvh = _kv_head(H, Hkv)
+    heads = [kvh(h) for h in range(H)]
+    kx, vx = k[:, heads], v[:, heads]                        # per query head
+    mask = token_mask(layout, bs)
+    if mask.shape != (H, Sq, Sk):
+        raise ValueError("layout does not match q/k shapes")
+    if causal:
+        mask = mask & (np.arange(Sk)[None, None, :] <= np.arange(Sq)[None, :, None])
+    s = scale * np.matmul(q, np.swapaxes(kx, -1, -2))        # scaled, uncapped
+    out, lse = attention_dense_masked(q, k, v, layout, bs, scale, sink=sink,
+                                      soft_cap=soft_cap, causal=causal)
+    live_row = np.isfinite(lse)[..., None]
+    c = np.where(mask[None], _cap(s, soft_cap), -np.inf)
+    with np.errstate(invalid="ignore"):
+        p = np.where(live_row & mask[None], np.exp(c - np.where(live_row, lse[..., None], 0.0)), 0.0)
+    dv_x = np.matmul(np.swapaxes(p, -1, -2), dout)           # [B, H, Sk, d]
+    dp = np.matmul(dout, np.swapaxes(vx, -1, -2))            # [B, H, Sq, Sk]
+    D = (dout * out).sum(axis=-1, keepdims=True)             # [B, H, Sq, 1]
+    ds = p * (dp - D) * _cap_slope(s, soft_cap)
+    dq = scale * np.matmul(ds, kx)
+    dk_x = scale * np.matmul(np.swapaxes(ds, -1, -2), q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for h in range(H):
+        dk[:, heads[h]] += dk_x[:, h]
+        dv[:, heads[h]] += dv_x[:, h]
+    dsink = None
+    if sink is not None:
+        sk = _as64(sink)
+        with np.errstate(invalid="ignore"):
+            w = np.where(np.isfinite(lse), np.exp(sk[None, :, None] - np.where(np.isfinite(lse), lse, 0.0)), 0.0)
+        dsink = -(w * D[..., 0]).sum(axis=(0, 2))
+    return dq, dk, dv, dsink
+
+
+def attention_backward_live_tiles(q, k, v, dout, layout, bs: int, scale: float, *,
+                                  row_blocks=None, col_blocks=None, sink=None,
+                                  soft_cap: Optional[float] = None, causal: bool = False):
+    """The same gradients over live tiles only, for sampled blocks.
+
+    ``row_blocks`` lists (b, h, m) query blocks whose dq rows are computed;
+    ``col_blocks`` lists (b, kvh, n) key blocks whose dk and dv rows are
+    computed (summing the query heads of the K/V head's group).  Entries not
+    computed are NaN.  dsink is returned only when both lists are None (then
+    every block is computed).  Each needed query row's out and lse come from
+    attention_live_tiles.
+    """
+    q, k, v, dout = _as64(q), _as64(k), _as64(v), _as64(dout)
+    B, H, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    kvh = _kv_head(H, Hkv)
+    g = H // Hkv
+    lay = np.asarray(layout) != 0
+    Mb, Nb = Sq // bs, Sk // bs
+    if lay.shape != (H, Mb, Nb):
+        raise ValueError("layout does not match q/k shapes")
+    full = row_blocks is None and col_blocks is None
+    if row_blocks is None:
+        row_blocks = [(b, h, m) for b in range(B) for h in range(H) for m in range(Mb)]
+    if col_blocks is None:
+        col_blocks = [(b, j, n) for b in range(B) for j in range(Hkv) for n in range(Nb)]
+    need = set(row_blocks)
+    for (b, j, n) in col_blocks:
+        for h in range(j * g, (j + 1) * g):
+            need.update((b, h, int(m)) for m in np.flatnonzero(lay[h, :, n]))
+    need = sorted(need)
+    out, lse = attention_live_tiles(q, k, v, layout, bs, scale, row_blocks=need, sink=sink,
+                                    soft_cap=soft_cap, causal=causal)
+    D = (dout * out).sum(axis=-1)                            # NaN where not computed
+    offs = np.arange(bs)
+
+    def tile_terms(b, h, m, n):
+        """P, dS of tile (m, n) of head h: [bs queries, bs keys]."""
+        rows = slice(m * bs, (m + 1) * bs)
+        keys = slice(n * bs, (n + 1) * bs)
+        s = scale * (q[b, h, rows] @ k[b, kvh(h), keys].T)
+        c = _cap(s, soft_cap)
+        if causal:
+            c = np.where((n * bs + offs)[None, :] <= (m * bs + offs)[:, None], c, -np.inf)
+        lr = lse[b, h, rows][:, None]
+        live = np.isfinite(lr)
+        with np.errstate(invalid="ignore"):
+            p = np.where(live, np.exp(c - np.where(live, lr, 0.0)), 0.0)
+        dp = dout[b, h, rows] @ v[b, kvh(h), keys].T
+        ds = p * (dp - D[b, h, rows][:, None]) * _cap_slope(s, soft_cap)
+        return p, ds
+
+    dq = np.full(q.shape, np.nan)
+    for (b, h, m) in row_blocks:
+        acc = np.zeros((bs, d))
+        for n in np.flatnonzero(lay[h, m]):
+            _, ds = tile_terms(b, h, m, int(n))
+            acc += scale * ds @ k[b, kvh(h), n * bs:(n + 1) * bs]
+        dq[b, h, m * bs:(m + 1) * bs] = acc
+    dk = np.full(k.shape, np.nan)
+    dv = np.full(v.shape, np.nan)
+    for (b, j, n) in col_blocks:
+        ak = np.zeros((bs, d))
+        av = np.zeros((bs, v.shape[3]))
+        for h in range(j * g, (j + 1) * g):
+            for m in np.flatnonzero(lay[h, :, n]):
+                p, ds = tile_terms(b, h, int(m), n)
+                rows = slice(int(m) * bs, (int(m) + 1) * bs)
+                av += p.T @ dout[b, h, rows]
+                ak += scale * ds.T @ q[b, h, rows]
+        dk[b, j, n * bs:(n + 1) * bs] = ak
+        dv[b, j, n * bs:(n + 1) * bs] = av
+    dsink = None
+    if full and sink is not None:
+        sk = _as64(sink)
+        with np.errstate(invalid="ignore"):
+            w = np.where(np.isfinite(lse), np.exp(sk[None, :, None] - np.where(np.isfinite(lse), lse, 0.0)), 0.0)
+        dsink = -(w * D).sum(axis=(0, 2))
+    return dq, dk, dv, dsink
 
 
 # --------------------------------------------------------------------------
