@@ -9,6 +9,9 @@ missing, every call raises.
     bsa_plan(layout)                      -> Plan   (per-row CSR of live tiles)
     bsa_forward(q, k, v, plan, scale, *, attn_sink, soft_cap, causal)
                                           -> (out, lse)
+    bsa_plan_cols(layout, kv_heads)       -> PlanCols (per-column CSR, backward)
+    bsa_backward(q, k, v, out, dout, lse, plan, plan_cols, scale, *, options)
+                                          -> (dq, dk, dv, dsink)
     topk_sparse_attn(q, kv, idx, attn_sink, scale) -> out
 """
 
@@ -28,6 +31,9 @@ __all__ = [
     "plan_buffer",
     "bsa_plan_nnz",
     "bsa_forward",
+    "PlanCols",
+    "bsa_plan_cols",
+    "bsa_backward",
     "topk_sparse_attn",
     "library_path",
     "load_library",
@@ -91,6 +97,20 @@ def load_library():
     lib.bsa_forward_ex.argtypes = [vp, vp, vp, ctypes.POINTER(_PlanT), i32, i32, i32, i32, i32,
                                    i32, i32, f32, ctypes.POINTER(_FwdOptsT), vp, vp, vp]
     lib.bsa_forward_ex.restype = ctypes.c_int
+    lib.bsa_plan_cols_buffer_bytes.argtypes = [i32, i32, i32, i32]
+    lib.bsa_plan_cols_buffer_bytes.restype = ctypes.c_size_t
+    lib.bsa_plan_cols_sections.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.bsa_plan_cols_sections.restype = ctypes.c_int
+    lib.bsa_plan_cols.argtypes = [vp, i32, i32, i32, i32, vp, ctypes.c_size_t,
+                                  ctypes.POINTER(_PlanColsT), vp]
+    lib.bsa_plan_cols.restype = ctypes.c_int
+    lib.bsa_backward_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.bsa_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.bsa_backward.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(_PlanT),
+                                 ctypes.POINTER(_PlanColsT), i32, i32, i32, i32, i32, i32, i32,
+                                 f32, ctypes.POINTER(_FwdOptsT), vp, ctypes.c_size_t, vp, vp, vp,
+                                 vp, vp]
+    lib.bsa_backward.restype = ctypes.c_int
     lib.topk_sparse_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp]
     lib.topk_sparse_attn.restype = ctypes.c_int
     lib.bsa_status_string.argtypes = [ctypes.c_int]
@@ -127,6 +147,17 @@ class _FwdOptsT(ctypes.Structure):
         ("soft_cap", ctypes.c_float),
         ("causal", ctypes.c_int32),
         ("kv_heads", ctypes.c_int32),
+    ]
+
+
+class _PlanColsT(ctypes.Structure):
+    _fields_ = [
+        ("H", ctypes.c_int32),
+        ("Hkv", ctypes.c_int32),
+        ("Mb", ctypes.c_int32),
+        ("Nb", ctypes.c_int32),
+        ("dev_buf", ctypes.c_void_p),
+        ("dev_bytes", ctypes.c_size_t),
     ]
 
 
@@ -270,6 +301,127 @@ def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
         ctypes.c_void_p(v.data_ptr()), ctypes.byref(plan._raw), B, H, Sq, Sk, bs, d, dtype,
         float(scale), ctypes.byref(opts), ctypes.c_void_p(out.data_ptr()), lse_ptr, _stream(q)))
     return out, lse
+
+
+class PlanCols:
+    """A built column plan (backward): owns its device buffer."""
+
+    def __init__(self, buf: torch.Tensor, raw: _PlanColsT, H: int, Hkv: int, Mb: int, Nb: int):
+        self.buf = buf
+        self._raw = raw
+        self.H, self.Hkv, self.Mb, self.Nb = H, Hkv, Mb, Nb
+        offs = (ctypes.c_size_t * 4)()
+        _check(load_library().bsa_plan_cols_sections(H, Hkv, Mb, Nb, offs))
+        self._offs = [int(o) for o in offs]
+
+    def _section(self, i: int, count: int) -> torch.Tensor:
+        off = self._offs[i]
+        return self.buf[off:off + 4 * count].view(torch.int32)
+
+    @property
+    def col_ptr(self) -> torch.Tensor:
+        return self._section(0, self.H * self.Nb + 1)
+
+    @property
+    def col_order(self) -> torch.Tensor:
+        return self._section(1, self.Hkv * self.Nb)
+
+    @property
+    def nnz_total_dev(self) -> torch.Tensor:
+        return self._section(2, 1)
+
+    def row_idx(self, nnz_total: int) -> torch.Tensor:
+        return self._section(3, nnz_total)
+
+
+def bsa_plan_cols(layout: torch.Tensor, kv_heads: Optional[int] = None,
+                  buf: Optional[torch.Tensor] = None) -> PlanCols:
+    """Build the column plan (for the backward) of an int32 layout [H, Mb, Nb]
+    whose query heads share kv_heads K/V heads (default: H)."""
+    _require_gpu("layout", layout)
+    if layout.dtype != torch.int32 or layout.dim() != 3:
+        raise ValueError("layout must be an int32 tensor [H, Mb, Nb]")
+    lib = load_library()
+    H, Mb, Nb = (int(x) for x in layout.shape)
+    Hkv = H if kv_heads is None else int(kv_heads)
+    nbytes = lib.bsa_plan_cols_buffer_bytes(H, Hkv, Mb, Nb)
+    if nbytes == 0:
+        raise ValueError(f"invalid layout shape {tuple(layout.shape)} for kv_heads={Hkv}")
+    if buf is None:
+        raw_buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=layout.device)
+        shift = (-raw_buf.data_ptr()) % 256
+        buf = raw_buf[shift:shift + nbytes]
+    elif buf.dtype != torch.uint8 or buf.numel() < nbytes or buf.device != layout.device:
+        raise ValueError("buf must be a 256-byte aligned uint8 buffer of enough bytes")
+    raw = _PlanColsT()
+    _check(lib.bsa_plan_cols(ctypes.c_void_p(layout.data_ptr()), H, Hkv, Mb, Nb,
+                             ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.byref(raw),
+                             _stream(layout)))
+    return PlanCols(buf, raw, H, Hkv, Mb, Nb)
+
+
+def bsa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                 dout: torch.Tensor, lse: torch.Tensor, plan: Plan, plan_cols: PlanCols,
+                 scale: Optional[float] = None, *, attn_sink: Optional[torch.Tensor] = None,
+                 soft_cap: Optional[float] = None, causal: bool = False,
+                 dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                 dv: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None):
+    """Gradients of bsa_forward for the upstream gradient dout.
+
+    q, k, v, scale and the options must be those of the forward call that
+    produced out and lse.  Returns (dq, dk, dv, dsink): dq like q, dk and dv
+    like k, dsink fp32 [H] (None without a sink).  bf16 only.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("lse", lse)):
+        _require_gpu(name, t)
+    if any(t.dtype != torch.bfloat16 for t in (q, k, v, out, dout)):
+        raise ValueError("q, k, v, out, dout must be bf16")
+    B, H, Sq, d = (int(x) for x in q.shape)
+    Hkv, Sk = int(k.shape[1]), int(k.shape[2])
+    if tuple(k.shape) != tuple(v.shape) or k.shape[0] != B or k.shape[3] != d or H % Hkv:
+        raise ValueError("k and v must be [B, Hkv, Sk, d] matching q, with Hkv dividing H")
+    if tuple(out.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("out and dout must match q")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Sq):
+        raise ValueError("lse must be fp32 [B, H, Sq]")
+    if Sq % plan.Mb != 0:
+        raise ValueError("Sq must be a multiple of the layout's block rows")
+    bs = Sq // plan.Mb
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if attn_sink is not None:
+        _require_gpu("attn_sink", attn_sink)
+        if attn_sink.dtype != torch.float32 or tuple(attn_sink.shape) != (H,):
+            raise ValueError("attn_sink must be fp32 [H]")
+    if soft_cap is not None and not (math.isfinite(soft_cap) and soft_cap > 0):
+        raise ValueError("soft_cap must be finite and > 0")
+    lib = load_library()
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _require_gpu(name, t)
+        if t.shape != like.shape or t.dtype != like.dtype:
+            raise ValueError(f"{name} must match {'q' if like is q else 'k'}")
+    wbytes = lib.bsa_backward_workspace_bytes(B, H, Sq)
+    if workspace is None:
+        workspace = torch.empty(wbytes // 4, dtype=torch.float32, device=q.device)
+    elif workspace.numel() * workspace.element_size() < wbytes:
+        raise ValueError("workspace too small")
+    dsink = torch.empty(H, dtype=torch.float32, device=q.device) if attn_sink is not None else None
+    opts = _FwdOptsT(ctypes.c_void_p(attn_sink.data_ptr() if attn_sink is not None else 0),
+                     float(soft_cap or 0.0), 1 if causal else 0, Hkv)
+    _check(lib.bsa_backward(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+        ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+        ctypes.c_void_p(dout.data_ptr()), ctypes.c_void_p(lse.data_ptr()),
+        ctypes.byref(plan._raw), ctypes.byref(plan_cols._raw), B, H, Sq, Sk, bs, d, BSA_BF16,
+        float(scale), ctypes.byref(opts), ctypes.c_void_p(workspace.data_ptr()),
+        workspace.numel() * workspace.element_size(), ctypes.c_void_p(dq.data_ptr()),
+        ctypes.c_void_p(dk.data_ptr()), ctypes.c_void_p(dv.data_ptr()),
+        ctypes.c_void_p(dsink.data_ptr() if dsink is not None else 0), _stream(q)))
+    return dq, dk, dv, dsink
 
 
 def topk_sparse_attn(q: torch.Tensor, kv: torch.Tensor, idx: torch.Tensor,

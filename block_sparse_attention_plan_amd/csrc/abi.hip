@@ -41,6 +41,47 @@ P *at(void *base, size_t off) {
   return reinterpret_cast<P *>(static_cast<char *>(base) + off);
 }
 
+int check_plan_cols(const bsa_plan_cols_t *pc, bsa::PlanColsGeometry *g) {
+  if (pc == nullptr) return fail(BSA_ERR_INVALID_ARG, "column plan is NULL");
+  if (pc->dev_buf == nullptr) return fail(BSA_ERR_INVALID_ARG, "column plan has no buffer");
+  if (!bsa::plan_cols_geometry(pc->H, pc->Hkv, pc->Mb, pc->Nb, g))
+    return fail(BSA_ERR_INVALID_ARG, "column plan has invalid dimensions");
+  if (pc->dev_bytes < g->total)
+    return fail(BSA_ERR_BUFFER_TOO_SMALL, "column plan buffer is %zu bytes, needs %zu",
+                pc->dev_bytes, g->total);
+  return BSA_OK;
+}
+
+// Options of the forward (and of the backward, which must repeat them),
+// validated and turned into kernel form.  `who` prefixes error messages.
+int make_options(const bsa_forward_opts_t *opts, int32_t H, float scale, bsa::FwdOptions *fo,
+                 const char *who) {
+  *fo = bsa::FwdOptions{nullptr, 0.f, 0.f, 0, 1};
+  if (opts == nullptr) return BSA_OK;
+  const int32_t hkv = opts->kv_heads == 0 ? H : opts->kv_heads;
+  if (hkv < 1 || H % hkv != 0)
+    return fail(BSA_ERR_INVALID_ARG, "%s: kv_heads=%d must divide H=%d", who,
+                (int)opts->kv_heads, (int)H);
+  if (!(std::isfinite(opts->soft_cap) && opts->soft_cap >= 0.f))
+    return fail(BSA_ERR_INVALID_ARG, "%s: soft_cap must be finite and >= 0", who);
+  if (opts->attn_sink != nullptr && !aligned(opts->attn_sink, 4))
+    return fail(BSA_ERR_MISALIGNED, "%s: attn_sink must be 4-byte aligned", who);
+  fo->sink = opts->attn_sink;
+  if (opts->soft_cap > 0.f) {
+    // tanh(x) = 1 - 2 / (exp(2x) + 1) with x = scale * s / cap, evaluated
+    // as exp2(s * cap_k); the kernel multiplies the result by cap_b and
+    // later by scale, so that the capped score is cap * tanh(x).
+    fo->cap_k = (float)(2.0 * (double)scale * 1.4426950408889634 / (double)opts->soft_cap);
+    fo->cap_b = (float)((double)opts->soft_cap / (double)scale);
+    if (!(std::isfinite(fo->cap_k) && std::isfinite(fo->cap_b) && fo->cap_b > 0.f))
+      return fail(BSA_ERR_INVALID_ARG, "%s: soft_cap %g out of range for scale %g", who,
+                  (double)opts->soft_cap, (double)scale);
+  }
+  fo->causal = opts->causal != 0;
+  fo->kv_group = H / hkv;
+  return BSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -131,30 +172,9 @@ int bsa_forward_ex(const void *q, const void *k, const void *v, const bsa_plan_t
     return fail(BSA_ERR_MISALIGNED, "bsa_forward: tensors must be 16-byte aligned");
   const int64_t work = (int64_t)B * plan->H * plan->Mb;
   if (work > 0x7ffffff0LL) return fail(BSA_ERR_UNSUPPORTED, "bsa_forward: problem too large");
-  bsa::FwdOptions fo{nullptr, 0.f, 0.f, 0, 1};
-  if (opts != nullptr) {
-    const int32_t hkv = opts->kv_heads == 0 ? H : opts->kv_heads;
-    if (hkv < 1 || H % hkv != 0)
-      return fail(BSA_ERR_INVALID_ARG, "bsa_forward: kv_heads=%d must divide H=%d",
-                  (int)opts->kv_heads, (int)H);
-    if (!(std::isfinite(opts->soft_cap) && opts->soft_cap >= 0.f))
-      return fail(BSA_ERR_INVALID_ARG, "bsa_forward: soft_cap must be finite and >= 0");
-    if (opts->attn_sink != nullptr && !aligned(opts->attn_sink, 4))
-      return fail(BSA_ERR_MISALIGNED, "bsa_forward: attn_sink must be 4-byte aligned");
-    fo.sink = opts->attn_sink;
-    if (opts->soft_cap > 0.f) {
-      // tanh(x) = 1 - 2 / (exp(2x) + 1) with x = scale * s / cap, evaluated
-      // as exp2(s * cap_k); the kernel multiplies the result by cap_b and
-      // later by scale, so that the capped score is cap * tanh(x).
-      fo.cap_k = (float)(2.0 * (double)scale * 1.4426950408889634 / (double)opts->soft_cap);
-      fo.cap_b = (float)((double)opts->soft_cap / (double)scale);
-      if (!(std::isfinite(fo.cap_k) && std::isfinite(fo.cap_b) && fo.cap_b > 0.f))
-        return fail(BSA_ERR_INVALID_ARG, "bsa_forward: soft_cap %g out of range for scale %g",
-                    (double)opts->soft_cap, (double)scale);
-    }
-    fo.causal = opts->causal != 0;
-    fo.kv_group = H / hkv;
-  }
+  bsa::FwdOptions fo;
+  st = make_options(opts, H, scale, &fo, "bsa_forward");
+  if (st != BSA_OK) return st;
   hipError_t e = bsa::launch_forward(
       q, k, v, at<int32_t>(plan->dev_buf, g.off_row_ptr), at<int32_t>(plan->dev_buf, g.off_col_idx),
       at<int32_t>(plan->dev_buf, g.off_row_order), B, plan->H, plan->Mb, plan->Nb, bs, d,
@@ -168,6 +188,130 @@ int bsa_forward(const void *q, const void *k, const void *v, const bsa_plan_t *p
                 float scale, void *out, float *lse, void *stream) {
   return bsa_forward_ex(q, k, v, plan, B, H, Sq, Sk, bs, d, dtype, scale, nullptr, out, lse,
                         stream);
+}
+
+size_t bsa_plan_cols_buffer_bytes(int32_t H, int32_t Hkv, int32_t Mb, int32_t Nb) {
+  bsa::PlanColsGeometry g;
+  if (!bsa::plan_cols_geometry(H, Hkv, Mb, Nb, &g)) return 0;
+  return g.total;
+}
+
+int bsa_plan_cols_sections(int32_t H, int32_t Hkv, int32_t Mb, int32_t Nb, size_t offsets_out[4]) {
+  bsa::PlanColsGeometry g;
+  if (offsets_out == nullptr) return fail(BSA_ERR_INVALID_ARG, "offsets_out is NULL");
+  if (!bsa::plan_cols_geometry(H, Hkv, Mb, Nb, &g))
+    return fail(BSA_ERR_INVALID_ARG, "invalid dimensions H=%d Hkv=%d Mb=%d Nb=%d", H, Hkv, Mb,
+                Nb);
+  offsets_out[0] = g.off_col_ptr;
+  offsets_out[1] = g.off_col_order;
+  offsets_out[2] = g.off_nnz;
+  offsets_out[3] = g.off_row_idx;
+  return BSA_OK;
+}
+
+int bsa_plan_cols(const int32_t *layout, int32_t H, int32_t Hkv, int32_t Mb, int32_t Nb,
+                  void *dev_buf, size_t dev_bytes, bsa_plan_cols_t *plan_out, void *stream) {
+  if (layout == nullptr || dev_buf == nullptr || plan_out == nullptr)
+    return fail(BSA_ERR_INVALID_ARG, "bsa_plan_cols: NULL pointer argument");
+  if (Hkv == 0) Hkv = H;
+  bsa::PlanColsGeometry g;
+  if (!bsa::plan_cols_geometry(H, Hkv, Mb, Nb, &g))
+    return fail(BSA_ERR_INVALID_ARG, "bsa_plan_cols: invalid dimensions H=%d Hkv=%d Mb=%d Nb=%d",
+                H, Hkv, Mb, Nb);
+  if ((int64_t)(H / Hkv) * Mb > bsa::kPlanMaxNb)
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_plan_cols: (H/Hkv)*Mb=%lld exceeds %d",
+                (long long)(H / Hkv) * Mb, bsa::kPlanMaxNb);
+  if (!aligned(dev_buf, 256))
+    return fail(BSA_ERR_MISALIGNED, "bsa_plan_cols: buffer not 256-byte aligned");
+  if (dev_bytes < g.total)
+    return fail(BSA_ERR_BUFFER_TOO_SMALL, "bsa_plan_cols: buffer is %zu bytes, needs %zu",
+                dev_bytes, g.total);
+  hipError_t e = bsa::launch_plan_cols(layout, H, Hkv, Mb, Nb, at<int32_t>(dev_buf, g.off_col_ptr),
+                                       at<int32_t>(dev_buf, g.off_col_order),
+                                       at<int32_t>(dev_buf, g.off_nnz),
+                                       at<int32_t>(dev_buf, g.off_row_idx), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "bsa_plan_cols launch");
+  plan_out->H = H;
+  plan_out->Hkv = Hkv;
+  plan_out->Mb = Mb;
+  plan_out->Nb = Nb;
+  plan_out->dev_buf = dev_buf;
+  plan_out->dev_bytes = dev_bytes;
+  return BSA_OK;
+}
+
+size_t bsa_backward_workspace_bytes(int32_t B, int32_t H, int32_t Sq) {
+  if (B <= 0 || H <= 0 || Sq <= 0) return 0;
+  return (size_t)2 * B * H * Sq * sizeof(float);
+}
+
+int bsa_backward(const void *q, const void *k, const void *v, const void *out, const void *dout,
+                 const float *lse, const bsa_plan_t *plan, const bsa_plan_cols_t *plan_cols,
+                 int32_t B, int32_t H, int32_t Sq, int32_t Sk, int32_t bs, int32_t d,
+                 bsa_dtype_t dtype, float scale, const bsa_forward_opts_t *opts, void *workspace,
+                 size_t workspace_bytes, void *dq, void *dk, void *dv, float *dsink,
+                 void *stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr ||
+      lse == nullptr || dq == nullptr || dk == nullptr || dv == nullptr || workspace == nullptr)
+    return fail(BSA_ERR_INVALID_ARG, "bsa_backward: NULL tensor pointer");
+  bsa::PlanGeometry g;
+  int st = check_plan(plan, &g);
+  if (st != BSA_OK) return st;
+  bsa::PlanColsGeometry gc;
+  st = check_plan_cols(plan_cols, &gc);
+  if (st != BSA_OK) return st;
+  if (B <= 0 || H <= 0 || Sq <= 0 || Sk <= 0 || bs <= 0 || d <= 0)
+    return fail(BSA_ERR_INVALID_ARG, "bsa_backward: sizes must be positive");
+  if (H != plan->H || (int64_t)Sq != (int64_t)plan->Mb * bs || (int64_t)Sk != (int64_t)plan->Nb * bs)
+    return fail(BSA_ERR_PLAN_MISMATCH,
+                "bsa_backward: H=%d Sq=%d Sk=%d bs=%d do not match plan H=%d Mb=%d Nb=%d", H, Sq,
+                Sk, bs, plan->H, plan->Mb, plan->Nb);
+  if (dtype != BSA_BF16)
+    return fail(dtype == BSA_F32 ? BSA_ERR_UNSUPPORTED : BSA_ERR_INVALID_ARG,
+                "bsa_backward: dtype %d (only bf16 has a backward kernel)", (int)dtype);
+  if (!(std::isfinite(scale) && scale > 0.f))
+    return fail(BSA_ERR_INVALID_ARG, "bsa_backward: scale must be finite and > 0");
+  bsa::FwdOptions fo;
+  st = make_options(opts, H, scale, &fo, "bsa_backward");
+  if (st != BSA_OK) return st;
+  if (plan_cols->H != H || plan_cols->Mb != plan->Mb || plan_cols->Nb != plan->Nb ||
+      plan_cols->Hkv != H / fo.kv_group)
+    return fail(BSA_ERR_PLAN_MISMATCH,
+                "bsa_backward: column plan H=%d Hkv=%d Mb=%d Nb=%d does not match H=%d Hkv=%d "
+                "Mb=%d Nb=%d", plan_cols->H, plan_cols->Hkv, plan_cols->Mb, plan_cols->Nb, H,
+                H / fo.kv_group, plan->Mb, plan->Nb);
+  if (!bsa::backward_supported(bs, d))
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_backward: no kernel for bs=%d d=%d", bs, d);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || !aligned(workspace, 16) || (dsink != nullptr && !aligned(dsink, 4)))
+    return fail(BSA_ERR_MISALIGNED, "bsa_backward: tensors must be 16-byte aligned");
+  const size_t ws = bsa_backward_workspace_bytes(B, H, Sq);
+  if (workspace_bytes < ws)
+    return fail(BSA_ERR_BUFFER_TOO_SMALL, "bsa_backward: workspace is %zu bytes, needs %zu",
+                workspace_bytes, ws);
+  const int64_t work = (int64_t)B * H * plan->Mb;
+  const int64_t rows = (int64_t)B * H * Sq;
+  if (work > 0x7ffffff0LL || (int64_t)B * H * plan->Nb > 0x7ffffff0LL)
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_backward: problem too large");
+  bsa::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse;
+  a.row_ptr = at<int32_t>(plan->dev_buf, g.off_row_ptr);
+  a.col_idx = at<int32_t>(plan->dev_buf, g.off_col_idx);
+  a.row_order = at<int32_t>(plan->dev_buf, g.off_row_order);
+  a.col_ptr = at<int32_t>(plan_cols->dev_buf, gc.off_col_ptr);
+  a.row_idx = at<int32_t>(plan_cols->dev_buf, gc.off_row_idx);
+  a.col_order = at<int32_t>(plan_cols->dev_buf, gc.off_col_order);
+  a.B = B; a.H = H; a.Mb = plan->Mb; a.Nb = plan->Nb; a.bs = bs; a.d = d;
+  a.scale = scale;
+  a.opt = fo;
+  a.Dv = static_cast<float *>(workspace);
+  a.lse2 = static_cast<float *>(workspace) + rows;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.dsink = fo.sink != nullptr ? dsink : nullptr;
+  hipError_t e = bsa::launch_backward(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "bsa_backward launch");
+  return BSA_OK;
 }
 
 int topk_sparse_attn(const void *q, const void *kv, const int32_t *idx, const float *attn_sink,

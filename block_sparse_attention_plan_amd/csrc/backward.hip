@@ -1,0 +1,483 @@
+// Block-sparse attention backward (gfx950).
+//
+// Gradients of the forward in forward.hip for an upstream gradient dO.  The
+// next.gr "Block Sparse Attention Techniques" tutorial ("Gradient Propagation
+// in Block Sparse Attention") fixes that gradients flow through the live
+// blocks only: dQ of query block m sums over the live tiles of its block row,
+// dK and dV of key block n over the live tiles of its block column.  With the
+// forward's lse saved, every tile is recomputed independently:
+//   P   = exp(c(scale * Q K^T) - lse)      (c: optional tanh cap, masks -> 0)
+//   dP  = dO V^T,   D_i = dO_i . out_i
+//   dS  = P * (dP - D) * c'(.)
+//   dQ  = scale * dS K,   dK = scale * dS^T Q,   dV = P^T dO
+//   dsink_h = -sum_i exp(sink_h - lse_i) D_i
+//
+// Four kernels, none with atomics, so every gradient is bit-for-bit
+// repeatable:
+//   bwd_pre_kernel   D_i and lse_i * log2(e) per query row (workspace)
+//   bwd_dq_kernel    work item (b, h, query block m) over the row plan; the
+//                    wave owning 32 query rows keeps Q^T and dO^T in registers
+//                    and computes S^T = K Q^T, dP^T = V dO^T and
+//                    dQ^T += K^T dS^T (dS^T straight from the accumulators as
+//                    the B operand, K^T by LDS transpose reads)
+//   bwd_dkdv_kernel  work item (b, K/V head, key block n) over the column plan
+//                    (the query heads of a group one after another); the wave
+//                    owning 32 key rows keeps K^T and V^T in registers and
+//                    computes S = Q K^T, dP = dO V^T, dV^T += dO^T P and
+//                    dK^T += Q^T dS
+//   bwd_dsink_kernel one workgroup per head, fixed-order reduction
+// Tiles travel from HBM straight into LDS (buffer_load_dwordx4 ... lds); each
+// tile is read both row-wise (16-byte reads) and transposed
+// (ds_read_b64_tr_b16), so its 16-byte chunks are XOR-swizzled per row with a
+// pattern that keeps both read shapes free of bank conflicts.
+#include <type_traits>
+
+#include "bsa_device.h"
+#include "bsa_internal.h"
+
+namespace bsa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Chunk c of tile row r sits at chunk c ^ f(r).  Row reads touch 16
+// consecutive rows at one logical chunk (f is a bijection on r % 16 among the
+// rows that share LDS banks); transpose reads touch 4 aligned rows at 4
+// aligned chunks (f moves each of those rows to a different 64-byte bank
+// group).  f depends on r % 16 only.
+template <int D> struct BSwz {
+  static __device__ __forceinline__ int f(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    else return (r >> 2) & 3;
+  }
+};
+
+// Copy a contiguous BS x D bf16 tile into LDS with the swizzle; the NW waves
+// of the workgroup share its 1 KiB copy instructions.
+template <int BS, int D, int NW>
+__device__ __forceinline__ void copy_tile(const __bf16 *src, __bf16 *dst, int wid, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int NI = BS * D * 2 / 1024;
+  constexpr int RPI = 64 / CPR;
+  static_assert(NI % NW == 0, "copies must split evenly over the waves");
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, BS * D * 2);
+#pragma unroll
+  for (int j = 0; j < NI / NW; ++j) {
+    const int i = wid + NW * j;
+    const int row = RPI * i + lane / CPR;
+    const int logical = (lane % CPR) ^ BSwz<D>::f(row);
+    copy16_to_lds(rs, dst + i * 512, (uint32_t)((row * D + logical * 8) * 2), 0u);
+  }
+}
+
+// Row operand: 8 elements of tile row `row`, logical chunk `chunk`
+// (sw = f(row)).
+template <int D>
+__device__ __forceinline__ bf16x8 row_read(const __bf16 *tile, int row, int chunk, int sw) {
+  return *reinterpret_cast<const bf16x8 *>(tile + row * D + ((chunk ^ sw) << 3));
+}
+
+// Transposed operand X^T (rows of X are the contraction index) for the 32
+// columns of block dt and the 16 rows starting at r16 (a multiple of 16):
+// this lane reads rows r16 + tr_r and r16 + tr_r + 8, columns
+// 32 dt + 16 (G % 2) + 4 c_src .. +3 (the k-slot order of the 32x32x16
+// accumulator layout).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_read(const __bf16 *tile, int r16, int dt, int tr_r, int lc_off,
+                                          int pc, int sw0, int sw8) {
+  const int lc = 4 * dt + lc_off;
+  const __bf16 *p0 = tile + (r16 + tr_r) * D + ((lc ^ sw0) << 3) + pc;
+  const __bf16 *p8 = tile + (r16 + tr_r + 8) * D + ((lc ^ sw8) << 3) + pc;
+  return cat4(lds_read_tr4(p0), lds_read_tr4(p8));
+}
+
+__device__ __forceinline__ void store4_bf16(__bf16 *p, float a, float b, float c, float d) {
+  bf16x4 r;
+  r[0] = (__bf16)a; r[1] = (__bf16)b; r[2] = (__bf16)c; r[3] = (__bf16)d;
+  *reinterpret_cast<bf16x4 *>(p) = r;
+}
+
+// D_i = dO_i . out_i (fp32 over bf16 products) and lse_i * log2(e), with
+// +inf for a row without a live key (lse = -inf), so that its weights
+// exp2(s - lse2) vanish.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_pre_kernel(const __bf16 *__restrict__ out,
+                                                      const __bf16 *__restrict__ dout,
+                                                      const float *__restrict__ lse, int64_t rows,
+                                                      float *__restrict__ Dv,
+                                                      float *__restrict__ lse2) {
+  constexpr int LPR = D / 8;          // lanes per row
+  constexpr int RPB = 256 / LPR;      // rows per workgroup pass
+  const int tid = threadIdx.x;
+  const int sub = tid % LPR;
+  for (int64_t r0 = (int64_t)blockIdx.x * RPB; r0 < rows; r0 += (int64_t)gridDim.x * RPB) {
+    const int64_t r = r0 + tid / LPR;
+    float acc = 0.f;
+    if (r < rows) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(out + r * D + sub * 8);
+      const bf16x8 g = *reinterpret_cast<const bf16x8 *>(dout + r * D + sub * 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc = fmaf((float)a[i], (float)g[i], acc);
+    }
+#pragma unroll
+    for (int o = LPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (r < rows && sub == 0) {
+      Dv[r] = acc;
+      const float l = lse[r];
+      lse2[r] = l == -__builtin_inff() ? __builtin_inff() : l * kLog2e;
+    }
+  }
+}
+
+// dsink_h = -sum over batch items and rows of exp2(sink_h log2 e - lse2) D.
+__global__ void __launch_bounds__(256) bwd_dsink_kernel(const float *__restrict__ lse2,
+                                                        const float *__restrict__ Dv,
+                                                        const float *__restrict__ sink, int32_t B,
+                                                        int32_t H, int64_t Sq,
+                                                        float *__restrict__ dsink) {
+  __shared__ float part[256];
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float s2 = sink[h] * kLog2e;
+  float acc = 0.f;
+  for (int b = 0; b < B; ++b) {
+    const int64_t base = ((int64_t)b * H + h) * Sq;
+    for (int64_t i = tid; i < Sq; i += 256) acc += fast_exp2(s2 - lse2[base + i]) * Dv[base + i];
+  }
+  part[tid] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) part[tid] += part[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) dsink[h] = -part[0];
+}
+
+// Options on one score of a recomputed tile (MASK instances): the tanh cap
+// and its slope, then the weight exp2(c * scale_log2 - lse2).
+struct Weight {
+  float p, slope;
+};
+template <bool MASK>
+__device__ __forceinline__ Weight weight(float s, float scale_log2, float l2, const FwdOptions &opt) {
+  float slope = 1.f;
+  if (MASK && opt.cap_k != 0.f) {
+    s = capped_score(s, opt.cap_k, opt.cap_b);
+    const float t = s / opt.cap_b;   // tanh of the scaled score over the cap
+    slope = fmaf(-t, t, 1.f);
+  }
+  return Weight{fast_exp2(fmaf(s, scale_log2, -l2)), slope};
+}
+
+template <int BS, int D, bool MASK>
+__global__ void __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2)))
+bwd_dq_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
+              const __bf16 *__restrict__ v, const __bf16 *__restrict__ dout,
+              const float *__restrict__ lse2, const float *__restrict__ Dv,
+              const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
+              const int32_t *__restrict__ row_order, int32_t B, int32_t H, int32_t Mb, int32_t Nb,
+              float scale_log2, float scale, const FwdOptions opt, __bf16 *__restrict__ dq) {
+  constexpr int NW = BS / 32;
+  constexpr int TILE = BS * D;
+  constexpr int QC = D / 16;
+  constexpr int JT = BS / 32;
+  constexpr int DT = D / 32;
+
+  __shared__ __attribute__((aligned(1024))) __bf16 Ks[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 Vs[TILE];
+
+  const int64_t W = (int64_t)B * H * Mb;
+  const int64_t per = (W + 7) / 8;
+  const int64_t w = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (w >= W) return;
+  const int64_t HM = (int64_t)H * Mb;
+  const int b = (int)(w / HM);
+  const int r = row_order[w % HM];
+  const int h = r / Mb;
+  const int m = r % Mb;
+  const int beg = row_ptr[r];
+  const int end = row_ptr[r + 1];
+
+  const int tid = threadIdx.x;
+  const int wid = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64;
+  const int h2 = lane / 32, l32 = lane % 32;
+  const int G = lane / 16, l16 = lane % 16;
+
+  const int64_t bh = (int64_t)b * H + h;
+  const int64_t Sq = (int64_t)Mb * BS, Sk = (int64_t)Nb * BS;
+  const int64_t bkv = (int64_t)b * (H / opt.kv_group) + h / opt.kv_group;
+  const __bf16 *kh = k + bkv * Sk * D;
+  const __bf16 *vh = v + bkv * Sk * D;
+  const int qrow = 32 * wid + l32;            // query row inside the block
+  const int64_t i_row = (int64_t)m * BS + qrow;
+
+  const float l2 = lse2[bh * Sq + i_row];
+  const float dd = Dv[bh * Sq + i_row];
+  bf16x8 qf[QC], gf[QC];
+#pragma unroll
+  for (int c = 0; c < QC; ++c) {
+    qf[c] = *reinterpret_cast<const bf16x8 *>(q + (bh * Sq + i_row) * D + 16 * c + 8 * h2);
+    gf[c] = *reinterpret_cast<const bf16x8 *>(dout + (bh * Sq + i_row) * D + 16 * c + 8 * h2);
+  }
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+
+  const int sw_row = BSwz<D>::f(l32);
+  const int tr_r = 4 * h2 + l16 / 4;
+  const int c_src = l16 % 4;
+  const int lc_off = 2 * (G % 2) + c_src / 2, pc = 4 * (c_src % 2);
+  const int sw0 = BSwz<D>::f(tr_r), sw8 = BSwz<D>::f(tr_r + 8);
+
+  for (int t = beg; t < end; ++t) {
+    const int ncol = col_idx[t];
+    if (MASK && opt.causal && ncol > m) continue;   // every key after every query
+    __syncthreads();                                // previous tile fully read
+    copy_tile<BS, D, NW>(kh + (int64_t)ncol * TILE, Ks, wid, lane);
+    copy_tile<BS, D, NW>(vh + (int64_t)ncol * TILE, Vs, wid, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const bool diag = MASK && opt.causal && ncol == m;
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int c = 0; c < QC; ++c) {
+        s = mfma32(row_read<D>(Ks, 32 * jt + l32, 2 * c + h2, sw_row), qf[c], s);
+        dp = mfma32(row_read<D>(Vs, 32 * jt + l32, 2 * c + h2, sw_row), gf[c], dp);
+      }
+      // S^T[key][query]: key 32jt + 8(e/4) + 4h2 + e%4, query qrow
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const Weight wt = weight<MASK>(s[e], scale_log2, l2, opt);
+        float p = wt.p;
+        if (diag && 32 * jt + 8 * (e / 4) + 4 * h2 + (e % 4) > qrow) p = 0.f;
+        s[e] = p * (dp[e] - dd) * wt.slope;
+      }
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const bf16x8 dsf = to_bf16x8(s[8 * c2 + 0], s[8 * c2 + 1], s[8 * c2 + 2], s[8 * c2 + 3],
+                                     s[8 * c2 + 4], s[8 * c2 + 5], s[8 * c2 + 6], s[8 * c2 + 7]);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          acc[dt] = mfma32(tr_read<D>(Ks, 32 * jt + 16 * c2, dt, tr_r, lc_off, pc, sw0, sw8), dsf,
+                           acc[dt]);
+      }
+    }
+  }
+  __bf16 *dqh = dq + (bh * Sq + i_row) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      store4_bf16(dqh + 32 * dt + 8 * a + 4 * h2, scale * acc[dt][4 * a], scale * acc[dt][4 * a + 1],
+                  scale * acc[dt][4 * a + 2], scale * acc[dt][4 * a + 3]);
+}
+
+template <int BS, int D, bool MASK>
+__global__ void __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2)))
+bwd_dkdv_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
+                const __bf16 *__restrict__ v, const __bf16 *__restrict__ dout,
+                const float *__restrict__ lse2, const float *__restrict__ Dv,
+                const int32_t *__restrict__ col_ptr, const int32_t *__restrict__ row_idx,
+                const int32_t *__restrict__ col_order, int32_t B, int32_t H, int32_t Hkv,
+                int32_t Mb, int32_t Nb, float scale_log2, float scale, const FwdOptions opt,
+                __bf16 *__restrict__ dk, __bf16 *__restrict__ dv) {
+  constexpr int NW = BS / 32;
+  constexpr int TILE = BS * D;
+  constexpr int QC = D / 16;
+  constexpr int JT = BS / 32;
+  constexpr int DT = D / 32;
+
+  __shared__ __attribute__((aligned(1024))) __bf16 Qs[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 Gs[TILE];   // dO tile
+  __shared__ __attribute__((aligned(16))) float Ls[BS];         // lse2 of the tile's rows
+  __shared__ __attribute__((aligned(16))) float Ds[BS];         // D of the tile's rows
+
+  const int64_t W = (int64_t)B * Hkv * Nb;
+  const int64_t per = (W + 7) / 8;
+  const int64_t w = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (w >= W) return;
+  const int64_t KN = (int64_t)Hkv * Nb;
+  const int b = (int)(w / KN);
+  const int item = col_order[w % KN];
+  const int kvh = item / Nb;
+  const int n = item % Nb;
+  const int g = H / Hkv;
+
+  const int tid = threadIdx.x;
+  const int wid = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64;
+  const int h2 = lane / 32, l32 = lane % 32;
+  const int G = lane / 16, l16 = lane % 16;
+
+  const int64_t Sq = (int64_t)Mb * BS, Sk = (int64_t)Nb * BS;
+  const int64_t bkv = (int64_t)b * Hkv + kvh;
+  const int krow = 32 * wid + l32;            // key row inside the block
+  const int64_t j_row = (int64_t)n * BS + krow;
+
+  bf16x8 kf[QC], vf[QC];
+#pragma unroll
+  for (int c = 0; c < QC; ++c) {
+    kf[c] = *reinterpret_cast<const bf16x8 *>(k + (bkv * Sk + j_row) * D + 16 * c + 8 * h2);
+    vf[c] = *reinterpret_cast<const bf16x8 *>(v + (bkv * Sk + j_row) * D + 16 * c + 8 * h2);
+  }
+  f32x16 ak[DT], av[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    ak[dt] = f32x16{};
+    av[dt] = f32x16{};
+  }
+
+  const int sw_row = BSwz<D>::f(l32);
+  const int tr_r = 4 * h2 + l16 / 4;
+  const int c_src = l16 % 4;
+  const int lc_off = 2 * (G % 2) + c_src / 2, pc = 4 * (c_src % 2);
+  const int sw0 = BSwz<D>::f(tr_r), sw8 = BSwz<D>::f(tr_r + 8);
+
+  for (int hh = 0; hh < g; ++hh) {
+    const int h = kvh * g + hh;
+    const int64_t bh = (int64_t)b * H + h;
+    const int beg = col_ptr[h * Nb + n];
+    const int end = col_ptr[h * Nb + n + 1];
+    for (int t = beg; t < end; ++t) {
+      const int m = row_idx[t];
+      if (MASK && opt.causal && m < n) continue;    // every key after every query
+      __syncthreads();                              // previous tile fully read
+      copy_tile<BS, D, NW>(q + (bh * Sq + (int64_t)m * BS) * D, Qs, wid, lane);
+      copy_tile<BS, D, NW>(dout + (bh * Sq + (int64_t)m * BS) * D, Gs, wid, lane);
+      if (tid < BS) {
+        Ls[tid] = lse2[bh * Sq + (int64_t)m * BS + tid];
+        Ds[tid] = Dv[bh * Sq + (int64_t)m * BS + tid];
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      const bool diag = MASK && opt.causal && m == n;
+      // One 32-query chunk at a time: K^T, V^T and both accumulators stay
+      // live across the loop, so the chunks are not unrolled into each other.
+#pragma unroll 1
+      for (int jq = 0; jq < JT; ++jq) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int c = 0; c < QC; ++c) {
+          s = mfma32(row_read<D>(Qs, 32 * jq + l32, 2 * c + h2, sw_row), kf[c], s);
+          dp = mfma32(row_read<D>(Gs, 32 * jq + l32, 2 * c + h2, sw_row), vf[c], dp);
+        }
+        // S[query][key]: query 32jq + 8(e/4) + 4h2 + e%4, key krow.  P
+        // replaces S and dS replaces dP in place.
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&Ls[32 * jq + 8 * a + 4 * h2]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&Ds[32 * jq + 8 * a + 4 * h2]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = 4 * a + i;
+            const Weight wt = weight<MASK>(s[e], scale_log2, l4[i], opt);
+            float p = wt.p;
+            if (diag && krow > 32 * jq + 8 * a + 4 * h2 + i) p = 0.f;
+            s[e] = p;
+            dp[e] = p * (dp[e] - d4[i]) * wt.slope;
+          }
+        }
+        const f32x16 &ds = dp;
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const bf16x8 pf = to_bf16x8(s[8 * c2 + 0], s[8 * c2 + 1], s[8 * c2 + 2], s[8 * c2 + 3],
+                                      s[8 * c2 + 4], s[8 * c2 + 5], s[8 * c2 + 6], s[8 * c2 + 7]);
+          const bf16x8 dsf = to_bf16x8(ds[8 * c2 + 0], ds[8 * c2 + 1], ds[8 * c2 + 2],
+                                       ds[8 * c2 + 3], ds[8 * c2 + 4], ds[8 * c2 + 5],
+                                       ds[8 * c2 + 6], ds[8 * c2 + 7]);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            av[dt] = mfma32(tr_read<D>(Gs, 32 * jq + 16 * c2, dt, tr_r, lc_off, pc, sw0, sw8), pf,
+                            av[dt]);
+            ak[dt] = mfma32(tr_read<D>(Qs, 32 * jq + 16 * c2, dt, tr_r, lc_off, pc, sw0, sw8), dsf,
+                            ak[dt]);
+          }
+        }
+      }
+    }
+  }
+  __bf16 *dkr = dk + (bkv * Sk + j_row) * D;
+  __bf16 *dvr = dv + (bkv * Sk + j_row) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      store4_bf16(dkr + 32 * dt + 8 * a + 4 * h2, scale * ak[dt][4 * a], scale * ak[dt][4 * a + 1],
+                  scale * ak[dt][4 * a + 2], scale * ak[dt][4 * a + 3]);
+      store4_bf16(dvr + 32 * dt + 8 * a + 4 * h2, av[dt][4 * a], av[dt][4 * a + 1],
+                  av[dt][4 * a + 2], av[dt][4 * a + 3]);
+    }
+}
+
+template <int BS, int D, bool MASK>
+hipError_t launch_grads(const BwdArgs &a, hipStream_t stream) {
+  const float scale_log2 = a.scale * kLog2e;
+  {
+    const int64_t W = (int64_t)a.B * a.H * a.Mb;
+    const int64_t grid = (W + 7) / 8 * 8;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_dq_kernel<BS, D, MASK>), dim3((unsigned)grid), dim3(BS * 2), 0, stream,
+                       (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v,
+                       (const __bf16 *)a.dout, a.lse2, a.Dv, a.row_ptr, a.col_idx, a.row_order,
+                       a.B, a.H, a.Mb, a.Nb, scale_log2, a.scale, a.opt, (__bf16 *)a.dq);
+  }
+  {
+    const int32_t Hkv = a.H / a.opt.kv_group;
+    const int64_t W = (int64_t)a.B * Hkv * a.Nb;
+    const int64_t grid = (W + 7) / 8 * 8;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<BS, D, MASK>), dim3((unsigned)grid), dim3(BS * 2), 0,
+                       stream, (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v,
+                       (const __bf16 *)a.dout, a.lse2, a.Dv, a.col_ptr, a.row_idx, a.col_order,
+                       a.B, a.H, Hkv, a.Mb, a.Nb, scale_log2, a.scale, a.opt, (__bf16 *)a.dk,
+                       (__bf16 *)a.dv);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_pre(const BwdArgs &a, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.B * a.H * a.Mb * a.bs;
+  const int64_t rpb = 256 / (D / 8);
+  int64_t grid = (rows + rpb - 1) / rpb;
+  if (grid > 65536) grid = 65536;
+  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)grid), dim3(256), 0, stream,
+                     (const __bf16 *)a.out, (const __bf16 *)a.dout, a.lse, rows, a.Dv, a.lse2);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool backward_supported(int32_t bs, int32_t d) {
+  return (bs == 32 || bs == 64 || bs == 128) && (d == 32 || d == 64 || d == 128);
+}
+
+hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
+  if (!backward_supported(a.bs, a.d)) return hipErrorInvalidValue;
+  if (a.opt.kv_group < 1 || a.H % a.opt.kv_group != 0) return hipErrorInvalidValue;
+  hipError_t e = a.d == 32 ? launch_pre<32>(a, stream)
+               : a.d == 64 ? launch_pre<64>(a, stream)
+                           : launch_pre<128>(a, stream);
+  if (e != hipSuccess) return e;
+  const bool mask = a.opt.cap_k != 0.f || a.opt.causal != 0;
+#define BSA_BWD_CASE(BS_, D_)                                                                  \
+  if (a.bs == BS_ && a.d == D_) e = mask ? launch_grads<BS_, D_, true>(a, stream)             \
+                                         : launch_grads<BS_, D_, false>(a, stream);
+  BSA_BWD_CASE(32, 32) BSA_BWD_CASE(32, 64) BSA_BWD_CASE(32, 128)
+  BSA_BWD_CASE(64, 32) BSA_BWD_CASE(64, 64) BSA_BWD_CASE(64, 128)
+  BSA_BWD_CASE(128, 32) BSA_BWD_CASE(128, 64) BSA_BWD_CASE(128, 128)
+#undef BSA_BWD_CASE
+  if (e != hipSuccess) return e;
+  if (a.opt.sink != nullptr && a.dsink != nullptr) {
+    hipLaunchKernelGGL(bwd_dsink_kernel, dim3(a.H), dim3(256), 0, stream, (const float *)a.lse2,
+                       (const float *)a.Dv, a.opt.sink, a.B, a.H, (int64_t)a.Mb * a.bs, a.dsink);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace bsa

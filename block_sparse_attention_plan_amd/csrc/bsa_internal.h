@@ -37,6 +37,32 @@ hipError_t launch_forward(const void *q, const void *k, const void *v,
                           const FwdOptions &opt, void *out, float *lse, hipStream_t stream);
 bool forward_supported(int32_t bs, int32_t d);
 
+// Column plan (backward): byte offsets of col_ptr, col_order, nnz_total,
+// row_idx and the total size, all sections 256-byte aligned.
+struct PlanColsGeometry {
+  size_t off_col_ptr, off_col_order, off_nnz, off_row_idx, total;
+};
+bool plan_cols_geometry(int32_t H, int32_t Hkv, int32_t Mb, int32_t Nb, PlanColsGeometry *g);
+hipError_t launch_plan_cols(const int32_t *layout, int32_t H, int32_t Hkv, int32_t Mb, int32_t Nb,
+                            int32_t *col_ptr, int32_t *col_order, int32_t *nnz_total,
+                            int32_t *row_idx, hipStream_t stream);
+
+// Everything the backward launchers need (already validated).
+struct BwdArgs {
+  const void *q, *k, *v, *out, *dout;
+  const float *lse;                                    // forward lse (natural log)
+  const int32_t *row_ptr, *col_idx, *row_order;        // row plan
+  const int32_t *col_ptr, *row_idx, *col_order;        // column plan
+  int32_t B, H, Mb, Nb, bs, d;
+  float scale;
+  FwdOptions opt;
+  float *Dv, *lse2;                                    // workspace, B*H*Mb*bs floats each
+  void *dq, *dk, *dv;
+  float *dsink;                                        // [H] or nullptr
+};
+hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
+bool backward_supported(int32_t bs, int32_t d);
+
 hipError_t launch_topk(const void *q, const void *kv, const int32_t *idx,
                        const float *sink, int32_t B, int32_t M, int32_t N, int32_t H,
                        int32_t d, int32_t topk, float scale, void *out,

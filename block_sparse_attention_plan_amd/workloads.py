@@ -150,6 +150,12 @@ def make_bsa(name: str, B: int, H: int, S: int, bs: int, d: int, dtype: str, lay
                      seed=seed, params=params, sink=sink)
 
 
+def upstream_gradient(shape, seed: int, std: float = 1.0) -> torch.Tensor:
+    """An upstream gradient dO of the given shape: bf16 N(0, std^2) on the CPU."""
+    rng = np.random.default_rng(seed)
+    return _tensor(_normal(rng, tuple(int(x) for x in shape), std), "bf16")
+
+
 def sink_logits(H: int, mean: float, seed: int) -> torch.Tensor:
     """Per-head sink logits N(mean, 1), fp32 [H] on the CPU."""
     rng = np.random.default_rng(seed)

@@ -163,6 +163,86 @@ int bsa_forward_ex(const void *q, const void *k, const void *v, const bsa_plan_t
                    bsa_dtype_t dtype, float scale, const bsa_forward_opts_t *opts, void *out,
                    float *lse, void *stream);
 
+/* Column plan of a layout, for the backward: per key block n of query head
+ * h the live query blocks m, and the order of the key-block work items. */
+typedef struct {
+  int32_t H, Hkv, Mb, Nb;
+  void *dev_buf;
+  size_t dev_bytes;
+} bsa_plan_cols_t;
+
+/* Bytes a column-plan buffer needs (worst case: every tile live); 0 for bad
+ * dimensions (non-positive, Hkv not dividing H, or H*Mb*Nb >= 2^31). */
+size_t bsa_plan_cols_buffer_bytes(int32_t H, int32_t Hkv, int32_t Mb, int32_t Nb);
+
+/* Byte offsets of the four column-plan sections (col_ptr, col_order,
+ * nnz_total, row_idx).  Host-only. */
+int bsa_plan_cols_sections(int32_t H, int32_t Hkv, int32_t Mb, int32_t Nb, size_t offsets_out[4]);
+
+/*
+ * Build the column plan of a block layout: the transposed CSR the backward
+ * walks to accumulate dK and dV of one key block (next.gr tutorial, section
+ * 3.2 for the CSR form; "Gradient Propagation in Block Sparse Attention" for
+ * gradients flowing through the live blocks only).
+ *
+ *   col_ptr   [H*Nb+1]: column c = h*Nb + n holds row_idx[col_ptr[c] ..
+ *             col_ptr[c+1]), the live query blocks m in ascending order
+ *   col_order [Hkv*Nb]: key-block work items kvh*Nb + n, K/V head by K/V
+ *             head, each by its live tile count summed over the H/Hkv query
+ *             heads of the group, descending, ties by n ascending
+ *   layout    device, int32 [H, Mb, Nb], read only
+ *   Hkv       K/V heads (0 means H); H % Hkv == 0 and (H/Hkv)*Mb <= 16384
+ *   dev_buf   device, caller-owned, >= bsa_plan_cols_buffer_bytes bytes,
+ *             256-byte aligned; overwritten
+ * Errors: BSA_ERR_INVALID_ARG, BSA_ERR_UNSUPPORTED, BSA_ERR_MISALIGNED,
+ * BSA_ERR_BUFFER_TOO_SMALL, BSA_ERR_HIP.
+ */
+int bsa_plan_cols(const int32_t *layout, int32_t H, int32_t Hkv, int32_t Mb, int32_t Nb,
+                  void *dev_buf, size_t dev_bytes, bsa_plan_cols_t *plan_out, void *stream);
+
+/* Bytes of the backward's workspace: two fp32 values per query row. */
+size_t bsa_backward_workspace_bytes(int32_t B, int32_t H, int32_t Sq);
+
+/*
+ * Block-sparse attention backward: gradients of bsa_forward_ex's out.
+ *
+ * Operation: the chain rule of the forward, through the live tiles only
+ * (next.gr tutorial, "Gradient Propagation in Block Sparse Attention", and
+ * its block-structured Jacobian).  With c_ij the (capped) scaled score,
+ * P_ij = exp(c_ij - lse_i) and D_i = dout_i . out_i:
+ *   dv_j    = sum_i P_ij dout_i
+ *   ds_ij   = P_ij (dout_i . v_j - D_i) * (1 - tanh^2(s_ij / cap)) (no factor
+ *             without a cap)
+ *   dq_i    = scale sum_j ds_ij k_j,   dk_j = scale sum_i ds_ij q_i
+ *   dsink_h = -sum over b, i of exp(sink_h - lse_i) D_i
+ * Under grouped heads dk and dv of a K/V head sum over its query heads.
+ * Masked entries (outside the layout, or above the diagonal with causal)
+ * contribute nothing.
+ *
+ *   q, k, v, plan, B, H, Sq, Sk, bs, d, scale, opts: exactly as passed to
+ *         the forward that produced out and lse (same options)
+ *   out   device [B, H, Sq, d] bf16, the forward's output
+ *   dout  device [B, H, Sq, d] bf16, upstream gradient
+ *   lse   device fp32 [B, H, Sq], the forward's lse (required)
+ *   plan_cols  host pointer to a column plan of the same layout with
+ *         Hkv = the K/V head count (BSA_ERR_PLAN_MISMATCH otherwise)
+ *   workspace  device, caller-owned, >= bsa_backward_workspace_bytes,
+ *         16-byte aligned; overwritten (holds D and lse * log2 e)
+ *   dq    device [B, H, Sq, d] bf16, written
+ *   dk, dv  device [B, Hkv, Sk, d] bf16, written (every row)
+ *   dsink device fp32 [H], written when opts->attn_sink is set; may be NULL
+ * Supported: dtype BSA_BF16, bs in {32, 64, 128}, d in {32, 64, 128}.
+ * Deterministic: no atomics, so repeated calls give identical bits.
+ * Errors: as bsa_forward_ex, plus BSA_ERR_UNSUPPORTED for BSA_F32 or
+ * bs = 16, BSA_ERR_BUFFER_TOO_SMALL for a short workspace.
+ */
+int bsa_backward(const void *q, const void *k, const void *v, const void *out, const void *dout,
+                 const float *lse, const bsa_plan_t *plan, const bsa_plan_cols_t *plan_cols,
+                 int32_t B, int32_t H, int32_t Sq, int32_t Sk, int32_t bs, int32_t d,
+                 bsa_dtype_t dtype, float scale, const bsa_forward_opts_t *opts, void *workspace,
+                 size_t workspace_bytes, void *dq, void *dk, void *dv, float *dsink,
+                 void *stream);
+
 /*
  * Top-k gathered sparse attention forward with a per-head attention sink.
  *
