@@ -18,13 +18,18 @@ tile per head per batch item + 4*d*H per valid top-k index) / step time.
 After the timed steps, the forward with all of its optional terms (causal
 mask, per-head sink, tanh logit cap 50, eight K/V heads shared by the 32
 query heads) is timed on the same workload and reported beside the plain
-forward under kernels.bsa_forward_options; it is not part of `value`.
+forward under kernels.bsa_forward_options; it is not part of `value`.  Then
+the backward of the plain forward (column plan + bsa_backward for a random
+upstream gradient) is timed the same way, under kernels.bsa_backward, with
+its FLOPs counted as the 10*b^2*d per live tile of the five tile products a
+backward needs (the kernels execute 14: S and dP are recomputed once more).
 
 Flags: --gpus N (only 1 is supported), --steps K, --warmup W,
 --no-cpu-baseline (skip the oracle timing), --cpu-seconds S (oracle sample
 budget per kernel), --copy-calibration (also run one plain elementwise copy
 of 1 GiB, for HBM counter scaling under a profiler), --option-steps N (launches
-of the forward with options; 0 skips that leg).
+of the forward with options; 0 skips that leg), --backward-steps N (calls of
+the backward; 0 skips that leg).
 
 --summarize-counters FETCH_CSV WRITE_CSV (no GPU needed) turns the counter
 files of two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of
@@ -232,6 +237,7 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--option-steps", type=int, default=20)
+    ap.add_argument("--backward-steps", type=int, default=10)
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
@@ -328,6 +334,37 @@ def main(argv=None) -> int:
                    "traffic": measured_traffic("bsa_forward_options")}
         log(f"[bench] forward with options: {t_opt:.4f} ms")
 
+    bwd_leg = None
+    if args.backward_steps > 0:
+        dout = W.upstream_gradient(fwd.q.shape, seed=41).to(dev)
+        plan = bsa.bsa_plan(layout, buf=pbuf)
+        bsa.bsa_forward(q, k, v, plan, fwd.scale, out=out, lse=lse)
+        g_q, g_k, g_v = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(bsa.load_library().bsa_backward_workspace_bytes(B, H, S) // 4,
+                         dtype=torch.float32, device=dev)
+
+        def bwd():
+            pc = bsa.bsa_plan_cols(layout)
+            bsa.bsa_backward(q, k, v, out, dout, lse, plan, pc, fwd.scale, dq=g_q, dk=g_k,
+                             dv=g_v, workspace=ws)
+        for _ in range(2):
+            bwd()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.backward_steps):
+            bwd()
+        e1.record()
+        torch.cuda.synchronize()
+        t_bwd = e0.elapsed_time(e1) / args.backward_steps
+        b_flops = 2.5 * f_flops
+        b_tflops = b_flops / (t_bwd * 1e-3) / 1e12
+        bwd_leg = {"avg_ms": round(t_bwd, 5), "calls": args.backward_steps,
+                   "includes": "bsa_plan_cols + bsa_backward (D/lse pass, dq kernel, dk/dv kernel)",
+                   "flops": b_flops, "tflops": round(b_tflops, 2),
+                   "pct_bf16_peak": round(100 * b_tflops / PEAK_BF16_TFLOPS, 2)}
+        log(f"[bench] backward: {t_bwd:.4f} ms")
+
     if args.copy_calibration:
         # one full-grid elementwise kernel that reads 1 GiB and writes 1 GiB
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -355,6 +392,8 @@ def main(argv=None) -> int:
     }
     if opt_leg is not None:
         kernels["bsa_forward_options"] = opt_leg
+    if bwd_leg is not None:
+        kernels["bsa_backward"] = bwd_leg
     # dominant kernel of the step and its roofline
     if t_fwd >= t_topk:
         roof = {"kernel": "bsa_forward", "bound": "mfma", "achieved": round(fwd_tflops, 2),
