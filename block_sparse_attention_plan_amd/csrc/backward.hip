@@ -356,21 +356,23 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
       __syncthreads();
       const bool diag = MASK && opt.causal && m == n;
       // One 32-query chunk at a time: K^T, V^T and both accumulators stay
-      // live across the loop, so the chunks are not unrolled into each other.
+      // live across the loop, so the chunks are not unrolled into each other,
+      // and each chunk runs in phases (fenced against the scheduler) that keep
+      // at most one fp32 score block live besides them:
+      //   S = Q K^T -> P (bf16, and P * cap slope for the MASK instances)
+      //   dV^T += dO^T P beside dP = dO V^T
+      //   dS = P (dP - D) from the bf16 P -> dK^T += Q^T dS
 #pragma unroll 1
       for (int jq = 0; jq < JT; ++jq) {
-        f32x16 s = f32x16{}, dp = f32x16{};
+        f32x16 s = f32x16{};
 #pragma unroll
-        for (int c = 0; c < QC; ++c) {
+        for (int c = 0; c < QC; ++c)
           s = mfma32(row_read<D>(Qs, 32 * jq + l32, 2 * c + h2, sw_row), kf[c], s);
-          dp = mfma32(row_read<D>(Gs, 32 * jq + l32, 2 * c + h2, sw_row), vf[c], dp);
-        }
-        // S[query][key]: query 32jq + 8(e/4) + 4h2 + e%4, key krow.  P
-        // replaces S and dS replaces dP in place.
+        // S[query][key]: query 32jq + 8(e/4) + 4h2 + e%4, key krow
+        f32x16 w;   // P times the cap slope (MASK instances)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&Ls[32 * jq + 8 * a + 4 * h2]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&Ds[32 * jq + 8 * a + 4 * h2]);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int e = 4 * a + i;
@@ -378,25 +380,52 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
             float p = wt.p;
             if (diag && krow > 32 * jq + 8 * a + 4 * h2 + i) p = 0.f;
             s[e] = p;
-            dp[e] = p * (dp[e] - d4[i]) * wt.slope;
+            if constexpr (MASK) w[e] = p * wt.slope;
           }
         }
-        const f32x16 &ds = dp;
+        bf16x8 pf[2], wf[2];
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
-          const bf16x8 pf = to_bf16x8(s[8 * c2 + 0], s[8 * c2 + 1], s[8 * c2 + 2], s[8 * c2 + 3],
-                                      s[8 * c2 + 4], s[8 * c2 + 5], s[8 * c2 + 6], s[8 * c2 + 7]);
-          const bf16x8 dsf = to_bf16x8(ds[8 * c2 + 0], ds[8 * c2 + 1], ds[8 * c2 + 2],
-                                       ds[8 * c2 + 3], ds[8 * c2 + 4], ds[8 * c2 + 5],
-                                       ds[8 * c2 + 6], ds[8 * c2 + 7]);
+          pf[c2] = to_bf16x8(s[8 * c2 + 0], s[8 * c2 + 1], s[8 * c2 + 2], s[8 * c2 + 3],
+                             s[8 * c2 + 4], s[8 * c2 + 5], s[8 * c2 + 6], s[8 * c2 + 7]);
+          if constexpr (MASK)
+            wf[c2] = to_bf16x8(w[8 * c2 + 0], w[8 * c2 + 1], w[8 * c2 + 2], w[8 * c2 + 3],
+                               w[8 * c2 + 4], w[8 * c2 + 5], w[8 * c2 + 6], w[8 * c2 + 7]);
+          else
+            wf[c2] = pf[c2];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 dp = f32x16{};
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            av[dt] = mfma32(tr_read<D>(Gs, 32 * jq + 16 * c2, dt, tr_r, lc_off, pc, sw0, sw8), pf,
-                            av[dt]);
-            ak[dt] = mfma32(tr_read<D>(Qs, 32 * jq + 16 * c2, dt, tr_r, lc_off, pc, sw0, sw8), dsf,
-                            ak[dt]);
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            av[dt] = mfma32(tr_read<D>(Gs, 32 * jq + 16 * c2, dt, tr_r, lc_off, pc, sw0, sw8),
+                            pf[c2], av[dt]);
+#pragma unroll
+        for (int c = 0; c < QC; ++c)
+          dp = mfma32(row_read<D>(Gs, 32 * jq + l32, 2 * c + h2, sw_row), vf[c], dp);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&Ds[32 * jq + 8 * a + 4 * h2]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = 4 * a + i;
+            dp[e] = (float)wf[e / 8][e % 8] * (dp[e] - d4[i]);
           }
         }
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const bf16x8 dsf = to_bf16x8(dp[8 * c2 + 0], dp[8 * c2 + 1], dp[8 * c2 + 2],
+                                       dp[8 * c2 + 3], dp[8 * c2 + 4], dp[8 * c2 + 5],
+                                       dp[8 * c2 + 6], dp[8 * c2 + 7]);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            ak[dt] = mfma32(tr_read<D>(Qs, 32 * jq + 16 * c2, dt, tr_r, lc_off, pc, sw0, sw8), dsf,
+                            ak[dt]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -431,7 +460,8 @@ hipError_t launch_grads(const BwdArgs &a, hipStream_t stream) {
     const int64_t grid = (W + 7) / 8 * 8;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL((bwd_dkdv_kernel<BS, D, MASK>), dim3((unsigned)grid), dim3(BS * 2), 0,
-                       stream, (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v,
+                       stream,
+                       (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v,
                        (const __bf16 *)a.dout, a.lse2, a.Dv, a.col_ptr, a.row_idx, a.col_order,
                        a.B, a.H, Hkv, a.Mb, a.Nb, scale_log2, a.scale, a.opt, (__bf16 *)a.dk,
                        (__bf16 *)a.dv);
