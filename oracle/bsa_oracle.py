@@ -73,6 +73,7 @@ __all__ = [
     "plan_columns",
     "attention_backward_dense",
     "attention_backward_live_tiles",
+    "adaptive_layout",
     "topk_attention",
 ]
 
@@ -472,6 +473,54 @@ def attention_backward_live_tiles(q, k, v, dout, layout, bs: int, scale: float, 
             w = np.where(np.isfinite(lse), np.exp(sk[None, :, None] - np.where(np.isfinite(lse), lse, 0.0)), 0.0)
         dsink = -(w * D).sum(axis=(0, 2))
     return dq, dk, dv, dsink
+
+
+# --------------------------------------------------------------------------
+# Content-adaptive block layout
+# --------------------------------------------------------------------------
+
+def adaptive_layout(q, k, bs: int, tau: float, *, causal: bool = False,
+                    keep_diagonal: bool = True):
+    """Block layout chosen from the content of q and k.
+
+    The next.gr tutorial ("Fixed vs. Adaptive Block Sparsity") marks a pair
+    live when sim(Q_i, K_j) >= tau, naming cosine similarity as the metric;
+    the Language AI Handbook ("Block Structure" discussion of choosing which
+    blocks to attend) scores the candidates at a coarser granularity than
+    tokens.  Reading used here: Q_i and K_j are the mean of the query rows of
+    block i and of the key rows of block j (mean pooling over the block's
+    tokens), sim is their cosine similarity (0 when either mean is the zero
+    vector), and a block pair is live when sim >= tau.  With ``causal`` only
+    pairs with j <= i may be live; with ``keep_diagonal`` the pairs j == i
+    are always live, so that every block row keeps a tile.
+
+    q: [H, Sq, d], k: [Hkv, Sk, d] (one batch item; query head h reads K/V
+    head h // (H / Hkv)).  Returns (layout int32 [H, Sq/bs, Sk/bs], sim).
+    """
+    q, k = _as64(q), _as64(k)
+    H, Sq, d = q.shape
+    Hkv, Sk, _ = k.shape
+    kvh = _kv_head(H, Hkv)
+    Mb, Nb = Sq // bs, Sk // bs
+    if Mb * bs != Sq or Nb * bs != Sk:
+        raise ValueError("sequence lengths must be multiples of the block size")
+    qbar = q.reshape(H, Mb, bs, d).mean(axis=2)
+    kbar = k.reshape(Hkv, Nb, bs, d).mean(axis=2)
+
+    def unit(x):
+        nrm = np.linalg.norm(x, axis=-1, keepdims=True)
+        return np.where(nrm > 0, x / np.where(nrm > 0, nrm, 1.0), 0.0)
+
+    qh, kh = unit(qbar), unit(kbar)
+    sim = np.stack([qh[h] @ kh[kvh(h)].T for h in range(H)])        # [H, Mb, Nb]
+    live = sim >= tau
+    m = np.arange(Mb)[:, None]
+    n = np.arange(Nb)[None, :]
+    if causal:
+        live &= (n <= m)[None]
+    if keep_diagonal:
+        live |= (n == m)[None]
+    return live.astype(np.int32), sim
 
 
 # --------------------------------------------------------------------------
