@@ -23,13 +23,17 @@ the backward of the plain forward (column plan + bsa_backward for a random
 upstream gradient) is timed the same way, under kernels.bsa_backward, with
 its FLOPs counted as the 10*b^2*d per live tile of the five tile products a
 backward needs (the kernels execute 14: S and dP are recomputed once more).
+Last, the content-adaptive layout producer runs on the same q and k (block
+means, cosine scores, threshold) under kernels.bsa_layout_adaptive, reported
+against HBM bandwidth for the q and k bytes it must read.
 
 Flags: --gpus N (only 1 is supported), --steps K, --warmup W,
 --no-cpu-baseline (skip the oracle timing), --cpu-seconds S (oracle sample
 budget per kernel), --copy-calibration (also run one plain elementwise copy
 of 1 GiB, for HBM counter scaling under a profiler), --option-steps N (launches
 of the forward with options; 0 skips that leg), --backward-steps N (calls of
-the backward; 0 skips that leg).
+the backward; 0 skips that leg), --adaptive-steps N (calls of the adaptive
+layout producer; 0 skips that leg).
 
 --summarize-counters FETCH_CSV WRITE_CSV (no GPU needed) turns the counter
 files of two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of
@@ -238,6 +242,7 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--option-steps", type=int, default=20)
     ap.add_argument("--backward-steps", type=int, default=10)
+    ap.add_argument("--adaptive-steps", type=int, default=20)
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
@@ -365,6 +370,29 @@ def main(argv=None) -> int:
                    "pct_bf16_peak": round(100 * b_tflops / PEAK_BF16_TFLOPS, 2)}
         log(f"[bench] backward: {t_bwd:.4f} ms")
 
+    ad_leg = None
+    if args.adaptive_steps > 0:
+        q0, k0 = q[0], k[0]
+        ad_ws = torch.empty(bsa.load_library().bsa_layout_adaptive_workspace_bytes(
+            H, H, S // fwd.bs, S // fwd.bs, d) // 4, dtype=torch.float32, device=dev)
+        for _ in range(3):
+            bsa.bsa_layout_adaptive(q0, k0, fwd.bs, 0.1, causal=True, workspace=ad_ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.adaptive_steps):
+            bsa.bsa_layout_adaptive(q0, k0, fwd.bs, 0.1, causal=True, workspace=ad_ws)
+        e1.record()
+        torch.cuda.synchronize()
+        t_ad = e0.elapsed_time(e1) / args.adaptive_steps
+        ad_bytes = float(q0.numel() + k0.numel()) * q0.element_size()
+        ad_gbs = ad_bytes / (t_ad * 1e-3) / 1e9
+        ad_leg = {"avg_ms": round(t_ad, 5), "calls": args.adaptive_steps,
+                  "config": f"H{H} S{S} bs{fwd.bs} d{d} bf16, tau 0.1, causal",
+                  "algorithmic_bytes": ad_bytes, "algorithmic_gbs": round(ad_gbs, 1),
+                  "pct_hbm_peak": round(100 * ad_gbs / PEAK_HBM_GBS, 2)}
+        log(f"[bench] adaptive layout: {t_ad:.4f} ms")
+
     if args.copy_calibration:
         # one full-grid elementwise kernel that reads 1 GiB and writes 1 GiB
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -394,6 +422,8 @@ def main(argv=None) -> int:
         kernels["bsa_forward_options"] = opt_leg
     if bwd_leg is not None:
         kernels["bsa_backward"] = bwd_leg
+    if ad_leg is not None:
+        kernels["bsa_layout_adaptive"] = ad_leg
     # dominant kernel of the step and its roofline
     if t_fwd >= t_topk:
         roof = {"kernel": "bsa_forward", "bound": "mfma", "achieved": round(fwd_tflops, 2),

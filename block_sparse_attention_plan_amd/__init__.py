@@ -12,6 +12,7 @@ missing, every call raises.
     bsa_plan_cols(layout, kv_heads)       -> PlanCols (per-column CSR, backward)
     bsa_backward(q, k, v, out, dout, lse, plan, plan_cols, scale, *, options)
                                           -> (dq, dk, dv, dsink)
+    bsa_layout_adaptive(q, k, bs, tau, causal, keep_diagonal) -> (layout, scores)
     topk_sparse_attn(q, kv, idx, attn_sink, scale) -> out
 """
 
@@ -34,6 +35,7 @@ __all__ = [
     "PlanCols",
     "bsa_plan_cols",
     "bsa_backward",
+    "bsa_layout_adaptive",
     "topk_sparse_attn",
     "library_path",
     "load_library",
@@ -111,6 +113,11 @@ def load_library():
                                  f32, ctypes.POINTER(_FwdOptsT), vp, ctypes.c_size_t, vp, vp, vp,
                                  vp, vp]
     lib.bsa_backward.restype = ctypes.c_int
+    lib.bsa_layout_adaptive_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.bsa_layout_adaptive_workspace_bytes.restype = ctypes.c_size_t
+    lib.bsa_layout_adaptive.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, i32,
+                                        vp, ctypes.c_size_t, vp, vp, vp]
+    lib.bsa_layout_adaptive.restype = ctypes.c_int
     lib.topk_sparse_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp]
     lib.topk_sparse_attn.restype = ctypes.c_int
     lib.bsa_status_string.argtypes = [ctypes.c_int]
@@ -422,6 +429,44 @@ def bsa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
         ctypes.c_void_p(dk.data_ptr()), ctypes.c_void_p(dv.data_ptr()),
         ctypes.c_void_p(dsink.data_ptr() if dsink is not None else 0), _stream(q)))
     return dq, dk, dv, dsink
+
+
+def bsa_layout_adaptive(q: torch.Tensor, k: torch.Tensor, bs: int, tau: float, *,
+                        causal: bool = False, keep_diagonal: bool = True,
+                        want_scores: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Content-adaptive block layout of one batch item.
+
+    q: [H, Sq, d], k: [Hkv, Sk, d] (bf16 or fp32, same dtype).  Returns
+    (layout int32 [H, Sq/bs, Sk/bs], scores fp32 of the same shape or None):
+    a block pair is live when the cosine similarity of its block-mean query
+    and key reaches tau.
+    """
+    for name, t in (("q", q), ("k", k)):
+        _require_gpu(name, t)
+        if t.dim() != 3:
+            raise ValueError(f"{name} must be [heads, S, d]")
+    if q.dtype != k.dtype or q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q and k must share dtype bf16 or fp32")
+    H, Sq, d = (int(x) for x in q.shape)
+    Hkv, Sk = int(k.shape[0]), int(k.shape[1])
+    if int(k.shape[2]) != d or H % Hkv:
+        raise ValueError("k must be [Hkv, Sk, d] with Hkv dividing H")
+    if Sq % bs or Sk % bs:
+        raise ValueError("Sq and Sk must be multiples of bs")
+    lib = load_library()
+    Mb, Nb = Sq // bs, Sk // bs
+    wbytes = lib.bsa_layout_adaptive_workspace_bytes(H, Hkv, Mb, Nb, d)
+    if workspace is None:
+        workspace = torch.empty(max(wbytes // 4, 1), dtype=torch.float32, device=q.device)
+    layout = torch.empty((H, Mb, Nb), dtype=torch.int32, device=q.device)
+    scores = torch.empty((H, Mb, Nb), dtype=torch.float32, device=q.device) if want_scores else None
+    _check(lib.bsa_layout_adaptive(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), H, Hkv, Sq, Sk, int(bs), d,
+        BSA_BF16 if q.dtype == torch.bfloat16 else BSA_F32, float(tau), 1 if causal else 0,
+        1 if keep_diagonal else 0, ctypes.c_void_p(workspace.data_ptr()),
+        workspace.numel() * workspace.element_size(), ctypes.c_void_p(layout.data_ptr()),
+        ctypes.c_void_p(scores.data_ptr() if scores is not None else 0), _stream(q)))
+    return layout, scores
 
 
 def topk_sparse_attn(q: torch.Tensor, kv: torch.Tensor, idx: torch.Tensor,

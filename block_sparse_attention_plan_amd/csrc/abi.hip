@@ -314,6 +314,51 @@ int bsa_backward(const void *q, const void *k, const void *v, const void *out, c
   return BSA_OK;
 }
 
+size_t bsa_layout_adaptive_workspace_bytes(int32_t H, int32_t Hkv, int32_t Mb, int32_t Nb,
+                                           int32_t d) {
+  if (H <= 0 || Hkv <= 0 || Mb <= 0 || Nb <= 0 || d <= 0) return 0;
+  return ((size_t)H * Mb + (size_t)Hkv * Nb) * (size_t)d * sizeof(float);
+}
+
+int bsa_layout_adaptive(const void *q, const void *k, int32_t H, int32_t Hkv, int32_t Sq,
+                        int32_t Sk, int32_t bs, int32_t d, bsa_dtype_t dtype, float tau,
+                        int32_t causal, int32_t keep_diagonal, void *workspace,
+                        size_t workspace_bytes, int32_t *layout_out, float *scores_out,
+                        void *stream) {
+  if (q == nullptr || k == nullptr || workspace == nullptr || layout_out == nullptr)
+    return fail(BSA_ERR_INVALID_ARG, "bsa_layout_adaptive: NULL pointer argument");
+  if (H <= 0 || Sq <= 0 || Sk <= 0 || bs <= 0 || d <= 0)
+    return fail(BSA_ERR_INVALID_ARG, "bsa_layout_adaptive: sizes must be positive");
+  if (Hkv == 0) Hkv = H;
+  if (Hkv < 1 || H % Hkv != 0)
+    return fail(BSA_ERR_INVALID_ARG, "bsa_layout_adaptive: Hkv=%d must divide H=%d", Hkv, H);
+  if (Sq % bs != 0 || Sk % bs != 0)
+    return fail(BSA_ERR_INVALID_ARG, "bsa_layout_adaptive: Sq=%d and Sk=%d must be multiples of "
+                "bs=%d", Sq, Sk, bs);
+  if (dtype != BSA_BF16 && dtype != BSA_F32)
+    return fail(BSA_ERR_INVALID_ARG, "bsa_layout_adaptive: unknown dtype %d", (int)dtype);
+  if (!std::isfinite(tau))
+    return fail(BSA_ERR_INVALID_ARG, "bsa_layout_adaptive: tau must be finite");
+  if (!bsa::adaptive_supported(bs, d))
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_layout_adaptive: no kernel for bs=%d d=%d", bs, d);
+  const int32_t Mb = Sq / bs, Nb = Sk / bs;
+  if ((int64_t)H * Mb * Nb >= (int64_t(1) << 31) || (int64_t)H * Mb + (int64_t)Hkv * Nb >= (1 << 30))
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_layout_adaptive: problem too large");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(workspace, 16) || !aligned(layout_out, 4) ||
+      (scores_out != nullptr && !aligned(scores_out, 4)))
+    return fail(BSA_ERR_MISALIGNED, "bsa_layout_adaptive: misaligned pointer");
+  const size_t ws = bsa_layout_adaptive_workspace_bytes(H, Hkv, Mb, Nb, d);
+  if (workspace_bytes < ws)
+    return fail(BSA_ERR_BUFFER_TOO_SMALL, "bsa_layout_adaptive: workspace is %zu bytes, needs %zu",
+                workspace_bytes, ws);
+  hipError_t e = bsa::launch_adaptive(q, k, H, Hkv, Mb, Nb, bs, d, dtype == BSA_F32, tau,
+                                      causal != 0, keep_diagonal != 0,
+                                      static_cast<float *>(workspace), layout_out, scores_out,
+                                      (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "bsa_layout_adaptive launch");
+  return BSA_OK;
+}
+
 int topk_sparse_attn(const void *q, const void *kv, const int32_t *idx, const float *attn_sink,
                      int32_t B, int32_t M, int32_t N, int32_t H, int32_t d, int32_t topk,
                      float scale, void *out, void *stream) {

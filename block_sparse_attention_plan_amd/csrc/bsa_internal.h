@@ -63,6 +63,14 @@ struct BwdArgs {
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
 bool backward_supported(int32_t bs, int32_t d);
 
+// Content-adaptive layout of one batch item; unit = workspace of
+// (H*Mb + Hkv*Nb)*d floats; scores may be nullptr.
+hipError_t launch_adaptive(const void *q, const void *k, int32_t H, int32_t Hkv, int32_t Mb,
+                           int32_t Nb, int32_t bs, int32_t d, bool f32, float tau, int32_t causal,
+                           int32_t keep_diagonal, float *unit, int32_t *layout, float *scores,
+                           hipStream_t stream);
+bool adaptive_supported(int32_t bs, int32_t d);
+
 hipError_t launch_topk(const void *q, const void *kv, const int32_t *idx,
                        const float *sink, int32_t B, int32_t M, int32_t N, int32_t H,
                        int32_t d, int32_t topk, float scale, void *out,

@@ -156,6 +156,30 @@ def upstream_gradient(shape, seed: int, std: float = 1.0) -> torch.Tensor:
     return _tensor(_normal(rng, tuple(int(x) for x in shape), std), "bf16")
 
 
+def make_topic_qk(H: int, Hkv: int, S: int, d: int, bs: int, n_topics: int, noise: float,
+                  seed: int, dtype: str = "bf16"):
+    """Queries and keys whose blocks each carry a topic: every token of block
+    m of head h is topic_vector[h, t(h, m)] plus N(0, noise^2) noise, the
+    topics drawn uniformly per (head, block).  Returns CPU q [H, S, d],
+    k [Hkv, S, d] and the topic ids (q topics [H, S/bs], k topics
+    [Hkv, S/bs]); blocks that share a topic have similar means."""
+    rng = np.random.default_rng(seed)
+    nb = S // bs
+    basis = rng.standard_normal((max(H, Hkv), n_topics, d)).astype(np.float32)
+    tq = rng.integers(0, n_topics, (H, nb))
+    tk = rng.integers(0, n_topics, (Hkv, nb))
+    g = H // Hkv
+    q = np.empty((H, S, d), np.float32)
+    k = np.empty((Hkv, S, d), np.float32)
+    for h in range(H):
+        q[h] = np.repeat(basis[h // g][tq[h]], bs, axis=0)
+    for j in range(Hkv):
+        k[j] = np.repeat(basis[j][tk[j]], bs, axis=0)
+    q += _normal(rng, q.shape, noise)
+    k += _normal(rng, k.shape, noise)
+    return _tensor(q, dtype), _tensor(k, dtype), tq, tk
+
+
 def sink_logits(H: int, mean: float, seed: int) -> torch.Tensor:
     """Per-head sink logits N(mean, 1), fp32 [H] on the CPU."""
     rng = np.random.default_rng(seed)

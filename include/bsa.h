@@ -243,6 +243,43 @@ int bsa_backward(const void *q, const void *k, const void *v, const void *out, c
                  size_t workspace_bytes, void *dq, void *dk, void *dv, float *dsink,
                  void *stream);
 
+/* Bytes of the adaptive-layout workspace: (H*Mb + Hkv*Nb) * d floats. */
+size_t bsa_layout_adaptive_workspace_bytes(int32_t H, int32_t Hkv, int32_t Mb, int32_t Nb,
+                                           int32_t d);
+
+/*
+ * Content-adaptive block layout of one batch item.
+ *
+ * Operation (next.gr tutorial, "Fixed vs. Adaptive Block Sparsity": a pair
+ * is live when the similarity of its queries and keys reaches a threshold,
+ * cosine similarity named as the metric; Language AI Handbook: blocks chosen
+ * from similarity scores at a coarser granularity than tokens).  Each block
+ * is represented by the mean of its rows:
+ *   score(h, m, n)  = cos(mean q[h, m*bs .. m*bs+bs-1, :],
+ *                         mean k[h / (H/Hkv), n*bs .. n*bs+bs-1, :])
+ *                     (0 when either mean is the zero vector)
+ *   layout[h][m][n] = score >= tau, then 0 where causal and n > m, then 1
+ *                     where keep_diagonal and n == m
+ * The layout feeds bsa_plan / bsa_plan_cols directly.
+ *
+ *   q     device [H, Sq, d], k device [Hkv, Sk, d] of dtype (one batch item)
+ *   Hkv   0 means H; must divide H.  Sq, Sk multiples of bs; bs a multiple of
+ *         16; d in {32, 64, 128}
+ *   tau   finite threshold (cosine scale, [-1, 1] meaningful)
+ *   workspace  device, caller-owned, >= bsa_layout_adaptive_workspace_bytes,
+ *         16-byte aligned; overwritten (the unit block means)
+ *   layout_out device int32 [H, Sq/bs, Sk/bs], written
+ *   scores_out device fp32 [H, Sq/bs, Sk/bs] or NULL, written when given
+ * Scores are fp32 sums in a fixed order, so repeated calls agree bit for
+ * bit.  Errors: BSA_ERR_INVALID_ARG, BSA_ERR_UNSUPPORTED, BSA_ERR_MISALIGNED,
+ * BSA_ERR_BUFFER_TOO_SMALL, BSA_ERR_HIP.
+ */
+int bsa_layout_adaptive(const void *q, const void *k, int32_t H, int32_t Hkv, int32_t Sq,
+                        int32_t Sk, int32_t bs, int32_t d, bsa_dtype_t dtype, float tau,
+                        int32_t causal, int32_t keep_diagonal, void *workspace,
+                        size_t workspace_bytes, int32_t *layout_out, float *scores_out,
+                        void *stream);
+
 /*
  * Top-k gathered sparse attention forward with a per-head attention sink.
  *
