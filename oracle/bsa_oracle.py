@@ -47,7 +47,10 @@ Readings where the pages are silent (each is listed in the design notes):
   so a row with no live key then has out = 0 and lse = sink_h.
 * With kv_heads = H / g, query head h reads key/value head h // g (groups of
   g consecutive query heads share one K/V head).
-* Sequence lengths are multiples of the block size.
+* Sequence lengths need not be multiples of the block size: as in the
+  Language AI Handbook's create_block_sparse_mask (ceil(len / bs) blocks, the
+  last block ending at the sequence end), a layout [H, ceil(Sq/bs),
+  ceil(Sk/bs)] covers the sequences and its token mask is cut to [Sq, Sk].
 * An absent sink (None) is the same as a sink of -infinity.
 * Duplicate top-k indices count once per occurrence.
 
@@ -142,15 +145,28 @@ def plan(layout: np.ndarray) -> PlanRef:
 # Block-sparse attention forward
 # --------------------------------------------------------------------------
 
-def token_mask(layout: np.ndarray, bs: int) -> np.ndarray:
-    """Expand a block layout [H, Mb, Nb] into a token mask [H, Mb*bs, Nb*bs].
+def token_mask(layout: np.ndarray, bs: int, Sq: Optional[int] = None,
+               Sk: Optional[int] = None) -> np.ndarray:
+    """Expand a block layout [H, Mb, Nb] into a token mask [H, Sq, Sk]
+    (default Sq = Mb*bs, Sk = Nb*bs; shorter lengths cut the last block).
 
     Every token of query block m sees every token of key block n iff
     layout[h, m, n] != 0 -- the block-to-token expansion of the Language AI
-    Handbook's create_block_sparse_mask example.
+    Handbook's create_block_sparse_mask example, whose last block ends at the
+    sequence end.
     """
     live = (np.asarray(layout) != 0)
-    return np.repeat(np.repeat(live, bs, axis=1), bs, axis=2)
+    Mb, Nb = live.shape[1], live.shape[2]
+    Sq = Mb * bs if Sq is None else Sq
+    Sk = Nb * bs if Sk is None else Sk
+    if _nblocks(Sq, bs) != Mb or _nblocks(Sk, bs) != Nb:
+        raise ValueError("layout does not cover the sequence lengths")
+    return np.repeat(np.repeat(live, bs, axis=1), bs, axis=2)[:, :Sq, :Sk]
+
+
+def _nblocks(S: int, bs: int) -> int:
+    """Blocks covering S tokens: ceil(S / bs) (the last one may be partial)."""
+    return (S + bs - 1) // bs
 
 
 def _as64(x) -> np.ndarray:
@@ -192,7 +208,7 @@ def attention_dense_masked(q, k, v, layout, bs: int, scale: float, *, sink=None,
     kvh = _kv_head(H, k.shape[1])
     k = k[:, [kvh(h) for h in range(H)]]
     v = v[:, [kvh(h) for h in range(H)]]
-    mask = token_mask(layout, bs)
+    mask = token_mask(layout, bs, Sq, Sk)
     if mask.shape != (H, Sq, Sk):
         raise ValueError("layout does not match q/k shapes")
     if causal:
@@ -235,8 +251,9 @@ def attention_live_tiles(q, k, v, layout, bs: int, scale: float,
     B, H, Sq, d = q.shape
     kvh = _kv_head(H, k.shape[1])
     lay = np.asarray(layout) != 0
-    Mb = Sq // bs
-    if lay.shape[0] != H or lay.shape[1] != Mb or lay.shape[2] * bs != k.shape[2]:
+    Sk = k.shape[2]
+    Mb = _nblocks(Sq, bs)
+    if lay.shape[0] != H or lay.shape[1] != Mb or lay.shape[2] != _nblocks(Sk, bs):
         raise ValueError("layout does not match q/k shapes")
     sk = None if sink is None else _as64(sink)
     out = np.full((B, H, Sq, v.shape[3]), np.nan)
@@ -245,14 +262,16 @@ def attention_live_tiles(q, k, v, layout, bs: int, scale: float,
         row_blocks = [(b, h, m) for b in range(B) for h in range(H) for m in range(Mb)]
     offs = np.arange(bs)
     for (b, h, m) in row_blocks:
-        rows = slice(m * bs, (m + 1) * bs)
+        rows = slice(m * bs, min((m + 1) * bs, Sq))
+        nr = rows.stop - rows.start
         cols = np.flatnonzero(lay[h, m])
         tok = (cols[:, None] * bs + offs[None, :]).reshape(-1)
-        s = _cap(scale * (q[b, h, rows] @ k[b, kvh(h), tok].T), soft_cap)   # [bs, T]
+        tok = tok[tok < Sk]                                   # the last key block may be cut
+        s = _cap(scale * (q[b, h, rows] @ k[b, kvh(h), tok].T), soft_cap)   # [nr, T]
         if causal:
-            qpos = m * bs + offs
+            qpos = m * bs + offs[:nr]
             s = np.where(tok[None, :] <= qpos[:, None], s, -np.inf)
-        mx = s.max(axis=1) if tok.size else np.full(bs, -np.inf)
+        mx = s.max(axis=1) if tok.size else np.full(nr, -np.inf)
         if sk is not None:
             mx = np.maximum(mx, sk[h])
         live = np.isfinite(mx)
@@ -362,7 +381,7 @@ def attention_backward_dense(q, k, v, dout, layout, bs: int, scale: float, *, si
     kvh = _kv_head(H, Hkv)
     heads = [kvh(h) for h in range(H)]
     kx, vx = k[:, heads], v[:, heads]                        # per query head
-    mask = token_mask(layout, bs)
+    mask = token_mask(layout, bs, Sq, Sk)
     if mask.shape != (H, Sq, Sk):
         raise ValueError("layout does not match q/k shapes")
     if causal:
@@ -412,7 +431,7 @@ def attention_backward_live_tiles(q, k, v, dout, layout, bs: int, scale: float, 
     kvh = _kv_head(H, Hkv)
     g = H // Hkv
     lay = np.asarray(layout) != 0
-    Mb, Nb = Sq // bs, Sk // bs
+    Mb, Nb = _nblocks(Sq, bs), _nblocks(Sk, bs)
     if lay.shape != (H, Mb, Nb):
         raise ValueError("layout does not match q/k shapes")
     full = row_blocks is None and col_blocks is None
@@ -428,16 +447,23 @@ def attention_backward_live_tiles(q, k, v, dout, layout, bs: int, scale: float, 
     out, lse = attention_live_tiles(q, k, v, layout, bs, scale, row_blocks=need, sink=sink,
                                     soft_cap=soft_cap, causal=causal)
     D = (dout * out).sum(axis=-1)                            # NaN where not computed
-    offs = np.arange(bs)
+
+    def rows_of(m):
+        return slice(m * bs, min((m + 1) * bs, Sq))
+
+    def keys_of(n):
+        return slice(n * bs, min((n + 1) * bs, Sk))
 
     def tile_terms(b, h, m, n):
-        """P, dS of tile (m, n) of head h: [bs queries, bs keys]."""
-        rows = slice(m * bs, (m + 1) * bs)
-        keys = slice(n * bs, (n + 1) * bs)
+        """P, dS of tile (m, n) of head h: [queries, keys] of the tile (the
+        last block row / column may be cut short)."""
+        rows, keys = rows_of(m), keys_of(n)
         s = scale * (q[b, h, rows] @ k[b, kvh(h), keys].T)
         c = _cap(s, soft_cap)
         if causal:
-            c = np.where((n * bs + offs)[None, :] <= (m * bs + offs)[:, None], c, -np.inf)
+            qpos = np.arange(rows.start, rows.stop)
+            kpos = np.arange(keys.start, keys.stop)
+            c = np.where(kpos[None, :] <= qpos[:, None], c, -np.inf)
         lr = lse[b, h, rows][:, None]
         live = np.isfinite(lr)
         with np.errstate(invalid="ignore"):
@@ -448,24 +474,26 @@ def attention_backward_live_tiles(q, k, v, dout, layout, bs: int, scale: float, 
 
     dq = np.full(q.shape, np.nan)
     for (b, h, m) in row_blocks:
-        acc = np.zeros((bs, d))
+        rows = rows_of(m)
+        acc = np.zeros((rows.stop - rows.start, d))
         for n in np.flatnonzero(lay[h, m]):
             _, ds = tile_terms(b, h, m, int(n))
-            acc += scale * ds @ k[b, kvh(h), n * bs:(n + 1) * bs]
-        dq[b, h, m * bs:(m + 1) * bs] = acc
+            acc += scale * ds @ k[b, kvh(h), keys_of(int(n))]
+        dq[b, h, rows] = acc
     dk = np.full(k.shape, np.nan)
     dv = np.full(v.shape, np.nan)
     for (b, j, n) in col_blocks:
-        ak = np.zeros((bs, d))
-        av = np.zeros((bs, v.shape[3]))
+        keys = keys_of(n)
+        ak = np.zeros((keys.stop - keys.start, d))
+        av = np.zeros((keys.stop - keys.start, v.shape[3]))
         for h in range(j * g, (j + 1) * g):
             for m in np.flatnonzero(lay[h, :, n]):
                 p, ds = tile_terms(b, h, int(m), n)
-                rows = slice(int(m) * bs, (int(m) + 1) * bs)
+                rows = rows_of(int(m))
                 av += p.T @ dout[b, h, rows]
                 ak += scale * ds.T @ q[b, h, rows]
-        dk[b, j, n * bs:(n + 1) * bs] = ak
-        dv[b, j, n * bs:(n + 1) * bs] = av
+        dk[b, j, keys] = ak
+        dv[b, j, keys] = av
     dsink = None
     if full and sink is not None:
         sk = _as64(sink)

@@ -188,3 +188,27 @@ def test_plan_columns_brute_force():
                 seq.append(j * Nb + best)
                 del work[best]
             assert list(pc.col_order[j * Nb:(j + 1) * Nb]) == seq
+
+
+@pytest.mark.parametrize("Sq,Sk", [(7, 9), (6, 5)])
+def test_backward_ragged_matches_finite_differences(Sq, Sk):
+    """Cut last blocks (bs = 4): the dense and live-tile backward agree with
+    central differences of the forward oracle."""
+    bs, d, H = 4, 3, 2
+    rng = np.random.default_rng(Sq + 10 * Sk)
+    Mb, Nb = -(-Sq // bs), -(-Sk // bs)
+    q = rng.standard_normal((1, H, Sq, d))
+    k = rng.standard_normal((1, 1, Sk, d))
+    v = rng.standard_normal((1, 1, Sk, d))
+    dout = rng.standard_normal((1, H, Sq, d))
+    lay = (rng.random((H, Mb, Nb)) < 0.7).astype(np.int32)
+    lay[:, :, Nb - 1] = 1
+    kw = dict(causal=True, sink=rng.standard_normal(H), soft_cap=1.1)
+    dq, dk, dv, ds = O.attention_backward_dense(q, k, v, dout, lay, bs, 0.6, **kw)
+    f = lambda: _loss(q, k, v, dout, lay, bs, 0.6, **kw)  # noqa: E731
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = _fd(f, x)
+        assert np.abs(num - g).max() <= 1e-7 * max(1.0, np.abs(num).max())
+    lt = O.attention_backward_live_tiles(q, k, v, dout, lay, bs, 0.6, **kw)
+    for a, b in zip((dq, dk, dv, ds), lt):
+        assert np.abs(a - b).max() <= 1e-12

@@ -602,3 +602,39 @@ def test_options_dense_and_live_tile_forms_agree():
     b_, lb = O.attention_live_tiles(q, k, v, lay, bs, 0.45, **kw)
     np.testing.assert_allclose(b_, a, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(lb, la, rtol=1e-12)
+
+
+# ------------------------------------------------ ragged sequence lengths
+
+@pytest.mark.parametrize("Sq,Sk,causal", [(37, 53, False), (64, 70, True), (17, 16, False),
+                                         (5, 29, True)])
+def test_ragged_lengths_match_sdpa(Sq, Sk, causal):
+    """Lengths that are not multiples of bs: the layout covers ceil(S/bs)
+    blocks and the last block is cut at the sequence end (Language AI
+    Handbook, create_block_sparse_mask).  Both oracle forms equal SDPA with a
+    mask built by index lookup on the cut sequences."""
+    import torch
+    bs, B, H, d = 8, 2, 3, 16
+    Mb, Nb = -(-Sq // bs), -(-Sk // bs)
+    rng = np.random.default_rng(Sq * 100 + Sk)
+    q = rng.standard_normal((B, H, Sq, d))
+    k = rng.standard_normal((B, H, Sk, d))
+    v = rng.standard_normal((B, H, Sk, d))
+    lay = (rng.random((H, Mb, Nb)) < 0.6).astype(np.int32)
+    lay[:, :, 0] = 1
+    scale = 0.3
+    m = np.stack([lay[h][np.arange(Sq)[:, None] // bs, np.arange(Sk)[None, :] // bs] != 0
+                  for h in range(H)])
+    if causal:
+        m &= np.arange(Sk)[None, None, :] <= np.arange(Sq)[None, :, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        attn_mask=torch.from_numpy(m)[None], scale=scale).numpy()
+    o1, l1 = O.attention_dense_masked(q, k, v, lay, bs, scale, causal=causal)
+    o2, l2 = O.attention_live_tiles(q, k, v, lay, bs, scale, causal=causal)
+    assert o1.shape == (B, H, Sq, d)
+    assert np.abs(o1 - ref).max() <= 1e-12 and np.abs(o2 - ref).max() <= 1e-12
+    assert np.abs(l1 - l2).max() <= 1e-12
+    # a layout that does not cover the lengths is rejected
+    with pytest.raises(ValueError):
+        O.attention_dense_masked(q, k, v, lay[:, :, :Nb - 1] if Nb > 1 else lay[:, :0], bs, scale)
