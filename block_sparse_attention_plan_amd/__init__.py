@@ -243,11 +243,24 @@ def bsa_plan_nnz(plan: Plan) -> int:
     return int(out.value)
 
 
+def _block_size(Sq: int, Sk: int, plan, bs: Optional[int]) -> int:
+    if bs is None:
+        if Sq % plan.Mb:
+            raise ValueError("Sq is not a multiple of the layout's block rows: pass bs")
+        bs = Sq // plan.Mb
+    bs = int(bs)
+    if bs <= 0 or -(-Sq // bs) != plan.Mb or -(-Sk // bs) != plan.Nb:
+        raise ValueError(f"bs={bs}: the layout's {plan.Mb} x {plan.Nb} blocks do not cover "
+                         f"Sq={Sq}, Sk={Sk}")
+    return bs
+
+
 def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
                 scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                 lse: Optional[torch.Tensor] = None, want_lse: bool = True, *,
                 attn_sink: Optional[torch.Tensor] = None, soft_cap: Optional[float] = None,
-                causal: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                causal: bool = False, bs: Optional[int] = None
+                ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Block-sparse attention forward.
 
     q: [B, H, Sq, d], k/v: [B, Hkv, Sk, d] with H % Hkv == 0 (query head h
@@ -256,7 +269,9 @@ def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
     lse [B, H, Sq] fp32 or None).  scale defaults to 1/sqrt(d).  attn_sink
     (fp32 [H]) adds exp(attn_sink[h]) to each softmax denominator; soft_cap
     caps the scaled scores to soft_cap * tanh(s / soft_cap); causal also masks
-    key tokens after the query token.
+    key tokens after the query token.  bs (default Sq / Mb) must be given when
+    a length is not a multiple of the block size: the plan's layout then
+    covers ceil(S / bs) blocks and the last block is cut at the sequence end.
     """
     for name, t in (("q", q), ("k", k), ("v", v)):
         _require_gpu(name, t)
@@ -276,9 +291,7 @@ def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
     if soft_cap is not None and not (math.isfinite(soft_cap) and soft_cap > 0):
         raise ValueError("soft_cap must be finite and > 0")
     Sk = int(k.shape[2])
-    if Sq % plan.Mb != 0:
-        raise ValueError("Sq must be a multiple of the layout's block rows")
-    bs = Sq // plan.Mb
+    bs = _block_size(Sq, Sk, plan, bs)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -373,7 +386,7 @@ def bsa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
                  soft_cap: Optional[float] = None, causal: bool = False,
                  dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
                  dv: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None):
+                 workspace: Optional[torch.Tensor] = None, bs: Optional[int] = None):
     """Gradients of bsa_forward for the upstream gradient dout.
 
     q, k, v, scale and the options must be those of the forward call that
@@ -392,9 +405,7 @@ def bsa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
         raise ValueError("out and dout must match q")
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Sq):
         raise ValueError("lse must be fp32 [B, H, Sq]")
-    if Sq % plan.Mb != 0:
-        raise ValueError("Sq must be a multiple of the layout's block rows")
-    bs = Sq // plan.Mb
+    bs = _block_size(Sq, Sk, plan, bs)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if attn_sink is not None:

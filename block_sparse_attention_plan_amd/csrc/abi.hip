@@ -25,6 +25,9 @@ int hip_fail(hipError_t e, const char *where) {
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Blocks covering S tokens: the last one is cut where S is not a multiple.
+int64_t blocks(int32_t S, int32_t bs) { return ((int64_t)S + bs - 1) / bs; }
+
 int check_plan(const bsa_plan_t *plan, bsa::PlanGeometry *g) {
   if (plan == nullptr) return fail(BSA_ERR_INVALID_ARG, "plan is NULL");
   if (plan->dev_buf == nullptr) return fail(BSA_ERR_INVALID_ARG, "plan has no buffer");
@@ -56,7 +59,7 @@ int check_plan_cols(const bsa_plan_cols_t *pc, bsa::PlanColsGeometry *g) {
 // validated and turned into kernel form.  `who` prefixes error messages.
 int make_options(const bsa_forward_opts_t *opts, int32_t H, float scale, bsa::FwdOptions *fo,
                  const char *who) {
-  *fo = bsa::FwdOptions{nullptr, 0.f, 0.f, 0, 1};
+  *fo = bsa::FwdOptions{nullptr, 0.f, 0.f, 0, 1, 0, 0};
   if (opts == nullptr) return BSA_OK;
   const int32_t hkv = opts->kv_heads == 0 ? H : opts->kv_heads;
   if (hkv < 1 || H % hkv != 0)
@@ -157,7 +160,7 @@ int bsa_forward_ex(const void *q, const void *k, const void *v, const bsa_plan_t
   if (st != BSA_OK) return st;
   if (B <= 0 || H <= 0 || Sq <= 0 || Sk <= 0 || bs <= 0 || d <= 0)
     return fail(BSA_ERR_INVALID_ARG, "bsa_forward: sizes must be positive");
-  if (H != plan->H || (int64_t)Sq != (int64_t)plan->Mb * bs || (int64_t)Sk != (int64_t)plan->Nb * bs)
+  if (H != plan->H || blocks(Sq, bs) != plan->Mb || blocks(Sk, bs) != plan->Nb)
     return fail(BSA_ERR_PLAN_MISMATCH,
                 "bsa_forward: H=%d Sq=%d Sk=%d bs=%d do not match plan H=%d Mb=%d Nb=%d", H, Sq,
                 Sk, bs, plan->H, plan->Mb, plan->Nb);
@@ -175,6 +178,8 @@ int bsa_forward_ex(const void *q, const void *k, const void *v, const bsa_plan_t
   bsa::FwdOptions fo;
   st = make_options(opts, H, scale, &fo, "bsa_forward");
   if (st != BSA_OK) return st;
+  fo.sq = Sq;
+  fo.sk = Sk;
   hipError_t e = bsa::launch_forward(
       q, k, v, at<int32_t>(plan->dev_buf, g.off_row_ptr), at<int32_t>(plan->dev_buf, g.off_col_idx),
       at<int32_t>(plan->dev_buf, g.off_row_order), B, plan->H, plan->Mb, plan->Nb, bs, d,
@@ -262,7 +267,7 @@ int bsa_backward(const void *q, const void *k, const void *v, const void *out, c
   if (st != BSA_OK) return st;
   if (B <= 0 || H <= 0 || Sq <= 0 || Sk <= 0 || bs <= 0 || d <= 0)
     return fail(BSA_ERR_INVALID_ARG, "bsa_backward: sizes must be positive");
-  if (H != plan->H || (int64_t)Sq != (int64_t)plan->Mb * bs || (int64_t)Sk != (int64_t)plan->Nb * bs)
+  if (H != plan->H || blocks(Sq, bs) != plan->Mb || blocks(Sk, bs) != plan->Nb)
     return fail(BSA_ERR_PLAN_MISMATCH,
                 "bsa_backward: H=%d Sq=%d Sk=%d bs=%d do not match plan H=%d Mb=%d Nb=%d", H, Sq,
                 Sk, bs, plan->H, plan->Mb, plan->Nb);
@@ -274,6 +279,8 @@ int bsa_backward(const void *q, const void *k, const void *v, const void *out, c
   bsa::FwdOptions fo;
   st = make_options(opts, H, scale, &fo, "bsa_backward");
   if (st != BSA_OK) return st;
+  fo.sq = Sq;
+  fo.sk = Sk;
   if (plan_cols->H != H || plan_cols->Mb != plan->Mb || plan_cols->Nb != plan->Nb ||
       plan_cols->Hkv != H / fo.kv_group)
     return fail(BSA_ERR_PLAN_MISMATCH,

@@ -54,14 +54,17 @@ template <int D> struct BSwz {
 };
 
 // Copy a contiguous BS x D bf16 tile into LDS with the swizzle; the NW waves
-// of the workgroup share its 1 KiB copy instructions.
+// of the workgroup share its 1 KiB copy instructions.  Only the first `bytes`
+// bytes exist (a block cut at the sequence end): the rest read as zeros (the
+// whole offset is per lane, where the buffer range check applies).
 template <int BS, int D, int NW>
-__device__ __forceinline__ void copy_tile(const __bf16 *src, __bf16 *dst, int wid, int lane) {
+__device__ __forceinline__ void copy_tile(const __bf16 *src, __bf16 *dst, int wid, int lane,
+                                          uint32_t bytes = BS * D * 2) {
   constexpr int CPR = D / 8;
   constexpr int NI = BS * D * 2 / 1024;
   constexpr int RPI = 64 / CPR;
   static_assert(NI % NW == 0, "copies must split evenly over the waves");
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, BS * D * 2);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, bytes);
 #pragma unroll
   for (int j = 0; j < NI / NW; ++j) {
     const int i = wid + NW * j;
@@ -206,20 +209,23 @@ bwd_dq_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   const int G = lane / 16, l16 = lane % 16;
 
   const int64_t bh = (int64_t)b * H + h;
-  const int64_t Sq = (int64_t)Mb * BS, Sk = (int64_t)Nb * BS;
+  const int64_t Sq = opt.sq, Sk = opt.sk;
   const int64_t bkv = (int64_t)b * (H / opt.kv_group) + h / opt.kv_group;
   const __bf16 *kh = k + bkv * Sk * D;
   const __bf16 *vh = v + bkv * Sk * D;
   const int qrow = 32 * wid + l32;            // query row inside the block
   const int64_t i_row = (int64_t)m * BS + qrow;
+  const bool q_ok = !MASK || i_row < Sq;     // rows past a cut last block
 
-  const float l2 = lse2[bh * Sq + i_row];
-  const float dd = Dv[bh * Sq + i_row];
+  const float l2 = q_ok ? lse2[bh * Sq + i_row] : __builtin_inff();
+  const float dd = q_ok ? Dv[bh * Sq + i_row] : 0.f;
   bf16x8 qf[QC], gf[QC];
 #pragma unroll
   for (int c = 0; c < QC; ++c) {
-    qf[c] = *reinterpret_cast<const bf16x8 *>(q + (bh * Sq + i_row) * D + 16 * c + 8 * h2);
-    gf[c] = *reinterpret_cast<const bf16x8 *>(dout + (bh * Sq + i_row) * D + 16 * c + 8 * h2);
+    qf[c] = q_ok ? *reinterpret_cast<const bf16x8 *>(q + (bh * Sq + i_row) * D + 16 * c + 8 * h2)
+                 : bf16x8{};
+    gf[c] = q_ok ? *reinterpret_cast<const bf16x8 *>(dout + (bh * Sq + i_row) * D + 16 * c + 8 * h2)
+                 : bf16x8{};
   }
   f32x16 acc[DT];
 #pragma unroll
@@ -235,8 +241,9 @@ bwd_dq_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     const int ncol = col_idx[t];
     if (MASK && opt.causal && ncol > m) continue;   // every key after every query
     __syncthreads();                                // previous tile fully read
-    copy_tile<BS, D, NW>(kh + (int64_t)ncol * TILE, Ks, wid, lane);
-    copy_tile<BS, D, NW>(vh + (int64_t)ncol * TILE, Vs, wid, lane);
+    const int kv = MASK ? (int)min((int64_t)BS, Sk - (int64_t)ncol * BS) : BS;  // keys that exist
+    copy_tile<BS, D, NW>(kh + (int64_t)ncol * TILE, Ks, wid, lane, (uint32_t)(kv * D * 2));
+    copy_tile<BS, D, NW>(vh + (int64_t)ncol * TILE, Vs, wid, lane, (uint32_t)(kv * D * 2));
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const bool diag = MASK && opt.causal && ncol == m;
@@ -254,6 +261,7 @@ bwd_dq_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
         const Weight wt = weight<MASK>(s[e], scale_log2, l2, opt);
         float p = wt.p;
         if (diag && 32 * jt + 8 * (e / 4) + 4 * h2 + (e % 4) > qrow) p = 0.f;
+        if (MASK && 32 * jt + 8 * (e / 4) + 4 * h2 + (e % 4) >= kv) p = 0.f;
         s[e] = p * (dp[e] - dd) * wt.slope;
       }
 #pragma unroll
@@ -267,6 +275,7 @@ bwd_dq_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
       }
     }
   }
+  if (!q_ok) return;
   __bf16 *dqh = dq + (bh * Sq + i_row) * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -313,16 +322,19 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   const int h2 = lane / 32, l32 = lane % 32;
   const int G = lane / 16, l16 = lane % 16;
 
-  const int64_t Sq = (int64_t)Mb * BS, Sk = (int64_t)Nb * BS;
+  const int64_t Sq = opt.sq, Sk = opt.sk;
   const int64_t bkv = (int64_t)b * Hkv + kvh;
   const int krow = 32 * wid + l32;            // key row inside the block
   const int64_t j_row = (int64_t)n * BS + krow;
+  const bool k_ok = !MASK || j_row < Sk;     // keys past a cut last block
 
   bf16x8 kf[QC], vf[QC];
 #pragma unroll
   for (int c = 0; c < QC; ++c) {
-    kf[c] = *reinterpret_cast<const bf16x8 *>(k + (bkv * Sk + j_row) * D + 16 * c + 8 * h2);
-    vf[c] = *reinterpret_cast<const bf16x8 *>(v + (bkv * Sk + j_row) * D + 16 * c + 8 * h2);
+    kf[c] = k_ok ? *reinterpret_cast<const bf16x8 *>(k + (bkv * Sk + j_row) * D + 16 * c + 8 * h2)
+                 : bf16x8{};
+    vf[c] = k_ok ? *reinterpret_cast<const bf16x8 *>(v + (bkv * Sk + j_row) * D + 16 * c + 8 * h2)
+                 : bf16x8{};
   }
   f32x16 ak[DT], av[DT];
 #pragma unroll
@@ -346,11 +358,14 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
       const int m = row_idx[t];
       if (MASK && opt.causal && m < n) continue;    // every key after every query
       __syncthreads();                              // previous tile fully read
-      copy_tile<BS, D, NW>(q + (bh * Sq + (int64_t)m * BS) * D, Qs, wid, lane);
-      copy_tile<BS, D, NW>(dout + (bh * Sq + (int64_t)m * BS) * D, Gs, wid, lane);
+      const int qv = MASK ? (int)min((int64_t)BS, Sq - (int64_t)m * BS) : BS;  // rows that exist
+      copy_tile<BS, D, NW>(q + (bh * Sq + (int64_t)m * BS) * D, Qs, wid, lane, (uint32_t)(qv * D * 2));
+      copy_tile<BS, D, NW>(dout + (bh * Sq + (int64_t)m * BS) * D, Gs, wid, lane,
+                           (uint32_t)(qv * D * 2));
       if (tid < BS) {
-        Ls[tid] = lse2[bh * Sq + (int64_t)m * BS + tid];
-        Ds[tid] = Dv[bh * Sq + (int64_t)m * BS + tid];
+        // rows past a cut last block: weight exp2(s - inf) = 0
+        Ls[tid] = tid < qv ? lse2[bh * Sq + (int64_t)m * BS + tid] : __builtin_inff();
+        Ds[tid] = tid < qv ? Dv[bh * Sq + (int64_t)m * BS + tid] : 0.f;
       }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -379,6 +394,7 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
             const Weight wt = weight<MASK>(s[e], scale_log2, l4[i], opt);
             float p = wt.p;
             if (diag && krow > 32 * jq + 8 * a + 4 * h2 + i) p = 0.f;
+            if (!k_ok) p = 0.f;
             s[e] = p;
             if constexpr (MASK) w[e] = p * wt.slope;
           }
@@ -429,6 +445,7 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
       }
     }
   }
+  if (!k_ok) return;
   __bf16 *dkr = dk + (bkv * Sk + j_row) * D;
   __bf16 *dvr = dv + (bkv * Sk + j_row) * D;
 #pragma unroll
@@ -471,7 +488,7 @@ hipError_t launch_grads(const BwdArgs &a, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_pre(const BwdArgs &a, hipStream_t stream) {
-  const int64_t rows = (int64_t)a.B * a.H * a.Mb * a.bs;
+  const int64_t rows = (int64_t)a.B * a.H * a.opt.sq;
   const int64_t rpb = 256 / (D / 8);
   int64_t grid = (rows + rpb - 1) / rpb;
   if (grid > 65536) grid = 65536;
@@ -493,7 +510,8 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
                : a.d == 64 ? launch_pre<64>(a, stream)
                            : launch_pre<128>(a, stream);
   if (e != hipSuccess) return e;
-  const bool mask = a.opt.cap_k != 0.f || a.opt.causal != 0;
+  const bool mask = a.opt.cap_k != 0.f || a.opt.causal != 0 || a.opt.sq % a.bs != 0 ||
+                    a.opt.sk % a.bs != 0;
 #define BSA_BWD_CASE(BS_, D_)                                                                  \
   if (a.bs == BS_ && a.d == D_) e = mask ? launch_grads<BS_, D_, true>(a, stream)             \
                                          : launch_grads<BS_, D_, false>(a, stream);
@@ -504,7 +522,7 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   if (a.opt.sink != nullptr && a.dsink != nullptr) {
     hipLaunchKernelGGL(bwd_dsink_kernel, dim3(a.H), dim3(256), 0, stream, (const float *)a.lse2,
-                       (const float *)a.Dv, a.opt.sink, a.B, a.H, (int64_t)a.Mb * a.bs, a.dsink);
+                       (const float *)a.Dv, a.opt.sink, a.B, a.H, (int64_t)a.opt.sq, a.dsink);
     e = hipGetLastError();
   }
   return e;

@@ -27,6 +27,8 @@ struct FwdOptions {
   float cap_b;        // cap/scale
   int32_t causal;     // nonzero: key token j > query token i is masked too
   int32_t kv_group;   // query heads per K/V head (1 without grouping)
+  int32_t sq, sk;     // sequence lengths; the last block is cut where they are
+                      // not multiples of the block size
 };
 
 // Returns hipErrorInvalidValue when no kernel instance matches (bs, d, f32).

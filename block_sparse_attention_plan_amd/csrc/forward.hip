@@ -126,7 +126,7 @@ bsa_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__rest
   const int li = lane % 16;  // query column owned by this lane
 
   const int64_t bh = (int64_t)b * H + h;
-  const int64_t Sq = (int64_t)Mb * BS, Sk = (int64_t)Nb * BS;
+  const int64_t Sq = opt.sq, Sk = opt.sk;
   const T *qh = q + bh * Sq * D;
   const int64_t bkv = (int64_t)b * (H / opt.kv_group) + h / opt.kv_group;  // K/V head
   const T *kh = k + bkv * Sk * D;
@@ -134,8 +134,10 @@ bsa_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__rest
   T *oh = out + bh * Sq * D;
   float *lh = lse ? lse + bh * Sq : nullptr;
   const int64_t i_row = (int64_t)m * BS + 16 * wid + li;  // this lane's query row
+  const bool q_ok = !MASK || i_row < Sq;                  // rows past a cut last block
 
   if (beg == end) {  // no live tile: zero output, lse = -inf (the sink logit with a sink)
+    if (!q_ok) return;
     for (int dt = 0; dt < DT; ++dt) Io<T>::store_zero4(oh + i_row * D + 16 * dt + 4 * G);
     if (lh && G == 0) lh[i_row] = opt.sink ? opt.sink[h] : -__builtin_inff();
     return;
@@ -144,19 +146,21 @@ bsa_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__rest
   // Q^T fragments (B operand of S^T = K Q^T): column = query row, k = d.
   bf16x8 qf[QC];
 #pragma unroll
-  for (int c = 0; c < QC; ++c) qf[c] = Io<T>::load8(qh + i_row * D + 32 * c + 8 * G);
+  for (int c = 0; c < QC; ++c) qf[c] = q_ok ? Io<T>::load8(qh + i_row * D + 32 * c + 8 * G) : bf16x8{};
 
   // Register prefetch of one K/V tile.
   bf16x8 kr[CPT], vr[CPT];
   auto load_tile = [&](int n) {
     const T *kt = kh + (int64_t)n * BS * D;
     const T *vt = vh + (int64_t)n * BS * D;
+    const int kval = MASK ? (int)min((int64_t)BS, Sk - (int64_t)n * BS) : BS;  // rows that exist
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int qid = c * NT + tid;
       const int row = qid / (D / 8), col = (qid % (D / 8)) * 8;
-      kr[c] = Io<T>::load8(kt + row * D + col);
-      vr[c] = Io<T>::load8(vt + row * D + col);
+      const bool ok = !MASK || row < kval;
+      kr[c] = ok ? Io<T>::load8(kt + row * D + col) : bf16x8{};
+      vr[c] = ok ? Io<T>::load8(vt + row * D + col) : bf16x8{};
     }
   };
   auto store_tile = [&]() {
@@ -209,6 +213,14 @@ bsa_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__rest
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (16 * jt + 4 * G + e > dq) s[jt][e] = -__builtin_inff();
+    }
+    if (MASK && (int64_t)(col_idx[t] + 1) * BS > Sk) {  // keys past a cut last block
+      const int kv = (int)(Sk - (int64_t)col_idx[t] * BS);
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (16 * jt + 4 * G + e >= kv) s[jt][e] = -__builtin_inff();
     }
     // Online softmax over this tile's keys for query column li.
     float mx = s[0][0];
@@ -265,6 +277,7 @@ bsa_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__rest
   float o_scale = 1.f;
   if (opt.sink) o_scale = fold_sink(m_run, l_tot, opt.sink[h] * kLog2e);
   const float inv = l_tot > 0.f ? o_scale / l_tot : 0.f;
+  if (!q_ok) return;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) Io<T>::store4(oh + i_row * D + 16 * dt + 4 * G, acc[dt] * inv);
   if (lh && G == 0) lh[i_row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
@@ -333,7 +346,7 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
   const int l16 = lane % 16;
 
   const int64_t bh = (int64_t)b * H + h;
-  const int64_t Sq = (int64_t)Mb * BS, Sk = (int64_t)Nb * BS;
+  const int64_t Sq = opt.sq, Sk = opt.sk;
   const T *qh = q + bh * Sq * D;
   const int64_t bkv = (int64_t)b * (H / opt.kv_group) + h / opt.kv_group;  // K/V head
   const T *kh = k + bkv * Sk * D;
@@ -341,9 +354,10 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
   T *oh = out + bh * Sq * D;
   float *lh = lse ? lse + bh * Sq : nullptr;
   const int64_t i_row = (int64_t)m * BS + 32 * rg + l32;
+  const bool q_ok = !MASK || i_row < Sq;  // rows past a cut last block
 
   if (beg == end) {
-    if (ks == 0) {
+    if (ks == 0 && q_ok) {
       for (int dt = 0; dt < DT; ++dt)
         for (int a = 0; a < 4; ++a) Io<T>::store_zero4(oh + i_row * D + 32 * dt + 8 * a + 4 * h2);
       if (lh && h2 == 0) lh[i_row] = opt.sink ? opt.sink[h] : -__builtin_inff();
@@ -353,24 +367,30 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
 
   bf16x8 qf[QC];
 #pragma unroll
-  for (int c = 0; c < QC; ++c) qf[c] = Io<T>::load8(qh + i_row * D + 16 * c + 8 * h2);
+  for (int c = 0; c < QC; ++c) qf[c] = q_ok ? Io<T>::load8(qh + i_row * D + 16 * c + 8 * h2) : bf16x8{};
 
   // Register staging of one K tile and one V tile (16-byte pieces).
   bf16x8 kr[CPT], vr[CPT];
+  // (MASK instances: rows past a cut last block load zeros)
+  auto kval_of = [&](int n) { return MASK ? (int)min((int64_t)BS, Sk - (int64_t)n * BS) : BS; };
   auto load_k = [&](int n) {
     const T *src = kh + (int64_t)n * BS * D;
+    const int kval = kval_of(n);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int qid = c * NT + tid;
-      kr[c] = Io<T>::load8(src + (qid / (D / 8)) * D + (qid % (D / 8)) * 8);
+      kr[c] = (!MASK || qid / (D / 8) < kval)
+                  ? Io<T>::load8(src + (qid / (D / 8)) * D + (qid % (D / 8)) * 8) : bf16x8{};
     }
   };
   auto load_v = [&](int n) {
     const T *src = vh + (int64_t)n * BS * D;
+    const int kval = kval_of(n);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int qid = c * NT + tid;
-      vr[c] = Io<T>::load8(src + (qid / (D / 8)) * D + (qid % (D / 8)) * 8);
+      vr[c] = (!MASK || qid / (D / 8) < kval)
+                  ? Io<T>::load8(src + (qid / (D / 8)) * D + (qid % (D / 8)) * 8) : bf16x8{};
     }
   };
   auto store_k = [&](int buf) {
@@ -427,6 +447,14 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
 #pragma unroll
         for (int e = 0; e < 16; ++e)
           if (32 * jt + 8 * (e / 4) + (e % 4) > dq) s[jt][e] = -__builtin_inff();
+    }
+    if ((int64_t)(ncol + 1) * BS > Sk) {  // keys past a cut last block
+      const int kv = (int)(Sk - (int64_t)ncol * BS) - key0 - 4 * h2;
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (32 * jt + 8 * (e / 4) + (e % 4) >= kv) s[jt][e] = -__builtin_inff();
     }
   };
 
@@ -552,6 +580,7 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
   float o_scale = 1.f;
   if (opt.sink) o_scale = fold_sink(m_run, l_tot, opt.sink[h] * kLog2e);
   const float inv = l_tot > 0.f ? o_scale / l_tot : 0.f;
+  if (!q_ok) return;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -633,7 +662,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   const int l16 = lane % 16;
 
   const int64_t bh = (int64_t)b * H + h;
-  const int64_t Sq = (int64_t)Mb * BS, Sk = (int64_t)Nb * BS;
+  const int64_t Sq = opt.sq, Sk = opt.sk;
   const __bf16 *qh = q + bh * Sq * D;
   const int64_t bkv = (int64_t)b * (H / opt.kv_group) + h / opt.kv_group;  // K/V head
   const __bf16 *kh = k + bkv * Sk * D;
@@ -641,9 +670,10 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   __bf16 *oh = out + bh * Sq * D;
   float *lh = lse ? lse + bh * Sq : nullptr;
   const int64_t i_row = (int64_t)m * BS + 32 * rg + l32;
+  const bool q_ok = !MASK || i_row < Sq;  // rows past a cut last block
 
   if (beg == end) {
-    if (ks == 0) {
+    if (ks == 0 && q_ok) {
       for (int dt = 0; dt < DT; ++dt)
         for (int a = 0; a < 4; ++a) Io<__bf16>::store_zero4(oh + i_row * D + 32 * dt + 8 * a + 4 * h2);
       if (lh && h2 == 0) lh[i_row] = opt.sink ? opt.sink[h] : -__builtin_inff();
@@ -653,7 +683,8 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
 
   bf16x8 qf[QC];
 #pragma unroll
-  for (int c = 0; c < QC; ++c) qf[c] = Io<__bf16>::load8(qh + i_row * D + 16 * c + 8 * h2);
+  for (int c = 0; c < QC; ++c)
+    qf[c] = q_ok ? Io<__bf16>::load8(qh + i_row * D + 16 * c + 8 * h2) : bf16x8{};
 
   // Load instruction j of this wave covers tile rows RPI*(wid + NW*j) ..;
   // lane l writes physical chunk l % CPR of row RPI*i + l / CPR.
@@ -661,16 +692,26 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   const int row0 = RPI * wid + lrow;  // row % CPR and f(row) are the same for every j
   const int k_src = lrow * D + (lph ^ (row0 & (CPR - 1))) * 8;
   const int v_src = lrow * D + (lph ^ VSwz<D>::f(row0)) * 8;
-  auto dma = [&](const __bf16 *src_tile, const int src_off, __bf16 *dst_tile) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src_tile, TILE * 2);
+  // (MASK instances: a cut last tile's resource ends at the sequence end, so
+  // the rows past it read as zeros.  The range check of a raw buffer load
+  // covers the per-lane offset, not the scalar one, so those instances carry
+  // the row offset per lane.)
+  auto dma = [&](const __bf16 *src_tile, const int src_off, __bf16 *dst_tile, uint32_t bytes) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src_tile, bytes);
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
       const int i = wid + NW * j;
-      copy16_to_lds(rs, dst_tile + i * 512, (uint32_t)(src_off * 2), (uint32_t)(i * RPI * D * 2));
+      if constexpr (MASK)
+        copy16_to_lds(rs, dst_tile + i * 512, (uint32_t)(src_off * 2 + i * RPI * D * 2), 0u);
+      else
+        copy16_to_lds(rs, dst_tile + i * 512, (uint32_t)(src_off * 2), (uint32_t)(i * RPI * D * 2));
     }
   };
-  auto load_k = [&](int n, __bf16 *dst) { dma(kh + (int64_t)n * TILE, k_src, dst); };
-  auto load_v = [&](int n, __bf16 *dst) { dma(vh + (int64_t)n * TILE, v_src, dst); };
+  auto tile_bytes = [&](int n) -> uint32_t {
+    return MASK ? (uint32_t)(min((int64_t)BS, Sk - (int64_t)n * BS) * D * 2) : (uint32_t)(TILE * 2);
+  };
+  auto load_k = [&](int n, __bf16 *dst) { dma(kh + (int64_t)n * TILE, k_src, dst, tile_bytes(n)); };
+  auto load_v = [&](int n, __bf16 *dst) { dma(vh + (int64_t)n * TILE, v_src, dst, tile_bytes(n)); };
 
   // Per-lane element offsets of the K operand reads (one per k chunk).
   const int key0 = ks * KW;
@@ -713,6 +754,14 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
 #pragma unroll
         for (int e = 0; e < 16; ++e)
           if (32 * jt + 8 * (e / 4) + (e % 4) > dq) s[jt][e] = -__builtin_inff();
+    }
+    if ((int64_t)(ncol + 1) * BS > Sk) {  // keys past a cut last block
+      const int kv = (int)(Sk - (int64_t)ncol * BS) - key0 - 4 * h2;
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (32 * jt + 8 * (e / 4) + (e % 4) >= kv) s[jt][e] = -__builtin_inff();
     }
   };
 
@@ -911,6 +960,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   float o_scale = 1.f;
   if (opt.sink) o_scale = fold_sink(m_run, l_tot, opt.sink[h] * kLog2e);
   const float inv = l_tot > 0.f ? o_scale / l_tot : 0.f;
+  if (!q_ok) return;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -953,9 +1003,9 @@ hipError_t dispatch(int32_t bs, int32_t d, const void *q, const void *k, const v
                     const int32_t *rp, const int32_t *ci, const int32_t *ro, int32_t B, int32_t H,
                     int32_t Mb, int32_t Nb, float scale, const FwdOptions &opt, void *out,
                     float *lse, hipStream_t s) {
-  // Score-changing options (cap, causal) select their own kernel instances,
-  // so the plain forward keeps the code it has without them.
-  const bool mask = opt.cap_k != 0.f || opt.causal != 0;
+  // Score-changing options (cap, causal) and cut last blocks select their own
+  // kernel instances, so the plain forward keeps the code it has without them.
+  const bool mask = opt.cap_k != 0.f || opt.causal != 0 || opt.sq % bs != 0 || opt.sk % bs != 0;
 #define BSA_CASE(BS_, D_)                                                                   \
   if (bs == BS_ && d == D_)                                                                 \
     return mask ? launch_one<BS_, D_, T, true>(q, k, v, rp, ci, ro, B, H, Mb, Nb, scale, opt, \

@@ -114,15 +114,15 @@ def make_bsa(name: str, B: int, H: int, S: int, bs: int, d: int, dtype: str, lay
     N(sink_mean, 1) is drawn last, so the other draws do not depend on it."""
     Sk = S if Sk is None else Sk
     Hkv = H if Hkv is None else Hkv
-    if S % bs or Sk % bs:
-        raise ValueError("sequence lengths must be multiples of the block size")
+    if (S % bs or Sk % bs) and layout not in ("given", "random"):
+        raise ValueError("the named layout families need lengths that are multiples of bs")
     if Hkv < 1 or H % Hkv:
         raise ValueError("Hkv must divide H")
     rng = np.random.default_rng(seed)
     q = _tensor(_normal(rng, (B, H, S, d), std), dtype)
     k = _tensor(_normal(rng, (B, Hkv, Sk, d), std), dtype)
     v = _tensor(_normal(rng, (B, Hkv, Sk, d), std), dtype)
-    mb, nb = S // bs, Sk // bs
+    mb, nb = -(-S // bs), -(-Sk // bs)     # the last block may be cut
     if layout == "band":
         if mb != nb:
             raise ValueError("band layout needs a square block grid")

@@ -115,8 +115,11 @@ int bsa_plan_nnz(const bsa_plan_t *plan, int64_t *nnz_host, void *stream);
  *   q     device [B, H, Sq, d] of dtype
  *   k, v  device [B, H, Sk, d] of dtype
  *   plan  host pointer to a plan built for this layout; H must equal plan->H,
- *         Sq must equal plan->Mb * bs and Sk plan->Nb * bs, otherwise the call
- *         returns BSA_ERR_PLAN_MISMATCH
+ *         ceil(Sq / bs) must equal plan->Mb and ceil(Sk / bs) plan->Nb,
+ *         otherwise the call returns BSA_ERR_PLAN_MISMATCH.  Lengths that are
+ *         not multiples of bs cut the last block row / column at the sequence
+ *         end (Language AI Handbook, create_block_sparse_mask): keys past Sk
+ *         take no weight and rows past Sq are neither read nor written
  *   bs    block size: 16, 32, 64 or 128;   d: 32, 64 or 128
  *   scale finite and > 0 (the Python binding defaults it to 1/sqrt(d))
  *   out   device [B, H, Sq, d] of dtype, written
