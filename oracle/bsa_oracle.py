@@ -47,6 +47,10 @@ Readings where the pages are silent (each is listed in the design notes):
   so a row with no live key then has out = 0 and lse = sink_h.
 * With kv_heads = H / g, query head h reads key/value head h // g (groups of
   g consecutive query heads share one K/V head).
+* Segment ids (the ejkernel operation's q_segment_ids [batch, seq_len] and
+  kv_segment_ids [batch, kv_len], "to handle multiple sequences"): query
+  token i may attend key token j only when their ids are equal, on top of
+  every other mask; they come in pairs.
 * Sequence lengths need not be multiples of the block size: as in the
   Language AI Handbook's create_block_sparse_mask (ceil(len / bs) blocks, the
   last block ending at the sequence end), a layout [H, ceil(Sq/bs),
@@ -181,12 +185,26 @@ def _kv_head(H: int, Hkv: int):
     return lambda h: h // g
 
 
+def _segments(q_segment_ids, kv_segment_ids, B, Sq, Sk):
+    """Per-batch [B, Sq, Sk] mask of equal segment ids, or None."""
+    if q_segment_ids is None and kv_segment_ids is None:
+        return None
+    if q_segment_ids is None or kv_segment_ids is None:
+        raise ValueError("segment ids come in pairs (queries and keys)")
+    qs = np.asarray(q_segment_ids)
+    ks = np.asarray(kv_segment_ids)
+    if qs.shape != (B, Sq) or ks.shape != (B, Sk):
+        raise ValueError("segment ids must be [B, Sq] and [B, Sk]")
+    return qs[:, :, None] == ks[:, None, :]
+
+
 def _cap(s: np.ndarray, soft_cap: Optional[float]) -> np.ndarray:
     return s if not soft_cap else soft_cap * np.tanh(s / soft_cap)
 
 
 def attention_dense_masked(q, k, v, layout, bs: int, scale: float, *, sink=None,
-                           soft_cap: Optional[float] = None, causal: bool = False
+                           soft_cap: Optional[float] = None, causal: bool = False,
+                           q_segment_ids=None, kv_segment_ids=None
                            ) -> Tuple[np.ndarray, np.ndarray]:
     """Dense definition with non-live tiles masked to -inf.
 
@@ -214,7 +232,9 @@ def attention_dense_masked(q, k, v, layout, bs: int, scale: float, *, sink=None,
     if causal:
         mask = mask & (np.arange(Sk)[None, None, :] <= np.arange(Sq)[None, :, None])
     s = _cap(scale * np.matmul(q, np.swapaxes(k, -1, -2)), soft_cap)
-    s = np.where(mask[None], s, -np.inf)
+    seg = _segments(q_segment_ids, kv_segment_ids, B, Sq, Sk)
+    full = mask[None] if seg is None else mask[None] & seg[:, None]
+    s = np.where(full, s, -np.inf)
     row_max = s.max(axis=-1, keepdims=True)
     sk = None if sink is None else _as64(sink)[None, :, None, None]
     if sk is not None:
@@ -235,7 +255,8 @@ def attention_dense_masked(q, k, v, layout, bs: int, scale: float, *, sink=None,
 
 def attention_live_tiles(q, k, v, layout, bs: int, scale: float,
                          row_blocks: Optional[Iterable[Tuple[int, int, int]]] = None, *,
-                         sink=None, soft_cap: Optional[float] = None, causal: bool = False
+                         sink=None, soft_cap: Optional[float] = None, causal: bool = False,
+                         q_segment_ids=None, kv_segment_ids=None
                          ) -> Tuple[np.ndarray, np.ndarray]:
     """Same definition evaluated over the live tiles of each row only.
 
@@ -256,6 +277,7 @@ def attention_live_tiles(q, k, v, layout, bs: int, scale: float,
     if lay.shape[0] != H or lay.shape[1] != Mb or lay.shape[2] != _nblocks(Sk, bs):
         raise ValueError("layout does not match q/k shapes")
     sk = None if sink is None else _as64(sink)
+    seg = _segments(q_segment_ids, kv_segment_ids, B, Sq, Sk)
     out = np.full((B, H, Sq, v.shape[3]), np.nan)
     lse = np.full((B, H, Sq), np.nan)
     if row_blocks is None:
@@ -271,6 +293,8 @@ def attention_live_tiles(q, k, v, layout, bs: int, scale: float,
         if causal:
             qpos = m * bs + offs[:nr]
             s = np.where(tok[None, :] <= qpos[:, None], s, -np.inf)
+        if seg is not None:
+            s = np.where(seg[b][rows][:, tok], s, -np.inf)
         mx = s.max(axis=1) if tok.size else np.full(nr, -np.inf)
         if sk is not None:
             mx = np.maximum(mx, sk[h])
@@ -370,7 +394,8 @@ def _cap_slope(s: np.ndarray, soft_cap: Optional[float]) -> np.ndarray:
 
 
 def attention_backward_dense(q, k, v, dout, layout, bs: int, scale: float, *, sink=None,
-                             soft_cap: Optional[float] = None, causal: bool = False):
+                             soft_cap: Optional[float] = None, causal: bool = False,
+                             q_segment_ids=None, kv_segment_ids=None):
     """Gradients of attention_dense_masked's ``out`` for the upstream gradient
     ``dout`` [B, H, Sq, d]: returns dq [B, H, Sq, d], dk and dv [B, Hkv, Sk, d],
     and dsink [H] (None without a sink).  Dense S x S form of the formulas
@@ -386,13 +411,16 @@ def attention_backward_dense(q, k, v, dout, layout, bs: int, scale: float, *, si
         raise ValueError("layout does not match q/k shapes")
     if causal:
         mask = mask & (np.arange(Sk)[None, None, :] <= np.arange(Sq)[None, :, None])
+    seg = _segments(q_segment_ids, kv_segment_ids, B, Sq, Sk)
+    mask = mask[None] if seg is None else mask[None] & seg[:, None]    # [B or 1, H, Sq, Sk]
     s = scale * np.matmul(q, np.swapaxes(kx, -1, -2))        # scaled, uncapped
     out, lse = attention_dense_masked(q, k, v, layout, bs, scale, sink=sink,
-                                      soft_cap=soft_cap, causal=causal)
+                                      soft_cap=soft_cap, causal=causal,
+                                      q_segment_ids=q_segment_ids, kv_segment_ids=kv_segment_ids)
     live_row = np.isfinite(lse)[..., None]
-    c = np.where(mask[None], _cap(s, soft_cap), -np.inf)
+    c = np.where(mask, _cap(s, soft_cap), -np.inf)
     with np.errstate(invalid="ignore"):
-        p = np.where(live_row & mask[None], np.exp(c - np.where(live_row, lse[..., None], 0.0)), 0.0)
+        p = np.where(live_row & mask, np.exp(c - np.where(live_row, lse[..., None], 0.0)), 0.0)
     dv_x = np.matmul(np.swapaxes(p, -1, -2), dout)           # [B, H, Sk, d]
     dp = np.matmul(dout, np.swapaxes(vx, -1, -2))            # [B, H, Sq, Sk]
     D = (dout * out).sum(axis=-1, keepdims=True)             # [B, H, Sq, 1]
@@ -415,7 +443,8 @@ def attention_backward_dense(q, k, v, dout, layout, bs: int, scale: float, *, si
 
 def attention_backward_live_tiles(q, k, v, dout, layout, bs: int, scale: float, *,
                                   row_blocks=None, col_blocks=None, sink=None,
-                                  soft_cap: Optional[float] = None, causal: bool = False):
+                                  soft_cap: Optional[float] = None, causal: bool = False,
+                                  q_segment_ids=None, kv_segment_ids=None):
     """The same gradients over live tiles only, for sampled blocks.
 
     ``row_blocks`` lists (b, h, m) query blocks whose dq rows are computed;
@@ -445,7 +474,9 @@ def attention_backward_live_tiles(q, k, v, dout, layout, bs: int, scale: float, 
             need.update((b, h, int(m)) for m in np.flatnonzero(lay[h, :, n]))
     need = sorted(need)
     out, lse = attention_live_tiles(q, k, v, layout, bs, scale, row_blocks=need, sink=sink,
-                                    soft_cap=soft_cap, causal=causal)
+                                    soft_cap=soft_cap, causal=causal,
+                                    q_segment_ids=q_segment_ids, kv_segment_ids=kv_segment_ids)
+    seg = _segments(q_segment_ids, kv_segment_ids, B, Sq, Sk)
     D = (dout * out).sum(axis=-1)                            # NaN where not computed
 
     def rows_of(m):
@@ -464,6 +495,8 @@ def attention_backward_live_tiles(q, k, v, dout, layout, bs: int, scale: float, 
             qpos = np.arange(rows.start, rows.stop)
             kpos = np.arange(keys.start, keys.stop)
             c = np.where(kpos[None, :] <= qpos[:, None], c, -np.inf)
+        if seg is not None:
+            c = np.where(seg[b][rows, keys], c, -np.inf)
         lr = lse[b, h, rows][:, None]
         live = np.isfinite(lr)
         with np.errstate(invalid="ignore"):

@@ -212,3 +212,24 @@ def test_backward_ragged_matches_finite_differences(Sq, Sk):
     lt = O.attention_backward_live_tiles(q, k, v, dout, lay, bs, 0.6, **kw)
     for a, b in zip((dq, dk, dv, ds), lt):
         assert np.abs(a - b).max() <= 1e-12
+
+
+def test_backward_segments_match_finite_differences():
+    rng = np.random.default_rng(31)
+    B, H, bs, Sq, Sk, d = 2, 2, 2, 5, 6, 3
+    q = rng.standard_normal((B, H, Sq, d))
+    k = rng.standard_normal((B, 1, Sk, d))
+    v = rng.standard_normal((B, 1, Sk, d))
+    dout = rng.standard_normal((B, H, Sq, d))
+    lay = (rng.random((H, 3, 3)) < 0.8).astype(np.int32)
+    qs = np.array([[0, 0, 1, 1, 1], [0, 1, 1, 2, 2]])
+    ks = np.array([[0, 0, 0, 1, 1, 1], [0, 1, 1, 1, 2, 2]])
+    kw = dict(causal=True, sink=rng.standard_normal(H), q_segment_ids=qs, kv_segment_ids=ks)
+    dq, dk, dv, ds = O.attention_backward_dense(q, k, v, dout, lay, bs, 0.6, **kw)
+    f = lambda: _loss(q, k, v, dout, lay, bs, 0.6, **kw)  # noqa: E731
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = _fd(f, x)
+        assert np.abs(num - g).max() <= 1e-7 * max(1.0, np.abs(num).max())
+    lt = O.attention_backward_live_tiles(q, k, v, dout, lay, bs, 0.6, **kw)
+    for a, b in zip((dq, dk, dv, ds), lt):
+        assert np.abs(a - b).max() <= 1e-12

@@ -638,3 +638,57 @@ def test_ragged_lengths_match_sdpa(Sq, Sk, causal):
     # a layout that does not cover the lengths is rejected
     with pytest.raises(ValueError):
         O.attention_dense_masked(q, k, v, lay[:, :, :Nb - 1] if Nb > 1 else lay[:, :0], bs, scale)
+
+
+# ------------------------------------------------------------- segment ids
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_segments_equal_separate_sequences(causal):
+    """Packed sequences: with a full layout and segment ids, every segment's
+    output equals attention over that segment alone (torch SDPA, fp64), and
+    the live-tile form agrees."""
+    import torch
+    bs, H, d = 8, 2, 16
+    lens = [[13, 20, 7], [25, 15]]          # two batch items, 40 tokens each
+    S = 40
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((2, H, S, d))
+    k = rng.standard_normal((2, H, S, d))
+    v = rng.standard_normal((2, H, S, d))
+    seg = np.zeros((2, S), np.int32)
+    for b, ls in enumerate(lens):
+        seg[b] = np.repeat(np.arange(len(ls)), ls)
+    nb = -(-S // bs)
+    lay = np.ones((H, nb, nb), np.int32)
+    out, lse = O.attention_dense_masked(q, k, v, lay, bs, 0.25, causal=causal,
+                                        q_segment_ids=seg, kv_segment_ids=seg)
+    o2, l2 = O.attention_live_tiles(q, k, v, lay, bs, 0.25, causal=causal,
+                                    q_segment_ids=seg, kv_segment_ids=seg)
+    assert np.abs(out - o2).max() <= 1e-12 and np.abs(lse - l2).max() <= 1e-12
+    for b, ls in enumerate(lens):
+        start = 0
+        for L in ls:
+            sl = slice(start, start + L)
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q[b:b + 1, :, sl]), torch.from_numpy(k[b:b + 1, :, sl]),
+                torch.from_numpy(v[b:b + 1, :, sl]), scale=0.25, is_causal=causal).numpy()
+            assert np.abs(out[b:b + 1, :, sl] - ref).max() <= 1e-12
+            start += L
+
+
+def test_segments_with_every_option_live_tiles_agree():
+    rng = np.random.default_rng(22)
+    B, H, Hkv, bs, Sq, Sk, d = 2, 4, 2, 4, 21, 27, 8
+    q = rng.standard_normal((B, H, Sq, d))
+    k = rng.standard_normal((B, Hkv, Sk, d))
+    v = rng.standard_normal((B, Hkv, Sk, d))
+    qs = np.sort(rng.integers(0, 3, (B, Sq)), axis=1)
+    ks = np.sort(rng.integers(0, 3, (B, Sk)), axis=1)
+    lay = (rng.random((H, -(-Sq // bs), -(-Sk // bs))) < 0.6).astype(np.int32)
+    kw = dict(sink=rng.standard_normal(H), soft_cap=1.5, causal=True, q_segment_ids=qs,
+              kv_segment_ids=ks)
+    o1, l1 = O.attention_dense_masked(q, k, v, lay, bs, 0.4, **kw)
+    o2, l2 = O.attention_live_tiles(q, k, v, lay, bs, 0.4, **kw)
+    assert np.abs(o1 - o2).max() <= 1e-12 and np.abs(l1 - l2).max() <= 1e-12
+    with pytest.raises(ValueError):
+        O.attention_dense_masked(q, k, v, lay, bs, 0.4, q_segment_ids=qs)
