@@ -154,7 +154,21 @@ class _FwdOptsT(ctypes.Structure):
         ("soft_cap", ctypes.c_float),
         ("causal", ctypes.c_int32),
         ("kv_heads", ctypes.c_int32),
+        ("q_segment_ids", ctypes.c_void_p),
+        ("kv_segment_ids", ctypes.c_void_p),
     ]
+
+
+def _segment_args(q_segment_ids, kv_segment_ids, B, Sq, Sk):
+    if (q_segment_ids is None) != (kv_segment_ids is None):
+        raise ValueError("segment ids come in pairs (queries and keys)")
+    if q_segment_ids is None:
+        return 0, 0
+    for name, t, S in (("q_segment_ids", q_segment_ids, Sq), ("kv_segment_ids", kv_segment_ids, Sk)):
+        _require_gpu(name, t)
+        if t.dtype != torch.int32 or tuple(t.shape) != (B, S):
+            raise ValueError(f"{name} must be int32 [B, {S}]")
+    return q_segment_ids.data_ptr(), kv_segment_ids.data_ptr()
 
 
 class _PlanColsT(ctypes.Structure):
@@ -259,7 +273,9 @@ def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
                 scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                 lse: Optional[torch.Tensor] = None, want_lse: bool = True, *,
                 attn_sink: Optional[torch.Tensor] = None, soft_cap: Optional[float] = None,
-                causal: bool = False, bs: Optional[int] = None
+                causal: bool = False, bs: Optional[int] = None,
+                q_segment_ids: Optional[torch.Tensor] = None,
+                kv_segment_ids: Optional[torch.Tensor] = None
                 ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Block-sparse attention forward.
 
@@ -272,6 +288,8 @@ def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
     key tokens after the query token.  bs (default Sq / Mb) must be given when
     a length is not a multiple of the block size: the plan's layout then
     covers ceil(S / bs) blocks and the last block is cut at the sequence end.
+    q_segment_ids / kv_segment_ids (int32 [B, Sq] / [B, Sk]) restrict every
+    query to the keys of its own segment (packed sequences).
     """
     for name, t in (("q", q), ("k", k), ("v", v)):
         _require_gpu(name, t)
@@ -308,14 +326,16 @@ def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
             raise ValueError("lse must be fp32 [B, H, Sq]")
     dtype = BSA_BF16 if q.dtype == torch.bfloat16 else BSA_F32
     lse_ptr = ctypes.c_void_p(lse.data_ptr() if lse is not None else 0)
-    if attn_sink is None and soft_cap is None and not causal and Hkv == H:
+    qsp, ksp = _segment_args(q_segment_ids, kv_segment_ids, B, Sq, Sk)
+    if attn_sink is None and soft_cap is None and not causal and Hkv == H and not qsp:
         _check(load_library().bsa_forward(
             ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
             ctypes.c_void_p(v.data_ptr()), ctypes.byref(plan._raw), B, H, Sq, Sk, bs, d, dtype,
             float(scale), ctypes.c_void_p(out.data_ptr()), lse_ptr, _stream(q)))
         return out, lse
     opts = _FwdOptsT(ctypes.c_void_p(attn_sink.data_ptr() if attn_sink is not None else 0),
-                     float(soft_cap or 0.0), 1 if causal else 0, Hkv)
+                     float(soft_cap or 0.0), 1 if causal else 0, Hkv, ctypes.c_void_p(qsp),
+                     ctypes.c_void_p(ksp))
     _check(load_library().bsa_forward_ex(
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
         ctypes.c_void_p(v.data_ptr()), ctypes.byref(plan._raw), B, H, Sq, Sk, bs, d, dtype,
@@ -386,7 +406,9 @@ def bsa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
                  soft_cap: Optional[float] = None, causal: bool = False,
                  dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
                  dv: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None, bs: Optional[int] = None):
+                 workspace: Optional[torch.Tensor] = None, bs: Optional[int] = None,
+                 q_segment_ids: Optional[torch.Tensor] = None,
+                 kv_segment_ids: Optional[torch.Tensor] = None):
     """Gradients of bsa_forward for the upstream gradient dout.
 
     q, k, v, scale and the options must be those of the forward call that
@@ -428,8 +450,10 @@ def bsa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
     elif workspace.numel() * workspace.element_size() < wbytes:
         raise ValueError("workspace too small")
     dsink = torch.empty(H, dtype=torch.float32, device=q.device) if attn_sink is not None else None
+    qsp, ksp = _segment_args(q_segment_ids, kv_segment_ids, B, Sq, Sk)
     opts = _FwdOptsT(ctypes.c_void_p(attn_sink.data_ptr() if attn_sink is not None else 0),
-                     float(soft_cap or 0.0), 1 if causal else 0, Hkv)
+                     float(soft_cap or 0.0), 1 if causal else 0, Hkv, ctypes.c_void_p(qsp),
+                     ctypes.c_void_p(ksp))
     _check(lib.bsa_backward(
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
         ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()),

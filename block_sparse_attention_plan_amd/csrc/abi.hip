@@ -59,7 +59,7 @@ int check_plan_cols(const bsa_plan_cols_t *pc, bsa::PlanColsGeometry *g) {
 // validated and turned into kernel form.  `who` prefixes error messages.
 int make_options(const bsa_forward_opts_t *opts, int32_t H, float scale, bsa::FwdOptions *fo,
                  const char *who) {
-  *fo = bsa::FwdOptions{nullptr, 0.f, 0.f, 0, 1, 0, 0};
+  *fo = bsa::FwdOptions{nullptr, 0.f, 0.f, 0, 1, 0, 0, nullptr, nullptr};
   if (opts == nullptr) return BSA_OK;
   const int32_t hkv = opts->kv_heads == 0 ? H : opts->kv_heads;
   if (hkv < 1 || H % hkv != 0)
@@ -82,6 +82,13 @@ int make_options(const bsa_forward_opts_t *opts, int32_t H, float scale, bsa::Fw
   }
   fo->causal = opts->causal != 0;
   fo->kv_group = H / hkv;
+  if ((opts->q_segment_ids == nullptr) != (opts->kv_segment_ids == nullptr))
+    return fail(BSA_ERR_INVALID_ARG, "%s: segment ids come in pairs (queries and keys)", who);
+  if ((opts->q_segment_ids != nullptr && !aligned(opts->q_segment_ids, 4)) ||
+      (opts->kv_segment_ids != nullptr && !aligned(opts->kv_segment_ids, 4)))
+    return fail(BSA_ERR_MISALIGNED, "%s: segment ids must be 4-byte aligned", who);
+  fo->qseg = opts->q_segment_ids;
+  fo->kseg = opts->kv_segment_ids;
   return BSA_OK;
 }
 

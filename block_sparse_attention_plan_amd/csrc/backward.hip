@@ -216,6 +216,7 @@ bwd_dq_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   const int qrow = 32 * wid + l32;            // query row inside the block
   const int64_t i_row = (int64_t)m * BS + qrow;
   const bool q_ok = !MASK || i_row < Sq;     // rows past a cut last block
+  const int qsg = (MASK && opt.qseg && q_ok) ? opt.qseg[(int64_t)b * Sq + i_row] : 0;
 
   const float l2 = q_ok ? lse2[bh * Sq + i_row] : __builtin_inff();
   const float dd = q_ok ? Dv[bh * Sq + i_row] : 0.f;
@@ -262,6 +263,10 @@ bwd_dq_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
         float p = wt.p;
         if (diag && 32 * jt + 8 * (e / 4) + 4 * h2 + (e % 4) > qrow) p = 0.f;
         if (MASK && 32 * jt + 8 * (e / 4) + 4 * h2 + (e % 4) >= kv) p = 0.f;
+        if (MASK && opt.qseg) {  // packed sequences: only keys of the query's segment
+          const int kt = 32 * jt + 8 * (e / 4) + 4 * h2 + (e % 4);
+          if (kt < kv && opt.kseg[(int64_t)b * Sk + (int64_t)ncol * BS + kt] != qsg) p = 0.f;
+        }
         s[e] = p * (dp[e] - dd) * wt.slope;
       }
 #pragma unroll
@@ -304,6 +309,7 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   __shared__ __attribute__((aligned(1024))) __bf16 Gs[TILE];   // dO tile
   __shared__ __attribute__((aligned(16))) float Ls[BS];         // lse2 of the tile's rows
   __shared__ __attribute__((aligned(16))) float Ds[BS];         // D of the tile's rows
+  __shared__ __attribute__((aligned(16))) int32_t Gq[BS];       // segment ids of the tile's rows
 
   const int64_t W = (int64_t)B * Hkv * Nb;
   const int64_t per = (W + 7) / 8;
@@ -327,6 +333,7 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   const int krow = 32 * wid + l32;            // key row inside the block
   const int64_t j_row = (int64_t)n * BS + krow;
   const bool k_ok = !MASK || j_row < Sk;     // keys past a cut last block
+  const int ksg = (MASK && opt.kseg && k_ok) ? opt.kseg[(int64_t)b * Sk + j_row] : 0;
 
   bf16x8 kf[QC], vf[QC];
 #pragma unroll
@@ -366,6 +373,7 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
         // rows past a cut last block: weight exp2(s - inf) = 0
         Ls[tid] = tid < qv ? lse2[bh * Sq + (int64_t)m * BS + tid] : __builtin_inff();
         Ds[tid] = tid < qv ? Dv[bh * Sq + (int64_t)m * BS + tid] : 0.f;
+        if (MASK && opt.qseg) Gq[tid] = tid < qv ? opt.qseg[(int64_t)b * Sq + (int64_t)m * BS + tid] : 0;
       }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -395,6 +403,7 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
             float p = wt.p;
             if (diag && krow > 32 * jq + 8 * a + 4 * h2 + i) p = 0.f;
             if (!k_ok) p = 0.f;
+            if (MASK && opt.qseg && Gq[32 * jq + 8 * a + 4 * h2 + i] != ksg) p = 0.f;
             s[e] = p;
             if constexpr (MASK) w[e] = p * wt.slope;
           }
@@ -511,7 +520,7 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
                            : launch_pre<128>(a, stream);
   if (e != hipSuccess) return e;
   const bool mask = a.opt.cap_k != 0.f || a.opt.causal != 0 || a.opt.sq % a.bs != 0 ||
-                    a.opt.sk % a.bs != 0;
+                    a.opt.sk % a.bs != 0 || a.opt.qseg != nullptr;
 #define BSA_BWD_CASE(BS_, D_)                                                                  \
   if (a.bs == BS_ && a.d == D_) e = mask ? launch_grads<BS_, D_, true>(a, stream)             \
                                          : launch_grads<BS_, D_, false>(a, stream);

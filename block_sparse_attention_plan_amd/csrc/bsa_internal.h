@@ -29,6 +29,8 @@ struct FwdOptions {
   int32_t kv_group;   // query heads per K/V head (1 without grouping)
   int32_t sq, sk;     // sequence lengths; the last block is cut where they are
                       // not multiples of the block size
+  const int32_t *qseg;  // [B, sq] segment ids of the queries, or nullptr
+  const int32_t *kseg;  // [B, sk] segment ids of the keys (set with qseg)
 };
 
 // Returns hipErrorInvalidValue when no kernel instance matches (bs, d, f32).

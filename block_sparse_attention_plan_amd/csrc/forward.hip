@@ -135,6 +135,7 @@ bsa_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__rest
   float *lh = lse ? lse + bh * Sq : nullptr;
   const int64_t i_row = (int64_t)m * BS + 16 * wid + li;  // this lane's query row
   const bool q_ok = !MASK || i_row < Sq;                  // rows past a cut last block
+  const int qsg = (MASK && opt.qseg && q_ok) ? opt.qseg[(int64_t)b * Sq + i_row] : 0;
 
   if (beg == end) {  // no live tile: zero output, lse = -inf (the sink logit with a sink)
     if (!q_ok) return;
@@ -221,6 +222,16 @@ bsa_fwd_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__rest
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (16 * jt + 4 * G + e >= kv) s[jt][e] = -__builtin_inff();
+    }
+    if (MASK && opt.qseg) {  // packed sequences: only keys of the query's segment
+      const int64_t k0 = (int64_t)col_idx[t] * BS;
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t key = k0 + 16 * jt + 4 * G + e;
+          if (key < Sk && opt.kseg[(int64_t)b * Sk + key] != qsg) s[jt][e] = -__builtin_inff();
+        }
     }
     // Online softmax over this tile's keys for query column li.
     float mx = s[0][0];
@@ -355,6 +366,7 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
   float *lh = lse ? lse + bh * Sq : nullptr;
   const int64_t i_row = (int64_t)m * BS + 32 * rg + l32;
   const bool q_ok = !MASK || i_row < Sq;  // rows past a cut last block
+  const int qsg = (MASK && opt.qseg && q_ok) ? opt.qseg[(int64_t)b * Sq + i_row] : 0;
 
   if (beg == end) {
     if (ks == 0 && q_ok) {
@@ -455,6 +467,16 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
 #pragma unroll
         for (int e = 0; e < 16; ++e)
           if (32 * jt + 8 * (e / 4) + (e % 4) >= kv) s[jt][e] = -__builtin_inff();
+    }
+    if (opt.qseg) {  // packed sequences: only keys of the query's segment
+      const int64_t k0 = (int64_t)ncol * BS + key0 + 4 * h2;
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t key = k0 + 32 * jt + 8 * (e / 4) + (e % 4);
+          if (key < Sk && opt.kseg[(int64_t)b * Sk + key] != qsg) s[jt][e] = -__builtin_inff();
+        }
     }
   };
 
@@ -671,6 +693,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   float *lh = lse ? lse + bh * Sq : nullptr;
   const int64_t i_row = (int64_t)m * BS + 32 * rg + l32;
   const bool q_ok = !MASK || i_row < Sq;  // rows past a cut last block
+  const int qsg = (MASK && opt.qseg && q_ok) ? opt.qseg[(int64_t)b * Sq + i_row] : 0;
 
   if (beg == end) {
     if (ks == 0 && q_ok) {
@@ -762,6 +785,16 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
 #pragma unroll
         for (int e = 0; e < 16; ++e)
           if (32 * jt + 8 * (e / 4) + (e % 4) >= kv) s[jt][e] = -__builtin_inff();
+    }
+    if (opt.qseg) {  // packed sequences: only keys of the query's segment
+      const int64_t k0 = (int64_t)ncol * BS + key0 + 4 * h2;
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t key = k0 + 32 * jt + 8 * (e / 4) + (e % 4);
+          if (key < Sk && opt.kseg[(int64_t)b * Sk + key] != qsg) s[jt][e] = -__builtin_inff();
+        }
     }
   };
 
@@ -984,11 +1017,20 @@ hipError_t launch_one(const void *q, const void *k, const void *v, const int32_t
                        stream, (const T *)q, (const T *)k, (const T *)v, row_ptr, col_idx,
                        row_order, B, H, Mb, Nb, scale * kLog2e, (T *)out, lse, opt);
   } else if constexpr (BS >= 64 && std::is_same<T, __bf16>::value) {
-    constexpr int KS = BS == 128 ? kDmaKeySplit : 2;
-    hipLaunchKernelGGL((bsa_fwd_dma_kernel<BS, D, KS, MASK>), dim3((unsigned)grid),
-                       dim3(BS * 2 * KS), 0, stream, (const __bf16 *)q, (const __bf16 *)k,
-                       (const __bf16 *)v, row_ptr, col_idx, row_order, B, H, Mb, Nb,
-                       scale * kLog2e, (__bf16 *)out, lse, opt);
+    if (opt.qseg == nullptr) {
+      constexpr int KS = BS == 128 ? kDmaKeySplit : 2;
+      hipLaunchKernelGGL((bsa_fwd_dma_kernel<BS, D, KS, MASK>), dim3((unsigned)grid),
+                         dim3(BS * 2 * KS), 0, stream, (const __bf16 *)q, (const __bf16 *)k,
+                         (const __bf16 *)v, row_ptr, col_idx, row_order, B, H, Mb, Nb,
+                         scale * kLog2e, (__bf16 *)out, lse, opt);
+    } else {
+      // segment ids need per-key loads beside the products, which the copy
+      // kernel's fixed-count waits do not allow: use the register-staged one
+      hipLaunchKernelGGL((bsa_fwd32_kernel<BS, D, T, 2, MASK>), dim3((unsigned)grid),
+                         dim3(BS * 4), 0, stream, (const T *)q, (const T *)k, (const T *)v,
+                         row_ptr, col_idx, row_order, B, H, Mb, Nb, scale * kLog2e, (T *)out, lse,
+                         opt);
+    }
   } else {
     constexpr int KSPLIT = BS >= 64 ? 2 : 1;
     hipLaunchKernelGGL((bsa_fwd32_kernel<BS, D, T, KSPLIT, MASK>), dim3((unsigned)grid),
@@ -1005,7 +1047,8 @@ hipError_t dispatch(int32_t bs, int32_t d, const void *q, const void *k, const v
                     float *lse, hipStream_t s) {
   // Score-changing options (cap, causal) and cut last blocks select their own
   // kernel instances, so the plain forward keeps the code it has without them.
-  const bool mask = opt.cap_k != 0.f || opt.causal != 0 || opt.sq % bs != 0 || opt.sk % bs != 0;
+  const bool mask = opt.cap_k != 0.f || opt.causal != 0 || opt.sq % bs != 0 || opt.sk % bs != 0 ||
+                    opt.qseg != nullptr;
 #define BSA_CASE(BS_, D_)                                                                   \
   if (bs == BS_ && d == D_)                                                                 \
     return mask ? launch_one<BS_, D_, T, true>(q, k, v, rp, ci, ro, B, H, Mb, Nb, scale, opt, \

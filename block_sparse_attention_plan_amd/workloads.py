@@ -180,6 +180,22 @@ def make_topic_qk(H: int, Hkv: int, S: int, d: int, bs: int, n_topics: int, nois
     return _tensor(q, dtype), _tensor(k, dtype), tq, tk
 
 
+def packed_segment_ids(B: int, S: int, min_len: int, max_len: int, seed: int) -> torch.Tensor:
+    """Segment ids of sequences packed back to back: per batch item, lengths
+    drawn uniformly from [min_len, max_len] until S tokens are filled (the
+    last one cut), ids 0, 1, 2, ... in order.  int32 [B, S] on the CPU."""
+    rng = np.random.default_rng(seed)
+    ids = np.empty((B, S), np.int32)
+    for b in range(B):
+        pos, sid = 0, 0
+        while pos < S:
+            L = int(rng.integers(min_len, max_len + 1))
+            ids[b, pos:pos + L] = sid
+            pos += L
+            sid += 1
+    return torch.from_numpy(ids)
+
+
 def sink_logits(H: int, mean: float, seed: int) -> torch.Tensor:
     """Per-head sink logits N(mean, 1), fp32 [H] on the CPU."""
     rng = np.random.default_rng(seed)

@@ -138,6 +138,8 @@ typedef struct {
   float soft_cap;         /* > 0: tanh logit cap; 0: none */
   int32_t causal;         /* nonzero: also mask key token j > query token i */
   int32_t kv_heads;       /* K/V heads Hkv (H % Hkv == 0); 0 means H */
+  const int32_t *q_segment_ids;  /* device int32 [B, Sq] or NULL (packed sequences) */
+  const int32_t *kv_segment_ids; /* device int32 [B, Sk]; given iff q_segment_ids is */
 } bsa_forward_opts_t;
 
 /*
@@ -155,11 +157,16 @@ typedef struct {
  *                  capped), so lse includes it and a row with no live key gets
  *                  out = 0 and lse = attn_sink[h];
  *   kv_heads:      k and v are [B, Hkv, Sk, d]; query head h reads K/V head
- *                  h / (H / Hkv) (grouped-query attention).
+ *                  h / (H / Hkv) (grouped-query attention);
+ *   segment ids:   (the operation's q_segment_ids / kv_segment_ids, for
+ *                  several sequences packed into one) s_ij = -inf also where
+ *                  q_segment_ids[b, i] != kv_segment_ids[b, j].  bf16 calls
+ *                  with bs >= 64 then run the register-staged kernel.
  * Arguments, layouts and ownership as for bsa_forward; opts is a host pointer
  * read during the call.  Errors as for bsa_forward, plus BSA_ERR_INVALID_ARG
- * for kv_heads < 0 or not dividing H, or a soft_cap that is negative or not
- * finite, and BSA_ERR_MISALIGNED for an attn_sink not 4-byte aligned.
+ * for kv_heads < 0 or not dividing H, a soft_cap that is negative or not
+ * finite, or only one of the two segment-id arrays, and BSA_ERR_MISALIGNED
+ * for an attn_sink or segment-id array not 4-byte aligned.
  */
 int bsa_forward_ex(const void *q, const void *k, const void *v, const bsa_plan_t *plan,
                    int32_t B, int32_t H, int32_t Sq, int32_t Sk, int32_t bs, int32_t d,

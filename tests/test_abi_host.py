@@ -134,6 +134,14 @@ def test_bsa_forward_ex_validation(lib):
     assert call(soft_cap=float("nan")) == INVALID
     assert call(soft_cap=1e-44) == INVALID      # 2*scale*log2(e)/cap overflows fp32
     assert call(sink=0x10002) == MISALIGNED
+    # segment ids come in pairs and are 4-byte aligned
+    def call_seg(qs, ks):
+        o = bsa._FwdOptsT(None, 0.0, 0, 0, qs, ks)
+        return lib.bsa_forward_ex(f, f, f, P, 1, 2, 64, 64, 16, 32, 0, 0.5, ctypes.byref(o), f,
+                                  None, None)
+    assert call_seg(0x10000, None) == INVALID
+    assert call_seg(None, 0x10000) == INVALID
+    assert call_seg(0x10002, 0x10000) == MISALIGNED
     # the plain checks still run first with options present
     assert call(kv_heads=1, H=3) == MISMATCH
     assert call(opts=False, d=48) == UNSUPPORTED

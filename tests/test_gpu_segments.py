@@ -1,0 +1,85 @@
+"""GPU parity of segment ids (packed sequences) against the fp64 oracle.
+
+Sequences of random lengths are packed back to back; a query attends only
+the keys of its own segment, on top of the layout (and the causal mask and
+cut last blocks where given).  Forward on every kernel family -- bf16 with
+bs >= 64 then runs the register-staged kernel -- and the backward, with the
+whole-block tolerances.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_plan_amd as bsa
+from block_sparse_attention_plan_amd import workloads as W
+from oracle import bsa_oracle as O
+
+from test_gpu_backward import check_plan_cols, compare_grad
+from test_gpu_parity import bf16_rounded, check_plan, compare, compare_lse, say, to64
+
+pytestmark = pytest.mark.gpu
+
+FWD = [(16, 64, "bf16", 160, 160), (16, 32, "f32", 100, 93), (32, 64, "bf16", 256, 256),
+       (64, 128, "f32", 320, 320), (64, 128, "bf16", 300, 300), (128, 128, "bf16", 512, 512),
+       (128, 64, "bf16", 500, 450)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("bs,d,dtype,Sq,Sk", FWD)
+def test_forward_segments(gpu, bs, d, dtype, Sq, Sk, causal):
+    H, B = 2, 2
+    Mb, Nb = -(-Sq // bs), -(-Sk // bs)
+    rng = np.random.default_rng(bs * 7 + d + Sq)
+    lay = (rng.random((H, Mb, Nb)) < 0.7).astype(np.int32)
+    lay[:, np.arange(min(Mb, Nb)), np.arange(min(Mb, Nb))] = 1
+    x = W.make_bsa("segments", B=B, H=H, S=Sq, Sk=Sk, bs=bs, d=d, dtype=dtype, layout="given",
+                   layout_array=lay, seed=Sq + d)
+    qs = W.packed_segment_ids(B, Sq, 5, 90, seed=Sq)
+    ks = qs if Sq == Sk else W.packed_segment_ids(B, Sk, 5, 90, seed=Sq)
+    say(f"[segments] forward bs={bs} d={d} {dtype} Sq={Sq} Sk={Sk} causal={causal}")
+    plan, _ = check_plan(gpu, lay)
+    out, lse = bsa.bsa_forward(x.q.to(gpu), x.k.to(gpu), x.v.to(gpu), plan, x.scale, bs=bs,
+                               causal=causal, q_segment_ids=qs.to(gpu),
+                               kv_segment_ids=ks.to(gpu))
+    torch.cuda.synchronize()
+    kw = dict(causal=causal, q_segment_ids=qs.numpy(), kv_segment_ids=ks.numpy())
+    ref, ref_lse = O.attention_live_tiles(to64(x.q), to64(x.k), to64(x.v), lay, bs, x.scale, **kw)
+    compare(to64(out), ref, f"segments bs={bs} d={d} {dtype}")
+    if dtype == "f32":
+        _, ref_lse = O.attention_live_tiles(bf16_rounded(x.q), bf16_rounded(x.k),
+                                            bf16_rounded(x.v), lay, bs, x.scale, **kw)
+    compare_lse(lse.cpu().numpy(), ref_lse, f"segments bs={bs} d={d}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("bs,d,S", [(32, 64, 250), (64, 128, 256), (128, 128, 400)])
+def test_backward_segments(gpu, bs, d, S, causal):
+    H, Hkv, B = 4, 2, 2
+    nb = -(-S // bs)
+    rng = np.random.default_rng(bs + S)
+    lay = (rng.random((H, nb, nb)) < 0.7).astype(np.int32)
+    lay[:, np.arange(nb), np.arange(nb)] = 1
+    x = W.make_bsa("segments_bwd", B=B, H=H, S=S, bs=bs, d=d, dtype="bf16", layout="given",
+                   layout_array=lay, seed=S + 3, Hkv=Hkv, sink_mean=1.0)
+    seg = W.packed_segment_ids(B, S, 5, 120, seed=S + 1)
+    dout = W.upstream_gradient(x.q.shape, seed=S + 2)
+    say(f"[segments] backward bs={bs} d={d} S={S} causal={causal}")
+    plan, _ = check_plan(gpu, lay)
+    pc = check_plan_cols(gpu, lay, Hkv)
+    q, k, v, sink, sg = x.q.to(gpu), x.k.to(gpu), x.v.to(gpu), x.sink.to(gpu), seg.to(gpu)
+    kw = dict(attn_sink=sink, causal=causal, bs=bs, q_segment_ids=sg, kv_segment_ids=sg)
+    out, lse = bsa.bsa_forward(q, k, v, plan, x.scale, **kw)
+    dq, dk, dv, dsink = bsa.bsa_backward(q, k, v, out, dout.to(gpu), lse, plan, pc, x.scale, **kw)
+    torch.cuda.synchronize()
+    sk64 = x.sink.numpy().astype(np.float64)
+    okw = dict(sink=sk64, causal=causal, q_segment_ids=seg.numpy(), kv_segment_ids=seg.numpy())
+    rq, rk, rv, rs = O.attention_backward_dense(to64(x.q), to64(x.k), to64(x.v), to64(dout), lay,
+                                                bs, x.scale, **okw)
+    compare_grad(to64(dq), rq, f"dq segments bs={bs}")
+    compare_grad(to64(dk), rk, f"dk segments bs={bs}")
+    compare_grad(to64(dv), rv, f"dv segments bs={bs}")
+    o64, l64 = O.attention_dense_masked(to64(x.q), to64(x.k), to64(x.v), lay, bs, x.scale, **okw)
+    w = np.exp(sk64[None, :, None] - l64)
+    bound = 2.0 * 2.0 ** -9 * (w * np.abs(to64(dout) * o64).sum(-1)).sum(axis=(0, 2))
+    assert np.all(np.abs(dsink.cpu().numpy() - rs) <= bound + 1e-6)
