@@ -114,6 +114,13 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rs, void *l
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (BSA_LDS void *)lds_base, 16, voff, soff, 0, 0);
 }
 
+// The same with 4 bytes per lane (buffer_load_dword ... lds): one wave
+// instruction fills 256 contiguous LDS bytes at lds_base + 4 * lane.
+__device__ __forceinline__ void copy4_to_lds(__amdgpu_buffer_rsrc_t rs, void *lds_base,
+                                             uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (BSA_LDS void *)lds_base, 4, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16 *lds_ptr) {
   i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BSA_LDS i16x4 *)(lds_ptr));
   return __builtin_bit_cast(bf16x4, r);

@@ -12,10 +12,13 @@
 //
 // Work item = (batch, position); one workgroup of four waves, wave w owning
 // heads 16w .. 16w+15 over all of d.  Slots are processed in chunks of 32
-// whose rows are copied straight from HBM into LDS (one
-// buffer_load_dwordx4 ... lds per 1 KiB row; slots without a valid index get a
-// zero row), one chunk ahead into the other of two buffers, so the one
-// gather serves all heads of the position.  Every wave computes
+// whose rows are copied straight from HBM into LDS (at d = 512 one
+// buffer_load_dwordx4 ... lds per 1 KiB row; at d = 128 and 256 one or two
+// buffer_load_dword ... lds of 256 bytes, so that every row keeps its
+// padding; slots without a valid index get a zero row), one chunk ahead into
+// the other of two buffers, so the one gather serves all heads of the
+// position.  The page's kernel takes d as a parameter; d_h = 512 is the size
+// its shapes show.  Every wave computes
 //   S^T = KV Q^T       (16x16x32 MFMA, Q^T resident in registers)
 //   online softmax     (lane owns one head column; the running maximum may
 //                      lag the true one by a bounded amount before the
@@ -48,7 +51,7 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
   constexpr int RPW = T / 4;          // rows gathered per wave per chunk
   constexpr int QC = D / 32;          // 32-wide k steps of S^T
   constexpr int DT = D / 16;          // 16-wide d tiles of O^T
-  static_assert(D == 512, "one wave instruction copies one 1 KiB row");
+  static_assert(D == 512 || D == 256 || D == 128, "row copies: one 1 KiB or D/128 256-byte pieces");
 
   __shared__ __attribute__((aligned(16))) __bf16 C0[T * STR];
   __shared__ __attribute__((aligned(16))) __bf16 C1[T * STR];
@@ -91,8 +94,15 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
       const int row = wid * RPW + j;
       const int src = __builtin_amdgcn_readlane(my, row);
       if (src >= 0) {
-        copy16_to_lds(kv_rs, dst + row * STR, (uint32_t)(lane * 16), (uint32_t)src * (uint32_t)(D * 2));
-      } else {
+        if constexpr (D == 512) {
+          copy16_to_lds(kv_rs, dst + row * STR, (uint32_t)(lane * 16), (uint32_t)src * (uint32_t)(D * 2));
+        } else {
+#pragma unroll
+          for (int p = 0; p < D / 128; ++p)
+            copy4_to_lds(kv_rs, dst + row * STR + 128 * p, (uint32_t)(lane * 4 + 256 * p),
+                         (uint32_t)src * (uint32_t)(D * 2));
+        }
+      } else if (lane < D / 8) {
         *reinterpret_cast<bf16x8 *>(dst + row * STR + lane * 8) = bf16x8{};
       }
     }
@@ -198,7 +208,9 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
 
 }  // namespace
 
-bool topk_supported(int32_t H, int32_t d) { return H >= 1 && H <= 64 && d == 512; }
+bool topk_supported(int32_t H, int32_t d) {
+  return H >= 1 && H <= 64 && (d == 128 || d == 256 || d == 512);
+}
 
 hipError_t launch_topk(const void *q, const void *kv, const int32_t *idx, const float *sink,
                        int32_t B, int32_t M, int32_t N, int32_t H, int32_t d, int32_t topk,
@@ -206,9 +218,14 @@ hipError_t launch_topk(const void *q, const void *kv, const int32_t *idx, const 
   if (!topk_supported(H, d)) return hipErrorInvalidValue;
   const int64_t grid = (int64_t)B * M;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(topk_kernel<512>, dim3((unsigned)grid), dim3(256), 0, stream,
-                     (const __bf16 *)q, (const __bf16 *)kv, idx, sink, M, N, H, topk,
-                     scale * kLog2e, (__bf16 *)out);
+#define BSA_TOPK_LAUNCH(D_)                                                                    \
+  hipLaunchKernelGGL(topk_kernel<D_>, dim3((unsigned)grid), dim3(256), 0, stream,              \
+                     (const __bf16 *)q, (const __bf16 *)kv, idx, sink, M, N, H, topk,           \
+                     scale * kLog2e, (__bf16 *)out)
+  if (d == 512) BSA_TOPK_LAUNCH(512);
+  else if (d == 256) BSA_TOPK_LAUNCH(256);
+  else BSA_TOPK_LAUNCH(128);
+#undef BSA_TOPK_LAUNCH
   return hipGetLastError();
 }
 

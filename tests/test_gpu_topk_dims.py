@@ -1,0 +1,40 @@
+"""GPU parity of the top-k gathered attention at head sizes 128 and 256 (the
+page's kernel takes d as a parameter) against the fp64 oracle, with the same
+cases as the d = 512 tests: sinks, -1 slots, out-of-range entries, head
+counts that are not multiples of 16, and a position with no valid slot."""
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_plan_amd as bsa
+from block_sparse_attention_plan_amd import workloads as W
+from oracle import bsa_oracle as O
+
+from test_gpu_parity import compare, say, to64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("H,topk,N,with_sink,drop", [
+    (64, 200, 300, True, 0.05), (16, 65, 80, True, 0.3), (5, 1, 10, True, 0.0),
+    (1, 130, 500, False, 0.1), (37, 127, 127, True, 0.5)])
+def test_topk_head_dims(gpu, d, H, topk, N, with_sink, drop):
+    t = W.make_topk("topk_dims", B=2, M=6, H=H, d=d, N=N, topk=topk, seed=H + topk + d,
+                    drop=drop, with_sink=with_sink)
+    idx = t.idx.clone()
+    idx[0, 0, :] = -1                      # a position with no valid slot
+    if topk > 2:
+        idx[1, 1, 0] = N + 5               # out of range acts as missing
+        idx[1, 1, 1] = -7
+    say(f"[topk] d={d} H={H} topk={topk} N={N} sink={with_sink} drop={drop}")
+    sink = t.sink.to(gpu) if with_sink else None
+    out = bsa.topk_sparse_attn(t.q.to(gpu), t.kv.to(gpu), idx.to(gpu), sink, t.scale)
+    torch.cuda.synchronize()
+    ref_idx = idx.numpy().copy()
+    ref_idx[(ref_idx < 0) | (ref_idx >= N)] = -1
+    ref = O.topk_attention(to64(t.q), to64(t.kv), ref_idx,
+                           t.sink.numpy() if with_sink else None, t.scale)
+    compare(to64(out), ref, f"topk d={d} H={H}")
+    assert torch.all(out[0, 0] == 0)
