@@ -413,12 +413,13 @@ def bsa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
 
     q, k, v, scale and the options must be those of the forward call that
     produced out and lse.  Returns (dq, dk, dv, dsink): dq like q, dk and dv
-    like k, dsink fp32 [H] (None without a sink).  bf16 only.
+    like k, dsink fp32 [H] (None without a sink).  bf16 or fp32 I/O.
     """
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("lse", lse)):
         _require_gpu(name, t)
-    if any(t.dtype != torch.bfloat16 for t in (q, k, v, out, dout)):
-        raise ValueError("q, k, v, out, dout must be bf16")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype) or \
+            q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q, k, v, out, dout must share dtype bf16 or fp32")
     B, H, Sq, d = (int(x) for x in q.shape)
     Hkv, Sk = int(k.shape[1]), int(k.shape[2])
     if tuple(k.shape) != tuple(v.shape) or k.shape[0] != B or k.shape[3] != d or H % Hkv:
@@ -458,7 +459,8 @@ def bsa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
         ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()),
         ctypes.c_void_p(dout.data_ptr()), ctypes.c_void_p(lse.data_ptr()),
-        ctypes.byref(plan._raw), ctypes.byref(plan_cols._raw), B, H, Sq, Sk, bs, d, BSA_BF16,
+        ctypes.byref(plan._raw), ctypes.byref(plan_cols._raw), B, H, Sq, Sk, bs, d,
+        BSA_BF16 if q.dtype == torch.bfloat16 else BSA_F32,
         float(scale), ctypes.byref(opts), ctypes.c_void_p(workspace.data_ptr()),
         workspace.numel() * workspace.element_size(), ctypes.c_void_p(dq.data_ptr()),
         ctypes.c_void_p(dk.data_ptr()), ctypes.c_void_p(dv.data_ptr()),

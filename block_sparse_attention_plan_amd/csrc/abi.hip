@@ -278,9 +278,8 @@ int bsa_backward(const void *q, const void *k, const void *v, const void *out, c
     return fail(BSA_ERR_PLAN_MISMATCH,
                 "bsa_backward: H=%d Sq=%d Sk=%d bs=%d do not match plan H=%d Mb=%d Nb=%d", H, Sq,
                 Sk, bs, plan->H, plan->Mb, plan->Nb);
-  if (dtype != BSA_BF16)
-    return fail(dtype == BSA_F32 ? BSA_ERR_UNSUPPORTED : BSA_ERR_INVALID_ARG,
-                "bsa_backward: dtype %d (only bf16 has a backward kernel)", (int)dtype);
+  if (dtype != BSA_BF16 && dtype != BSA_F32)
+    return fail(BSA_ERR_INVALID_ARG, "bsa_backward: unknown dtype %d", (int)dtype);
   if (!(std::isfinite(scale) && scale > 0.f))
     return fail(BSA_ERR_INVALID_ARG, "bsa_backward: scale must be finite and > 0");
   bsa::FwdOptions fo;
@@ -317,6 +316,7 @@ int bsa_backward(const void *q, const void *k, const void *v, const void *out, c
   a.row_idx = at<int32_t>(plan_cols->dev_buf, gc.off_row_idx);
   a.col_order = at<int32_t>(plan_cols->dev_buf, gc.off_col_order);
   a.B = B; a.H = H; a.Mb = plan->Mb; a.Nb = plan->Nb; a.bs = bs; a.d = d;
+  a.f32 = dtype == BSA_F32;
   a.scale = scale;
   a.opt = fo;
   a.Dv = static_cast<float *>(workspace);

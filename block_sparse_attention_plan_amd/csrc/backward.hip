@@ -101,12 +101,67 @@ __device__ __forceinline__ void store4_bf16(__bf16 *p, float a, float b, float c
   *reinterpret_cast<bf16x4 *>(p) = r;
 }
 
+// The two I/O types: 8 consecutive elements as a bf16 MFMA operand (fp32
+// rounds to nearest even, as the forward does), as floats, and 4 results
+// stored in the I/O type.
+template <typename T> struct BIo;
+template <> struct BIo<__bf16> {
+  static __device__ __forceinline__ bf16x8 load8(const __bf16 *p) {
+    return *reinterpret_cast<const bf16x8 *>(p);
+  }
+  static __device__ __forceinline__ void load8f(const __bf16 *p, float (&x)[8]) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (float)v[i];
+  }
+  static __device__ __forceinline__ void store4(__bf16 *p, float a, float b, float c, float d) {
+    store4_bf16(p, a, b, c, d);
+  }
+};
+template <> struct BIo<float> {
+  static __device__ __forceinline__ bf16x8 load8(const float *p) {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+    return to_bf16x8(a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]);
+  }
+  static __device__ __forceinline__ void load8f(const float *p, float (&x)[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = a[i];
+      x[4 + i] = b[i];
+    }
+  }
+  static __device__ __forceinline__ void store4(float *p, float a, float b, float c, float d) {
+    *reinterpret_cast<f32x4 *>(p) = f32x4{a, b, c, d};
+  }
+};
+
+// One tile into the swizzled bf16 LDS layout: bf16 tiles by LDS copies, fp32
+// tiles through registers (rounded to bf16).  Rows at or past `rows` (a block
+// cut at the sequence end) become zeros.
+template <int BS, int D, int NW, typename T>
+__device__ __forceinline__ void stage_tile(const T *src, __bf16 *dst, int wid, int lane, int rows) {
+  if constexpr (std::is_same<T, __bf16>::value) {
+    copy_tile<BS, D, NW>(src, dst, wid, lane, (uint32_t)(rows * D * 2));
+  } else {
+    constexpr int CPR = D / 8;
+    const int tid = wid * 64 + lane;
+    for (int i = tid; i < BS * CPR; i += NW * 64) {
+      const int row = i / CPR, ch = i % CPR;
+      const bf16x8 x = row < rows ? BIo<T>::load8(src + row * D + ch * 8) : bf16x8{};
+      *reinterpret_cast<bf16x8 *>(dst + row * D + ((ch ^ BSwz<D>::f(row)) << 3)) = x;
+    }
+  }
+}
+
 // D_i = dO_i . out_i (fp32 over bf16 products) and lse_i * log2(e), with
 // +inf for a row without a live key (lse = -inf), so that its weights
 // exp2(s - lse2) vanish.
-template <int D>
-__global__ void __launch_bounds__(256) bwd_pre_kernel(const __bf16 *__restrict__ out,
-                                                      const __bf16 *__restrict__ dout,
+template <typename T, int D>
+__global__ void __launch_bounds__(256) bwd_pre_kernel(const T *__restrict__ out,
+                                                      const T *__restrict__ dout,
                                                       const float *__restrict__ lse, int64_t rows,
                                                       float *__restrict__ Dv,
                                                       float *__restrict__ lse2) {
@@ -118,10 +173,11 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const __bf16 *__restrict__
     const int64_t r = r0 + tid / LPR;
     float acc = 0.f;
     if (r < rows) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(out + r * D + sub * 8);
-      const bf16x8 g = *reinterpret_cast<const bf16x8 *>(dout + r * D + sub * 8);
+      float a[8], g[8];
+      BIo<T>::load8f(out + r * D + sub * 8, a);
+      BIo<T>::load8f(dout + r * D + sub * 8, g);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc = fmaf((float)a[i], (float)g[i], acc);
+      for (int i = 0; i < 8; ++i) acc = fmaf(a[i], g[i], acc);
     }
 #pragma unroll
     for (int o = LPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
@@ -173,14 +229,14 @@ __device__ __forceinline__ Weight weight(float s, float scale_log2, float l2, co
   return Weight{fast_exp2(fmaf(s, scale_log2, -l2)), slope};
 }
 
-template <int BS, int D, bool MASK>
+template <int BS, int D, typename T, bool MASK>
 __global__ void __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2)))
-bwd_dq_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
-              const __bf16 *__restrict__ v, const __bf16 *__restrict__ dout,
+bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
+              const T *__restrict__ v, const T *__restrict__ dout,
               const float *__restrict__ lse2, const float *__restrict__ Dv,
               const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
               const int32_t *__restrict__ row_order, int32_t B, int32_t H, int32_t Mb, int32_t Nb,
-              float scale_log2, float scale, const FwdOptions opt, __bf16 *__restrict__ dq) {
+              float scale_log2, float scale, const FwdOptions opt, T *__restrict__ dq) {
   constexpr int NW = BS / 32;
   constexpr int TILE = BS * D;
   constexpr int QC = D / 16;
@@ -211,8 +267,8 @@ bwd_dq_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   const int64_t bh = (int64_t)b * H + h;
   const int64_t Sq = opt.sq, Sk = opt.sk;
   const int64_t bkv = (int64_t)b * (H / opt.kv_group) + h / opt.kv_group;
-  const __bf16 *kh = k + bkv * Sk * D;
-  const __bf16 *vh = v + bkv * Sk * D;
+  const T *kh = k + bkv * Sk * D;
+  const T *vh = v + bkv * Sk * D;
   const int qrow = 32 * wid + l32;            // query row inside the block
   const int64_t i_row = (int64_t)m * BS + qrow;
   const bool q_ok = !MASK || i_row < Sq;     // rows past a cut last block
@@ -223,10 +279,8 @@ bwd_dq_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   bf16x8 qf[QC], gf[QC];
 #pragma unroll
   for (int c = 0; c < QC; ++c) {
-    qf[c] = q_ok ? *reinterpret_cast<const bf16x8 *>(q + (bh * Sq + i_row) * D + 16 * c + 8 * h2)
-                 : bf16x8{};
-    gf[c] = q_ok ? *reinterpret_cast<const bf16x8 *>(dout + (bh * Sq + i_row) * D + 16 * c + 8 * h2)
-                 : bf16x8{};
+    qf[c] = q_ok ? BIo<T>::load8(q + (bh * Sq + i_row) * D + 16 * c + 8 * h2) : bf16x8{};
+    gf[c] = q_ok ? BIo<T>::load8(dout + (bh * Sq + i_row) * D + 16 * c + 8 * h2) : bf16x8{};
   }
   f32x16 acc[DT];
 #pragma unroll
@@ -243,8 +297,8 @@ bwd_dq_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     if (MASK && opt.causal && ncol > m) continue;   // every key after every query
     __syncthreads();                                // previous tile fully read
     const int kv = MASK ? (int)min((int64_t)BS, Sk - (int64_t)ncol * BS) : BS;  // keys that exist
-    copy_tile<BS, D, NW>(kh + (int64_t)ncol * TILE, Ks, wid, lane, (uint32_t)(kv * D * 2));
-    copy_tile<BS, D, NW>(vh + (int64_t)ncol * TILE, Vs, wid, lane, (uint32_t)(kv * D * 2));
+    stage_tile<BS, D, NW, T>(kh + (int64_t)ncol * TILE, Ks, wid, lane, kv);
+    stage_tile<BS, D, NW, T>(vh + (int64_t)ncol * TILE, Vs, wid, lane, kv);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const bool diag = MASK && opt.causal && ncol == m;
@@ -281,24 +335,25 @@ bwd_dq_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     }
   }
   if (!q_ok) return;
-  __bf16 *dqh = dq + (bh * Sq + i_row) * D;
+  T *dqh = dq + (bh * Sq + i_row) * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int a = 0; a < 4; ++a)
-      store4_bf16(dqh + 32 * dt + 8 * a + 4 * h2, scale * acc[dt][4 * a], scale * acc[dt][4 * a + 1],
-                  scale * acc[dt][4 * a + 2], scale * acc[dt][4 * a + 3]);
+      BIo<T>::store4(dqh + 32 * dt + 8 * a + 4 * h2, scale * acc[dt][4 * a],
+                     scale * acc[dt][4 * a + 1], scale * acc[dt][4 * a + 2],
+                     scale * acc[dt][4 * a + 3]);
 }
 
-template <int BS, int D, bool MASK>
+template <int BS, int D, typename T, bool MASK>
 __global__ void __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2)))
-bwd_dkdv_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
-                const __bf16 *__restrict__ v, const __bf16 *__restrict__ dout,
+bwd_dkdv_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                const T *__restrict__ v, const T *__restrict__ dout,
                 const float *__restrict__ lse2, const float *__restrict__ Dv,
                 const int32_t *__restrict__ col_ptr, const int32_t *__restrict__ row_idx,
                 const int32_t *__restrict__ col_order, int32_t B, int32_t H, int32_t Hkv,
                 int32_t Mb, int32_t Nb, float scale_log2, float scale, const FwdOptions opt,
-                __bf16 *__restrict__ dk, __bf16 *__restrict__ dv) {
+                T *__restrict__ dk, T *__restrict__ dv) {
   constexpr int NW = BS / 32;
   constexpr int TILE = BS * D;
   constexpr int QC = D / 16;
@@ -338,10 +393,8 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   bf16x8 kf[QC], vf[QC];
 #pragma unroll
   for (int c = 0; c < QC; ++c) {
-    kf[c] = k_ok ? *reinterpret_cast<const bf16x8 *>(k + (bkv * Sk + j_row) * D + 16 * c + 8 * h2)
-                 : bf16x8{};
-    vf[c] = k_ok ? *reinterpret_cast<const bf16x8 *>(v + (bkv * Sk + j_row) * D + 16 * c + 8 * h2)
-                 : bf16x8{};
+    kf[c] = k_ok ? BIo<T>::load8(k + (bkv * Sk + j_row) * D + 16 * c + 8 * h2) : bf16x8{};
+    vf[c] = k_ok ? BIo<T>::load8(v + (bkv * Sk + j_row) * D + 16 * c + 8 * h2) : bf16x8{};
   }
   f32x16 ak[DT], av[DT];
 #pragma unroll
@@ -366,9 +419,8 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
       if (MASK && opt.causal && m < n) continue;    // every key after every query
       __syncthreads();                              // previous tile fully read
       const int qv = MASK ? (int)min((int64_t)BS, Sq - (int64_t)m * BS) : BS;  // rows that exist
-      copy_tile<BS, D, NW>(q + (bh * Sq + (int64_t)m * BS) * D, Qs, wid, lane, (uint32_t)(qv * D * 2));
-      copy_tile<BS, D, NW>(dout + (bh * Sq + (int64_t)m * BS) * D, Gs, wid, lane,
-                           (uint32_t)(qv * D * 2));
+      stage_tile<BS, D, NW, T>(q + (bh * Sq + (int64_t)m * BS) * D, Qs, wid, lane, qv);
+      stage_tile<BS, D, NW, T>(dout + (bh * Sq + (int64_t)m * BS) * D, Gs, wid, lane, qv);
       if (tid < BS) {
         // rows past a cut last block: weight exp2(s - inf) = 0
         Ls[tid] = tid < qv ? lse2[bh * Sq + (int64_t)m * BS + tid] : __builtin_inff();
@@ -455,54 +507,55 @@ bwd_dkdv_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     }
   }
   if (!k_ok) return;
-  __bf16 *dkr = dk + (bkv * Sk + j_row) * D;
-  __bf16 *dvr = dv + (bkv * Sk + j_row) * D;
+  T *dkr = dk + (bkv * Sk + j_row) * D;
+  T *dvr = dv + (bkv * Sk + j_row) * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      store4_bf16(dkr + 32 * dt + 8 * a + 4 * h2, scale * ak[dt][4 * a], scale * ak[dt][4 * a + 1],
-                  scale * ak[dt][4 * a + 2], scale * ak[dt][4 * a + 3]);
-      store4_bf16(dvr + 32 * dt + 8 * a + 4 * h2, av[dt][4 * a], av[dt][4 * a + 1],
-                  av[dt][4 * a + 2], av[dt][4 * a + 3]);
+      BIo<T>::store4(dkr + 32 * dt + 8 * a + 4 * h2, scale * ak[dt][4 * a],
+                     scale * ak[dt][4 * a + 1], scale * ak[dt][4 * a + 2],
+                     scale * ak[dt][4 * a + 3]);
+      BIo<T>::store4(dvr + 32 * dt + 8 * a + 4 * h2, av[dt][4 * a], av[dt][4 * a + 1],
+                     av[dt][4 * a + 2], av[dt][4 * a + 3]);
     }
 }
 
-template <int BS, int D, bool MASK>
+template <int BS, int D, typename T, bool MASK>
 hipError_t launch_grads(const BwdArgs &a, hipStream_t stream) {
   const float scale_log2 = a.scale * kLog2e;
   {
     const int64_t W = (int64_t)a.B * a.H * a.Mb;
     const int64_t grid = (W + 7) / 8 * 8;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dq_kernel<BS, D, MASK>), dim3((unsigned)grid), dim3(BS * 2), 0, stream,
-                       (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v,
-                       (const __bf16 *)a.dout, a.lse2, a.Dv, a.row_ptr, a.col_idx, a.row_order,
-                       a.B, a.H, a.Mb, a.Nb, scale_log2, a.scale, a.opt, (__bf16 *)a.dq);
+    hipLaunchKernelGGL((bwd_dq_kernel<BS, D, T, MASK>), dim3((unsigned)grid), dim3(BS * 2), 0, stream,
+                       (const T *)a.q, (const T *)a.k, (const T *)a.v,
+                       (const T *)a.dout, a.lse2, a.Dv, a.row_ptr, a.col_idx, a.row_order,
+                       a.B, a.H, a.Mb, a.Nb, scale_log2, a.scale, a.opt, (T *)a.dq);
   }
   {
     const int32_t Hkv = a.H / a.opt.kv_group;
     const int64_t W = (int64_t)a.B * Hkv * a.Nb;
     const int64_t grid = (W + 7) / 8 * 8;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<BS, D, MASK>), dim3((unsigned)grid), dim3(BS * 2), 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<BS, D, T, MASK>), dim3((unsigned)grid), dim3(BS * 2), 0,
                        stream,
-                       (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v,
-                       (const __bf16 *)a.dout, a.lse2, a.Dv, a.col_ptr, a.row_idx, a.col_order,
-                       a.B, a.H, Hkv, a.Mb, a.Nb, scale_log2, a.scale, a.opt, (__bf16 *)a.dk,
-                       (__bf16 *)a.dv);
+                       (const T *)a.q, (const T *)a.k, (const T *)a.v,
+                       (const T *)a.dout, a.lse2, a.Dv, a.col_ptr, a.row_idx, a.col_order,
+                       a.B, a.H, Hkv, a.Mb, a.Nb, scale_log2, a.scale, a.opt, (T *)a.dk,
+                       (T *)a.dv);
   }
   return hipGetLastError();
 }
 
-template <int D>
+template <typename T, int D>
 hipError_t launch_pre(const BwdArgs &a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.H * a.opt.sq;
   const int64_t rpb = 256 / (D / 8);
   int64_t grid = (rows + rpb - 1) / rpb;
   if (grid > 65536) grid = 65536;
-  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)grid), dim3(256), 0, stream,
-                     (const __bf16 *)a.out, (const __bf16 *)a.dout, a.lse, rows, a.Dv, a.lse2);
+  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, stream,
+                     (const T *)a.out, (const T *)a.dout, a.lse, rows, a.Dv, a.lse2);
   return hipGetLastError();
 }
 
@@ -515,15 +568,24 @@ bool backward_supported(int32_t bs, int32_t d) {
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
   if (!backward_supported(a.bs, a.d)) return hipErrorInvalidValue;
   if (a.opt.kv_group < 1 || a.H % a.opt.kv_group != 0) return hipErrorInvalidValue;
-  hipError_t e = a.d == 32 ? launch_pre<32>(a, stream)
-               : a.d == 64 ? launch_pre<64>(a, stream)
-                           : launch_pre<128>(a, stream);
+  hipError_t e;
+  if (a.f32)
+    e = a.d == 32 ? launch_pre<float, 32>(a, stream)
+      : a.d == 64 ? launch_pre<float, 64>(a, stream)
+                  : launch_pre<float, 128>(a, stream);
+  else
+    e = a.d == 32 ? launch_pre<__bf16, 32>(a, stream)
+      : a.d == 64 ? launch_pre<__bf16, 64>(a, stream)
+                  : launch_pre<__bf16, 128>(a, stream);
   if (e != hipSuccess) return e;
   const bool mask = a.opt.cap_k != 0.f || a.opt.causal != 0 || a.opt.sq % a.bs != 0 ||
                     a.opt.sk % a.bs != 0 || a.opt.qseg != nullptr;
 #define BSA_BWD_CASE(BS_, D_)                                                                  \
-  if (a.bs == BS_ && a.d == D_) e = mask ? launch_grads<BS_, D_, true>(a, stream)             \
-                                         : launch_grads<BS_, D_, false>(a, stream);
+  if (a.bs == BS_ && a.d == D_)                                                               \
+    e = a.f32 ? (mask ? launch_grads<BS_, D_, float, true>(a, stream)                         \
+                      : launch_grads<BS_, D_, float, false>(a, stream))                       \
+              : (mask ? launch_grads<BS_, D_, __bf16, true>(a, stream)                        \
+                      : launch_grads<BS_, D_, __bf16, false>(a, stream));
   BSA_BWD_CASE(32, 32) BSA_BWD_CASE(32, 64) BSA_BWD_CASE(32, 128)
   BSA_BWD_CASE(64, 32) BSA_BWD_CASE(64, 64) BSA_BWD_CASE(64, 128)
   BSA_BWD_CASE(128, 32) BSA_BWD_CASE(128, 64) BSA_BWD_CASE(128, 128)

@@ -58,6 +58,7 @@ struct BwdArgs {
   const int32_t *row_ptr, *col_idx, *row_order;        // row plan
   const int32_t *col_ptr, *row_idx, *col_order;        // column plan
   int32_t B, H, Mb, Nb, bs, d;
+  bool f32;                                            // fp32 I/O (bf16 products)
   float scale;
   FwdOptions opt;
   float *Dv, *lse2;                                    // workspace, B*H*Mb*bs floats each

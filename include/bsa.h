@@ -231,20 +231,22 @@ size_t bsa_backward_workspace_bytes(int32_t B, int32_t H, int32_t Sq);
  *
  *   q, k, v, plan, B, H, Sq, Sk, bs, d, scale, opts: exactly as passed to
  *         the forward that produced out and lse (same options)
- *   out   device [B, H, Sq, d] bf16, the forward's output
- *   dout  device [B, H, Sq, d] bf16, upstream gradient
+ *   out   device [B, H, Sq, d] of dtype, the forward's output
+ *   dout  device [B, H, Sq, d] of dtype, upstream gradient
  *   lse   device fp32 [B, H, Sq], the forward's lse (required)
  *   plan_cols  host pointer to a column plan of the same layout with
  *         Hkv = the K/V head count (BSA_ERR_PLAN_MISMATCH otherwise)
  *   workspace  device, caller-owned, >= bsa_backward_workspace_bytes,
  *         16-byte aligned; overwritten (holds D and lse * log2 e)
- *   dq    device [B, H, Sq, d] bf16, written
- *   dk, dv  device [B, Hkv, Sk, d] bf16, written (every row)
+ *   dq    device [B, H, Sq, d] of dtype, written
+ *   dk, dv  device [B, Hkv, Sk, d] of dtype, written (every row)
  *   dsink device fp32 [H], written when opts->attn_sink is set; may be NULL
- * Supported: dtype BSA_BF16, bs in {32, 64, 128}, d in {32, 64, 128}.
+ * Supported: dtype BSA_BF16 or BSA_F32 (fp32 tiles are rounded to bf16 on
+ * load, as in the forward; products accumulate in fp32), bs in {32, 64, 128},
+ * d in {32, 64, 128}.
  * Deterministic: no atomics, so repeated calls give identical bits.
- * Errors: as bsa_forward_ex, plus BSA_ERR_UNSUPPORTED for BSA_F32 or
- * bs = 16, BSA_ERR_BUFFER_TOO_SMALL for a short workspace.
+ * Errors: as bsa_forward_ex, plus BSA_ERR_UNSUPPORTED for bs = 16,
+ * BSA_ERR_BUFFER_TOO_SMALL for a short workspace.
  */
 int bsa_backward(const void *q, const void *k, const void *v, const void *out, const void *dout,
                  const float *lse, const bsa_plan_t *plan, const bsa_plan_cols_t *plan_cols,

@@ -160,7 +160,7 @@ def test_topk_validation(lib):
     assert call(N=-1) == INVALID
     assert call(scale=float("inf")) == INVALID
     assert call(H=65) == UNSUPPORTED
-    assert call(d=256) == UNSUPPORTED
+    assert call(d=192) == UNSUPPORTED
     assert call(kv=ctypes.c_void_p(0x10004)) == MISALIGNED
     assert call(sink=ctypes.c_void_p(0x10001)) == MISALIGNED
 

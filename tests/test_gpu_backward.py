@@ -167,3 +167,40 @@ def test_backward_full_workload(gpu):
                  np.concatenate([rk[b, j, n * bs:(n + 1) * bs] for b, j, n in cols]), "dk full")
     compare_grad(np.concatenate([to64(dv[b, j, n * bs:(n + 1) * bs]) for b, j, n in cols]),
                  np.concatenate([rv[b, j, n * bs:(n + 1) * bs] for b, j, n in cols]), "dv full")
+
+
+@pytest.mark.parametrize("opt_name", ["plain", "all"])
+@pytest.mark.parametrize("bs,d,Sq,Sk", [(32, 32, 160, 224), (64, 128, 320, 256),
+                                        (128, 64, 256, 384), (64, 64, 250, 190)])
+def test_backward_f32(gpu, bs, d, Sq, Sk, opt_name):
+    """fp32 I/O: tiles are rounded to bf16 on load (as in the forward) and the
+    gradients come back in fp32; compared with the oracle's gradients at the
+    fp32 inputs, cut last blocks included."""
+    opts = OPTION_SETS[opt_name]
+    H, B = 4, 2
+    Hkv = opts.get("Hkv", H)
+    Mb, Nb = -(-Sq // bs), -(-Sk // bs)
+    rng = np.random.default_rng(bs + d + Sq)
+    lay = (rng.random((H, Mb, Nb)) < 0.5).astype(np.int32)
+    lay[:, :, 0] = 1
+    x = W.make_bsa("bwd_f32", B=B, H=H, S=Sq, Sk=Sk, bs=bs, d=d, dtype="f32", layout="given",
+                   layout_array=lay, seed=Sq + Sk, Hkv=Hkv, sink_mean=opts.get("sink_mean"))
+    dout = torch.from_numpy(np.random.default_rng(Sq).standard_normal(x.q.shape).astype(np.float32))
+    say(f"[backward] f32 {opt_name} bs={bs} d={d} Sq={Sq} Sk={Sk}")
+    plan, _ = check_plan(gpu, lay)
+    pc = check_plan_cols(gpu, lay, Hkv)
+    q, k, v = (t.to(gpu) for t in (x.q, x.k, x.v))
+    sink = x.sink.to(gpu) if x.sink is not None else None
+    kw = dict(attn_sink=sink, soft_cap=opts.get("soft_cap"), causal=opts.get("causal", False),
+              bs=bs)
+    out, lse = bsa.bsa_forward(q, k, v, plan, x.scale, **kw)
+    dq, dk, dv, dsink = bsa.bsa_backward(q, k, v, out, dout.to(gpu), lse, plan, pc, x.scale, **kw)
+    torch.cuda.synchronize()
+    assert dq.dtype == torch.float32 and dk.dtype == torch.float32
+    sk64 = None if x.sink is None else x.sink.numpy().astype(np.float64)
+    rq, rk, rv, rs = O.attention_backward_dense(
+        to64(x.q), to64(x.k), to64(x.v), to64(dout), lay, bs, x.scale, sink=sk64,
+        soft_cap=opts.get("soft_cap"), causal=opts.get("causal", False))
+    compare_grad(to64(dq), rq, f"dq f32 {opt_name} bs={bs} d={d}")
+    compare_grad(to64(dk), rk, f"dk f32 {opt_name} bs={bs} d={d}")
+    compare_grad(to64(dv), rv, f"dv f32 {opt_name} bs={bs} d={d}")
