@@ -25,7 +25,12 @@ its FLOPs counted as the 10*b^2*d per live tile of the five tile products a
 backward needs (the kernels execute 14: S and dP are recomputed once more).
 Last, the content-adaptive layout producer runs on the same q and k (block
 means, cosine scores, threshold) under kernels.bsa_layout_adaptive, reported
-against HBM bandwidth for the q and k bytes it must read.
+against HBM bandwidth for the q and k bytes it must read.  Then two more
+forms of the hot path on the same inputs: the forward over packed sequences
+(segment ids, sequence lengths uniform in [1024, 8192]; it runs the
+register-staged kernel) under kernels.bsa_forward_segments, and the top-k
+kernel at head size 256 (same indices and sink, fresh q and kv) under
+kernels.topk_sparse_attn_d256.
 
 Flags: --gpus N (only 1 is supported), --steps K, --warmup W,
 --no-cpu-baseline (skip the oracle timing), --cpu-seconds S (oracle sample
@@ -33,7 +38,8 @@ budget per kernel), --copy-calibration (also run one plain elementwise copy
 of 1 GiB, for HBM counter scaling under a profiler), --option-steps N (launches
 of the forward with options; 0 skips that leg), --backward-steps N (calls of
 the backward; 0 skips that leg), --adaptive-steps N (calls of the adaptive
-layout producer; 0 skips that leg).
+layout producer; 0 skips that leg), --variant-steps N (calls of each of the two
+forms above; 0 skips them).
 
 --summarize-counters FETCH_CSV WRITE_CSV (no GPU needed) turns the counter
 files of two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of
@@ -243,6 +249,7 @@ def main(argv=None) -> int:
     ap.add_argument("--option-steps", type=int, default=20)
     ap.add_argument("--backward-steps", type=int, default=10)
     ap.add_argument("--adaptive-steps", type=int, default=20)
+    ap.add_argument("--variant-steps", type=int, default=10)
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
@@ -393,6 +400,46 @@ def main(argv=None) -> int:
                   "pct_hbm_peak": round(100 * ad_gbs / PEAK_HBM_GBS, 2)}
         log(f"[bench] adaptive layout: {t_ad:.4f} ms")
 
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    seg_leg = d256_leg = None
+    if args.variant_steps > 0:
+        seg = W.packed_segment_ids(B, S, 1024, 8192, seed=7).to(dev)
+        plan = bsa.bsa_plan(layout, buf=pbuf)
+        t_seg = timed(lambda: bsa.bsa_forward(q, k, v, plan, fwd.scale, out=out, lse=lse,
+                                              q_segment_ids=seg, kv_segment_ids=seg),
+                      args.variant_steps)
+        seg_tf = f_flops / (t_seg * 1e-3) / 1e12
+        seg_leg = {"avg_ms": round(t_seg, 5), "calls": args.variant_steps,
+                   "segments": "packed, lengths uniform in [1024, 8192]",
+                   "tflops": round(seg_tf, 2),
+                   "pct_bf16_peak": round(100 * seg_tf / PEAK_BF16_TFLOPS, 2)}
+        log(f"[bench] forward with segment ids: {t_seg:.4f} ms")
+        rng = np.random.default_rng(8)
+        q256 = torch.from_numpy(rng.standard_normal((Bq, M, Hq, 256), dtype=np.float32)).to(
+            torch.bfloat16).to(dev)
+        kv256 = torch.from_numpy(rng.standard_normal((Bq, int(tk.kv.shape[1]), 256),
+                                                     dtype=np.float32)).to(torch.bfloat16).to(dev)
+        o256 = torch.empty_like(q256)
+        t_256 = timed(lambda: bsa.topk_sparse_attn(q256, kv256, tidx, tsink, 1.0 / 16.0, out=o256),
+                      args.variant_steps)
+        _, f256, b256 = topk_counts(tk.idx.numpy(), Hq, 256)
+        d256_leg = {"avg_ms": round(t_256, 5), "calls": args.variant_steps,
+                    "tflops": round(f256 / (t_256 * 1e-3) / 1e12, 2),
+                    "algorithmic_gbs": round(b256 / (t_256 * 1e-3) / 1e9, 1),
+                    "pct_hbm_peak": round(100 * b256 / (t_256 * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+        log(f"[bench] top-k at d 256: {t_256:.4f} ms")
+
     if args.copy_calibration:
         # one full-grid elementwise kernel that reads 1 GiB and writes 1 GiB
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -424,6 +471,10 @@ def main(argv=None) -> int:
         kernels["bsa_backward"] = bwd_leg
     if ad_leg is not None:
         kernels["bsa_layout_adaptive"] = ad_leg
+    if seg_leg is not None:
+        kernels["bsa_forward_segments"] = seg_leg
+    if d256_leg is not None:
+        kernels["topk_sparse_attn_d256"] = d256_leg
     # dominant kernel of the step and its roofline
     if t_fwd >= t_topk:
         roof = {"kernel": "bsa_forward", "bound": "mfma", "achieved": round(fwd_tflops, 2),

@@ -331,6 +331,8 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
 
   // one LDS block: two K tiles, then two V tiles; reused as merge scratch
   __shared__ __attribute__((aligned(16))) __bf16 smem[2 * BS * (KSTR + VSTR)];
+  // segment ids of the two K tiles' keys (MASK instances with segment ids)
+  __shared__ __attribute__((aligned(16))) int32_t kseg_s[MASK ? 2 * BS : 4];
   __bf16 *const Kbuf0 = smem;
   __bf16 *const Vbuf0 = smem + 2 * BS * KSTR;
 
@@ -385,6 +387,7 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
   bf16x8 kr[CPT], vr[CPT];
   // (MASK instances: rows past a cut last block load zeros)
   auto kval_of = [&](int n) { return MASK ? (int)min((int64_t)BS, Sk - (int64_t)n * BS) : BS; };
+  int ksr = 0;   // staged segment id of key `tid` of the next K tile
   auto load_k = [&](int n) {
     const T *src = kh + (int64_t)n * BS * D;
     const int kval = kval_of(n);
@@ -394,6 +397,8 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
       kr[c] = (!MASK || qid / (D / 8) < kval)
                   ? Io<T>::load8(src + (qid / (D / 8)) * D + (qid % (D / 8)) * 8) : bf16x8{};
     }
+    if (MASK && opt.qseg && tid < BS)
+      ksr = tid < kval ? opt.kseg[(int64_t)b * Sk + (int64_t)n * BS + tid] : 0;
   };
   auto load_v = [&](int n) {
     const T *src = vh + (int64_t)n * BS * D;
@@ -412,6 +417,7 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
       const int qid = c * NT + tid;
       *reinterpret_cast<bf16x8 *>(&dst[(qid / (D / 8)) * KSTR + (qid % (D / 8)) * 8]) = kr[c];
     }
+    if (MASK && opt.qseg && tid < BS) kseg_s[buf * BS + tid] = ksr;
   };
   auto store_v = [&](int buf) {
     __bf16 *dst = Vbuf0 + buf * BS * VSTR;
@@ -444,7 +450,7 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
   // Options on a fresh score tile of column ncol (MASK instances only): tanh
   // logit cap, then the causal mask when the tile reaches past the diagonal
   // (key row key0 + 32jt + 8(e/4) + 4h2 + e%4, query row 32rg + l32).
-  auto apply_opts = [&](f32x16 (&s)[JT], int ncol) {
+  auto apply_opts = [&](f32x16 (&s)[JT], int ncol, int buf) {
     if constexpr (!MASK) return;
     if (opt.cap_k != 0.f) {
 #pragma unroll
@@ -468,14 +474,16 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
         for (int e = 0; e < 16; ++e)
           if (32 * jt + 8 * (e / 4) + (e % 4) >= kv) s[jt][e] = -__builtin_inff();
     }
-    if (opt.qseg) {  // packed sequences: only keys of the query's segment
-      const int64_t k0 = (int64_t)ncol * BS + key0 + 4 * h2;
+    if (opt.qseg) {  // packed sequences: only keys of the query's segment (ids staged in LDS)
+      const int32_t *kst = kseg_s + buf * BS + key0 + 4 * h2;
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t key = k0 + 32 * jt + 8 * (e / 4) + (e % 4);
-          if (key < Sk && opt.kseg[(int64_t)b * Sk + key] != qsg) s[jt][e] = -__builtin_inff();
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const i32x4 ids = *reinterpret_cast<const i32x4 *>(kst + 32 * jt + 8 * a4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (ids[i] != qsg) s[jt][4 * a4 + i] = -__builtin_inff();
         }
     }
   };
@@ -552,7 +560,7 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
   }
   __syncthreads();
   qk(0, s_cur);
-  apply_opts(s_cur, cols[0]);
+  apply_opts(s_cur, cols[0], 0);
   if (n > 2) load_k(cols[2]);
   if (n > 1) load_v(cols[1]);
   // Steady state without branches: staging of tiles past the end re-loads
@@ -565,7 +573,7 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
     load_k(cols[min(t + 3, n - 1)]);
     load_v(cols[min(t + 2, n - 1)]);
     qk((t + 1) & 1, s_next);
-    apply_opts(s_next, cols[t + 1]);
+    apply_opts(s_next, cols[t + 1], (t + 1) & 1);
     softmax_pv(s_cur, t & 1);
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt) s_cur[jt] = s_next[jt];
@@ -693,7 +701,6 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   float *lh = lse ? lse + bh * Sq : nullptr;
   const int64_t i_row = (int64_t)m * BS + 32 * rg + l32;
   const bool q_ok = !MASK || i_row < Sq;  // rows past a cut last block
-  const int qsg = (MASK && opt.qseg && q_ok) ? opt.qseg[(int64_t)b * Sq + i_row] : 0;
 
   if (beg == end) {
     if (ks == 0 && q_ok) {
@@ -786,16 +793,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
         for (int e = 0; e < 16; ++e)
           if (32 * jt + 8 * (e / 4) + (e % 4) >= kv) s[jt][e] = -__builtin_inff();
     }
-    if (opt.qseg) {  // packed sequences: only keys of the query's segment
-      const int64_t k0 = (int64_t)ncol * BS + key0 + 4 * h2;
-#pragma unroll
-      for (int jt = 0; jt < JT; ++jt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t key = k0 + 32 * jt + 8 * (e / 4) + (e % 4);
-          if (key < Sk && opt.kseg[(int64_t)b * Sk + key] != qsg) s[jt][e] = -__builtin_inff();
-        }
-    }
+    // (calls with segment ids run the register-staged kernel)
   };
 
   float m_run = kMaxFloor;  // running max (log2 units)
@@ -1024,8 +1022,8 @@ hipError_t launch_one(const void *q, const void *k, const void *v, const int32_t
                          (const __bf16 *)v, row_ptr, col_idx, row_order, B, H, Mb, Nb,
                          scale * kLog2e, (__bf16 *)out, lse, opt);
     } else {
-      // segment ids need per-key loads beside the products, which the copy
-      // kernel's fixed-count waits do not allow: use the register-staged one
+      // segment ids are staged beside each K tile by the register-staged
+      // kernel; the copy kernel's fixed-count waits have no slot for them
       hipLaunchKernelGGL((bsa_fwd32_kernel<BS, D, T, 2, MASK>), dim3((unsigned)grid),
                          dim3(BS * 4), 0, stream, (const T *)q, (const T *)k, (const T *)v,
                          row_ptr, col_idx, row_order, B, H, Mb, Nb, scale * kLog2e, (T *)out, lse,
