@@ -30,7 +30,12 @@ forms of the hot path on the same inputs: the forward over packed sequences
 (segment ids, sequence lengths uniform in [1024, 8192]; it runs the
 register-staged kernel) under kernels.bsa_forward_segments, and the top-k
 kernel at head size 256 (same indices and sink, fresh q and kv) under
-kernels.topk_sparse_attn_d256.
+kernels.topk_sparse_attn_d256.  Last, the second block-sparse workload
+(causal local + global + strided, B2 H16 S16384 bs64 d128) is planned and
+its forward timed warm, under kernels.bsa_forward_lgs, and both block-sparse
+workloads are timed cold: before each timed launch a 1 GiB fill evicts L2
+and the Infinity Cache, and events bracket the forward alone.  Per-launch
+times of the step's kernels give p10 / median / p90 beside the averages.
 
 Flags: --gpus N (only 1 is supported), --steps K, --warmup W,
 --no-cpu-baseline (skip the oracle timing), --cpu-seconds S (oracle sample
@@ -39,7 +44,8 @@ of 1 GiB, for HBM counter scaling under a profiler), --option-steps N (launches
 of the forward with options; 0 skips that leg), --backward-steps N (calls of
 the backward; 0 skips that leg), --adaptive-steps N (calls of the adaptive
 layout producer; 0 skips that leg), --variant-steps N (calls of each of the two
-forms above; 0 skips them).
+forms above; 0 skips them), --config-steps N (launches of the second workload
+and of each cold-cache leg; 0 skips them).
 
 --summarize-counters FETCH_CSV WRITE_CSV (no GPU needed) turns the counter
 files of two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of
@@ -61,6 +67,8 @@ import numpy as np
 
 REPO = os.path.dirname(os.path.abspath(__file__))
 FWD_WORKLOAD = "causal_bernoulli_h32_s32768_bs128_d128"
+LGS_WORKLOAD = "causal_lgs_b2_h16_s16384_bs64_d128"
+FLUSH_BYTES = 1 << 30          # > the 256 MB Infinity Cache and 8 x 4 MB of L2
 TOPK_WORKLOAD = "topk2048_m4096_h64_d512_n8192"
 METRIC = "effective TFLOP/s on live tiles and % of bf16 MFMA peak, 1×MI355X"
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA, TFLOP/s
@@ -71,6 +79,7 @@ KERNEL_SOURCES = {
     "topk_sparse_attn": os.path.join(REPO, "block_sparse_attention_plan_amd", "csrc", "topk.hip"),
 }
 KERNEL_SOURCES["bsa_forward_options"] = KERNEL_SOURCES["bsa_forward"]
+KERNEL_SOURCES["bsa_forward_lgs"] = KERNEL_SOURCES["bsa_forward"]
 
 
 def log(*a):
@@ -97,6 +106,14 @@ def measured_traffic(kernel: str):
     if not ent or ent.get("source_sha") != source_hash(KERNEL_SOURCES[kernel]):
         return None
     return ent.get("bytes_per_launch")
+
+
+def percentiles(ms) -> dict:
+    """p10 / median / p90 of per-launch times (ms)."""
+    a = np.asarray(ms, dtype=np.float64)
+    return {"p10_ms": round(float(np.percentile(a, 10)), 5),
+            "median_ms": round(float(np.median(a)), 5),
+            "p90_ms": round(float(np.percentile(a, 90)), 5)}
 
 
 def bsa_counts(layout: np.ndarray, B: int, bs: int, d: int, elem: int = 2):
@@ -180,12 +197,14 @@ def cpu_baseline(fwd, topk_in, budget_s: float):
 
 
 CALIBRATION_BYTES = float(1 << 30)   # read and written by the calibration copy
-# Kernel-name tests; the forward's plain instances carry template argument
-# `false` (mangled Lb0E) for its options flag, the instances with options `true`.
+# Kernel-name tests on mangled names: the copy-staged forward for bs 128, d 128
+# (2 waves per key split) with its options flag `false` (Lb0E) or `true` (Lb1E),
+# the same for bs 64, and the d-512 top-k instance.
 KERNEL_MATCH = {
-    "bsa_forward": lambda n: "bsa_fwd" in n and "Lb0E" in n,
-    "bsa_forward_options": lambda n: "bsa_fwd" in n and "Lb1E" in n,
-    "topk_sparse_attn": lambda n: "topk_kernel" in n,
+    "bsa_forward": lambda n: "bsa_fwd_dma_kernelILi128ELi128ELi2ELb0EE" in n,
+    "bsa_forward_options": lambda n: "bsa_fwd_dma_kernelILi128ELi128ELi2ELb1EE" in n,
+    "bsa_forward_lgs": lambda n: "bsa_fwd_dma_kernelILi64ELi128ELi2ELb0EE" in n,
+    "topk_sparse_attn": lambda n: "topk_kernel" in n and ("<512>" in n or "ILi512EE" in n),
 }
 
 
@@ -250,6 +269,7 @@ def main(argv=None) -> int:
     ap.add_argument("--backward-steps", type=int, default=10)
     ap.add_argument("--adaptive-steps", type=int, default=20)
     ap.add_argument("--variant-steps", type=int, default=10)
+    ap.add_argument("--config-steps", type=int, default=10)
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
@@ -317,6 +337,8 @@ def main(argv=None) -> int:
     t_fwd = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
     t_topk = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
     t_step_ev = sum(e[0].elapsed_time(e[3]) for e in events) / args.steps
+    pct_fwd = percentiles([e[1].elapsed_time(e[2]) for e in events])
+    pct_topk = percentiles([e[2].elapsed_time(e[3]) for e in events])
     ms_per_step = wall * 1e3 / args.steps
 
     opt_leg = None
@@ -440,6 +462,68 @@ def main(argv=None) -> int:
                     "pct_hbm_peak": round(100 * b256 / (t_256 * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
         log(f"[bench] top-k at d 256: {t_256:.4f} ms")
 
+    def timed_cold(fn, n, flush):
+        """Per-launch ms of fn with L2 and the Infinity Cache evicted before each."""
+        fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            flush.zero_()
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    lgs_leg = cold_legs = None
+    if args.config_steps > 0:
+        flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        plan = bsa.bsa_plan(layout, buf=pbuf)
+        c4 = timed_cold(lambda: bsa.bsa_forward(q, k, v, plan, fwd.scale, out=out, lse=lse),
+                        args.config_steps, flush)
+        log(f"[bench] drawing {LGS_WORKLOAD}")
+        lw = W.make_workload(LGS_WORKLOAD)
+        lB, lH, lS, ld = (int(x) for x in lw.q.shape)
+        l_tiles, l_flops, l_bytes = bsa_counts(lw.layout, lB, lw.bs, ld)
+        l_layout = torch.from_numpy(lw.layout).to(dev)
+        lq, lk, lv = (t.to(dev) for t in (lw.q, lw.k, lw.v))
+        l_out = torch.empty_like(lq)
+        l_lse = torch.empty((lB, lH, lS), dtype=torch.float32, device=dev)
+        l_plan = bsa.bsa_plan(l_layout)
+        fn = lambda: bsa.bsa_forward(lq, lk, lv, l_plan, lw.scale, out=l_out, lse=l_lse)  # noqa: E731
+        for _ in range(3):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.config_steps)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        warm = [a.elapsed_time(b) for a, b in ev]
+        c3 = timed_cold(fn, args.config_steps, flush)
+        del flush
+        t_l = sum(warm) / len(warm)
+        l_tf = l_flops / (t_l * 1e-3) / 1e12
+        lgs_leg = {"workload": LGS_WORKLOAD, "avg_ms": round(t_l, 5), **percentiles(warm),
+                   "launches": args.config_steps, "live_tiles": l_tiles, "flops": l_flops,
+                   "tflops": round(l_tf, 2), "pct_bf16_peak": round(100 * l_tf / PEAK_BF16_TFLOPS, 2),
+                   "algorithmic_bytes": l_bytes,
+                   "algorithmic_gbs": round(l_bytes / (t_l * 1e-3) / 1e9, 1),
+                   "traffic": measured_traffic("bsa_forward_lgs")}
+        log(f"[bench] {LGS_WORKLOAD} forward: {t_l:.4f} ms")
+        cold_legs = {}
+        for name, ms, fl in ((FWD_WORKLOAD, c4, f_flops), (LGS_WORKLOAD, c3, l_flops)):
+            t_c = sum(ms) / len(ms)
+            cold_legs[name] = {"avg_ms": round(t_c, 5), **percentiles(ms), "launches": len(ms),
+                               "tflops": round(fl / (t_c * 1e-3) / 1e12, 2),
+                               "pct_bf16_peak": round(100 * fl / (t_c * 1e-3) / 1e12
+                                                      / PEAK_BF16_TFLOPS, 2),
+                               "flush": "1 GiB fill before each launch"}
+            log(f"[bench] {name} forward, cold caches: {t_c:.4f} ms")
+
     if args.copy_calibration:
         # one full-grid elementwise kernel that reads 1 GiB and writes 1 GiB
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -456,11 +540,11 @@ def main(argv=None) -> int:
     kernels = {
         "bsa_plan": {"avg_ms": round(t_plan, 5)},
         "bsa_forward": {
-            "avg_ms": round(t_fwd, 5), "live_tiles": tiles, "flops": f_flops,
+            "avg_ms": round(t_fwd, 5), **pct_fwd, "live_tiles": tiles, "flops": f_flops,
             "tflops": round(fwd_tflops, 2), "pct_bf16_peak": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
             "algorithmic_bytes": f_bytes, "algorithmic_gbs": round(fwd_gbs, 1)},
         "topk_sparse_attn": {
-            "avg_ms": round(t_topk, 5), "valid_indices": valid, "flops": t_flops,
+            "avg_ms": round(t_topk, 5), **pct_topk, "valid_indices": valid, "flops": t_flops,
             "tflops": round(topk_tflops, 2), "pct_bf16_peak": round(100 * topk_tflops / PEAK_BF16_TFLOPS, 2),
             "algorithmic_bytes": t_bytes, "algorithmic_gbs": round(topk_gbs, 1),
             "pct_hbm_peak": round(100 * topk_gbs / PEAK_HBM_GBS, 2)},
@@ -475,6 +559,10 @@ def main(argv=None) -> int:
         kernels["bsa_forward_segments"] = seg_leg
     if d256_leg is not None:
         kernels["topk_sparse_attn_d256"] = d256_leg
+    if lgs_leg is not None:
+        kernels["bsa_forward_lgs"] = lgs_leg
+    if cold_legs is not None:
+        kernels["bsa_forward_cold"] = cold_legs
     # dominant kernel of the step and its roofline
     if t_fwd >= t_topk:
         roof = {"kernel": "bsa_forward", "bound": "mfma", "achieved": round(fwd_tflops, 2),
