@@ -389,8 +389,8 @@ int topk_sparse_attn(const void *q, const void *kv, const int32_t *idx, const fl
     return fail(BSA_ERR_MISALIGNED, "topk_sparse_attn: tensors must be 16-byte aligned");
   if ((int64_t)B * M > 0x7fffffffLL)
     return fail(BSA_ERR_UNSUPPORTED, "topk_sparse_attn: problem too large");
-  if ((int64_t)N * d * 2 > 0xffffffffLL)
-    return fail(BSA_ERR_UNSUPPORTED, "topk_sparse_attn: one batch of kv exceeds 4 GiB");
+  if ((int64_t)N * d * 2 > 0xfffffc00LL)  // the kernel's row offsets wrap past this for -1
+    return fail(BSA_ERR_UNSUPPORTED, "topk_sparse_attn: one batch of kv exceeds 4 GiB - 1 KiB");
   hipError_t e = bsa::launch_topk(q, kv, idx, attn_sink, B, M, N, H, d, topk, scale, out,
                                   (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "topk_sparse_attn launch");

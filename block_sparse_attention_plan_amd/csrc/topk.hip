@@ -10,25 +10,30 @@
 // [0, N)) contribute nothing; the running maximum starts at a finite floor so
 // a position without a valid slot produces zeros instead of NaN.
 //
-// Work item = (batch, position); one workgroup of four waves, wave w owning
-// heads 16w .. 16w+15 over all of d.  Slots are processed in chunks of 32
-// whose rows are copied straight from HBM into LDS (at d = 512 one
-// buffer_load_dwordx4 ... lds per 1 KiB row; at d = 128 and 256 one or two
-// buffer_load_dword ... lds of 256 bytes, so that every row keeps its
-// padding; slots without a valid index get a zero row), one chunk ahead into
-// the other of two buffers, so the one gather serves all heads of the
-// position.  The page's kernel takes d as a parameter; d_h = 512 is the size
-// its shapes show.  Every wave computes
-//   S^T = KV Q^T       (16x16x32 MFMA, Q^T resident in registers)
-//   online softmax     (lane owns one head column; the running maximum may
-//                      lag the true one by a bounded amount before the
-//                      accumulator is rescaled)
-//   O^T += KV^T P^T    (16x16x32 MFMA, KV^T by LDS transpose reads)
-// The two buffers (2 x 33 KiB with rows padded by 32 bytes against bank
-// conflicts) let two workgroups share a CU, so each SIMD interleaves the
-// waves of two positions.  The buffers are distinct LDS objects and the
-// chunk loop is unrolled by two, so the compiler never waits for a copy
-// into the buffer it is not reading.
+// Work item = (batch, position); one workgroup of four waves.  Slots are
+// processed in chunks of 32 whose rows are copied straight from HBM into LDS
+// (at d = 512 one buffer_load_dwordx4 ... lds per 1 KiB row; at d = 128 and
+// 256 one or two buffer_load_dword ... lds of 256 bytes, so that every row
+// keeps its padding; a slot without a valid index reads as a zero row), one
+// chunk ahead into the other of two buffers, so the one gather serves all
+// heads of the position.  The page's kernel takes d as a parameter; d_h = 512
+// is the size its shapes show.  Wave w
+//   forms S^T = KV Q^T for heads 16w .. 16w+15 over all of d (16x16x32 MFMA,
+//     Q^T resident in registers) and their online softmax (a lane owns one
+//     head column; the running maximum may lag the true one by a bounded
+//     amount before the output is rescaled), writing the bf16 weights P and
+//     each head's rescale factor to LDS;
+//   after a block barrier, accumulates O^T += KV^T P^T for d columns
+//     w*d/4 .. (w+1)*d/4 - 1 of all 64 heads (32x32x16 MFMA, KV^T by LDS
+//     transpose reads of its quarter of the chunk only).
+// Splitting the output product over d rather than heads transposes each
+// gathered element once per workgroup instead of once per wave; the LDS
+// transpose reads were what bounded the head-split form.  The two chunk
+// buffers (2 x 33 KiB, rows padded by 32 bytes against bank conflicts) plus
+// P (5 KiB) let two workgroups share a CU, so each SIMD interleaves the waves
+// of two positions.  The buffers are distinct LDS objects and the chunk loop
+// is unrolled by two, so the compiler never waits for a copy into the buffer
+// it is not reading.
 #include "bsa_device.h"
 #include "bsa_internal.h"
 
@@ -38,36 +43,47 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMaxFloor = -1e30f;
 constexpr float kLazy = 8.0f;  // tolerated staleness of the running max (log2 units)
-constexpr int kReadAheadS = 6;   // KV row reads issued before the first score MFMA
-constexpr int kReadAheadV = 12;  // KV transpose reads issued before the first PV MFMA
+// KV row reads issued before the first score MFMA
+template <int D> constexpr int kReadAheadS = D == 512 ? 6 : 3;
 
 template <int D>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
             const int32_t *__restrict__ idx, const float *__restrict__ sink, int32_t M,
-            int32_t N, int32_t H, int32_t topk, float scale_log2, __bf16 *__restrict__ out) {
+            int32_t N, int32_t H, int32_t topk, float scale_log2,
+            __bf16 *__restrict__ out) {
   constexpr int T = 32;               // slots per chunk
   constexpr int STR = D + 16;         // LDS row stride (elements)
   constexpr int RPW = T / 4;          // rows gathered per wave per chunk
   constexpr int QC = D / 32;          // 32-wide k steps of S^T
-  constexpr int DT = D / 16;          // 16-wide d tiles of O^T
+  constexpr int DW = D / 4;           // output columns per wave
+  constexpr int DTW = DW / 32;        // 32-wide d tiles per wave
+  constexpr int PSTR = T + 8;         // row stride of P (elements per head)
   static_assert(D == 512 || D == 256 || D == 128, "row copies: one 1 KiB or D/128 256-byte pieces");
+  static_assert(DTW >= 1, "each wave owns at least one 32-wide d tile");
 
   __shared__ __attribute__((aligned(16))) __bf16 C0[T * STR];
   __shared__ __attribute__((aligned(16))) __bf16 C1[T * STR];
+  __shared__ __attribute__((aligned(16))) __bf16 Ps[64 * PSTR];  // P of every head, [head][slot]
+  __shared__ float As[64];  // per-head rescale factor of the chunk; 1/l at the end
 
   const int64_t pos = blockIdx.x;  // b * M + m
   const int64_t b = pos / M;
   const int tid = threadIdx.x, lane = tid % 64;
   const int wid = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform, kept in SGPRs
   const int G = lane / 16, li = lane % 16;
+  const int h2 = lane / 32, l32 = lane % 32;
   const int h = 16 * wid + li;
   const bool wave_active = 16 * wid < H;
+  const int d0 = wid * DW;
 
   const __bf16 *kvb = kv + b * (int64_t)N * D;
   const int32_t *ib = idx + pos * (int64_t)topk;
 
-  // Q^T fragments for this lane's head (zero for heads >= H).
+  // P rows of heads no wave writes stay zero, their factors one.
+  for (int i = tid; i < 64 * PSTR / 8; i += 256) *reinterpret_cast<bf16x8 *>(Ps + 8 * i) = bf16x8{};
+  if (tid < 64) As[tid] = 1.f;
+
   bf16x8 qf[QC];
 #pragma unroll
   for (int c = 0; c < QC; ++c) {
@@ -77,44 +93,40 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
       qf[c] = bf16x8{};
   }
 
-  // Lane j < 32 loads slot j of chunk ch (-1 past the end); `valid` maps an
-  // entry to its row, or to -1 when it names no row.  The two are kept apart
-  // so that the load of a later chunk's indices is not waited for (which
-  // would also wait for the row copies issued before it) until it is used.
   auto chunk_idx = [&](int ch) -> int {
     const int slot = ch * T + lane;
     return (lane < T && slot < topk) ? ib[slot] : -1;
   };
   auto valid = [&](int my) -> int { return (my >= 0 && my < N) ? my : -1; };
-  // Copy rows wid*RPW .. wid*RPW+RPW-1 of a chunk into `dst`.
   const __amdgpu_buffer_rsrc_t kv_rs = make_rsrc(kvb, (uint32_t)((int64_t)N * D * 2));
+  // The row offset rides in the per-lane offset, which is what the buffer
+  // range check covers: an invalid slot (-1) wraps it past the end of the
+  // table (the caller keeps N*d*2 <= 2^32 - 1024), so its row reads as zeros.
   auto gather = [&](int my, __bf16 *dst) {
 #pragma unroll
     for (int j = 0; j < RPW; ++j) {
       const int row = wid * RPW + j;
-      const int src = __builtin_amdgcn_readlane(my, row);
-      if (src >= 0) {
-        if constexpr (D == 512) {
-          copy16_to_lds(kv_rs, dst + row * STR, (uint32_t)(lane * 16), (uint32_t)src * (uint32_t)(D * 2));
-        } else {
+      const uint32_t roff = (uint32_t)__builtin_amdgcn_readlane(my, row) * (uint32_t)(D * 2);
+      if constexpr (D == 512) {
+        copy16_to_lds(kv_rs, dst + row * STR, roff + (uint32_t)(lane * 16), 0u);
+      } else {
 #pragma unroll
-          for (int p = 0; p < D / 128; ++p)
-            copy4_to_lds(kv_rs, dst + row * STR + 128 * p, (uint32_t)(lane * 4 + 256 * p),
-                         (uint32_t)src * (uint32_t)(D * 2));
-        }
-      } else if (lane < D / 8) {
-        *reinterpret_cast<bf16x8 *>(dst + row * STR + lane * 8) = bf16x8{};
+        for (int p = 0; p < D / 128; ++p)
+          copy4_to_lds(kv_rs, dst + row * STR + 128 * p, roff + (uint32_t)(lane * 4 + 256 * p), 0u);
       }
     }
   };
 
   float m_run = kMaxFloor, l_run = 0.f;
-  f32x4 acc[DT];
+  f32x16 o[DTW][2];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < DTW; ++dt) o[dt][0] = o[dt][1] = f32x16{};
 
-  const int e_src = li / 4, c_src = li % 4;
-  auto compute = [&](const __bf16 *kb, uint64_t vmask) {
+  // Scores and softmax of this wave's 16 heads; P (bf16) and the rescale
+  // factor go to LDS.  P is stored per head in the k order of the output
+  // product: within each 16-slot block, slot 4a' + e (a' = 0..3) sits at
+  // 8 * (a' % 2) + 4 * (a' / 2) + e.
+  auto scores = [&](const __bf16 *kb, uint64_t vmask) {
     f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int c = 0; c < QC; ++c)
@@ -123,48 +135,75 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
         const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kb + (16 * jt + li) * STR + 32 * c + 8 * G);
         s[jt] = mfma16(a, qf[c], s[jt]);
       }
-    sched_interleave<2 * QC, 2 * QC, kReadAheadS, 0>();
+    sched_interleave<2 * QC, 2 * QC, kReadAheadS<D>, 0>();
+    // validity of this lane's slots 4G + e (bits 0..3) and 16 + 4G + e (bits 16..19)
+    const uint32_t vbits = (uint32_t)(vmask >> (4 * G));
     float mx = -__builtin_inff();
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int j = 16 * jt + 4 * G + e;
-        if (!((vmask >> j) & 1ull)) s[jt][e] = -__builtin_inff();
+        if (!((vbits >> (16 * jt + e)) & 1u)) s[jt][e] = -__builtin_inff();
         mx = fmaxf(mx, s[jt][e]);
       }
     mx = max_xor32(max_xor16(mx)) * scale_log2;
+    float alpha = 1.f;
     if (__any(mx > m_run + kLazy)) {
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
+      alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
     }
     float psum = 0.f;
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
+    for (int jt = 0; jt < 2; ++jt) {
+      float p[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = fast_exp2(fmaf(s[jt][e], scale_log2, -m_run));
-        s[jt][e] = p;
-        psum += p;
+        p[e] = fast_exp2(fmaf(s[jt][e], scale_log2, -m_run));
+        psum += p[e];
       }
-    l_run += psum;
-    // k order of P^T: slots 4G+e (e < 4) then 16+4G+e, matching the rows of
-    // the two transpose reads below.
-    const bf16x8 pf = to_bf16x8(s[0][0], s[0][1], s[0][2], s[0][3], s[1][0], s[1][1], s[1][2], s[1][3]);
-    const __bf16 *rows = kb + (4 * G + e_src) * STR + 4 * c_src;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const bf16x8 a = cat4(lds_read_tr4(rows + 16 * dt), lds_read_tr4(rows + 16 * STR + 16 * dt));
-      acc[dt] = mfma16(a, pf, acc[dt]);
+      bf16x4 p4;
+      p4[0] = (__bf16)p[0]; p4[1] = (__bf16)p[1]; p4[2] = (__bf16)p[2]; p4[3] = (__bf16)p[3];
+      *reinterpret_cast<bf16x4 *>(Ps + h * PSTR + 16 * jt + 8 * (G % 2) + 4 * (G / 2)) = p4;
     }
-    sched_interleave<DT, 2 * DT, kReadAheadV, 0>();
+    l_run += psum;
+    if (G == 0) As[h] = alpha;
   };
-  // my_cur: validated rows of chunk ch; raw_next: unvalidated entries of
-  // chunk ch + 1.
+  // O^T[d0 .. d0+DW) x 64 heads += KV^T P^T for one chunk.
+  const int e_src = li / 4, c_src = li % 4;
+  auto outprod = [&](const __bf16 *kb) {
+    const float a0 = As[l32], a1 = As[32 + l32];
+    if (__any(a0 != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < DTW; ++dt) o[dt][0] *= a0;
+    }
+    if (__any(a1 != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < DTW; ++dt) o[dt][1] *= a1;
+    }
+#pragma unroll
+    for (int kq = 0; kq < 2; ++kq) {
+      const bf16x8 p0 = *reinterpret_cast<const bf16x8 *>(Ps + l32 * PSTR + 16 * kq + 8 * h2);
+      const bf16x8 p1 = *reinterpret_cast<const bf16x8 *>(Ps + (32 + l32) * PSTR + 16 * kq + 8 * h2);
+      // rows 16kq + 4h2 + e and 16kq + 8 + 4h2 + e, column d0 + 32dt + l32
+      const int col = d0 + 16 * (G % 2) + 4 * c_src;
+      const __bf16 *rlo = kb + (16 * kq + 4 * h2 + e_src) * STR + col;
+      const __bf16 *rhi = kb + (16 * kq + 8 + 4 * h2 + e_src) * STR + col;
+#pragma unroll
+      for (int dt = 0; dt < DTW; ++dt) {
+        const bf16x8 a = cat4(lds_read_tr4(rlo + 32 * dt), lds_read_tr4(rhi + 32 * dt));
+        o[dt][0] = mfma32(a, p0, o[dt][0]);
+        o[dt][1] = mfma32(a, p1, o[dt][1]);
+      }
+    }
+  };
+  // Block barrier that waits for this wave's LDS writes but leaves the row
+  // copies in flight (vmcnt stays at its maximum).
+  auto lds_barrier = []() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("s_barrier" ::: "memory");
+  };
   auto step = [&](int ch, int nchunks, int &my_cur, int &raw_next, const __bf16 *cur, __bf16 *nxt) {
     const uint64_t vmask = __ballot(my_cur >= 0);
     int my_following = -1;
@@ -173,9 +212,11 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
       gather(my_following, nxt);
       if (ch + 2 < nchunks) raw_next = chunk_idx(ch + 2);
     }
-    if (wave_active && vmask != 0) compute(cur, vmask);
+    if (wave_active && vmask != 0) scores(cur, vmask);
+    lds_barrier();  // P and the factors of this chunk visible
+    if (vmask != 0) outprod(cur);
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // next chunk visible; this chunk's buffer free
+    __syncthreads();  // next chunk visible; this chunk's buffer, P and factors free
     my_cur = my_following;
   };
 
@@ -189,20 +230,28 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
     step(ch, nchunks, my_cur, my_next, C0, C1);
     if (ch + 1 < nchunks) step(ch + 1, nchunks, my_cur, my_next, C1, C0);
   }
-  if (!wave_active) return;
 
+  // 1/l of each head (with the sink) through As, then each wave writes its
+  // d columns of every head.
   float l_tot = sum_xor32(sum_xor16(l_run));
   if (sink != nullptr && h < H) l_tot += fast_exp2(fmaf(sink[h], kLog2e, -m_run));
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (h < H) {
-    __bf16 *oh = out + (pos * H + h) * (int64_t)D;
+  if (wave_active && G == 0) As[h] = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  __syncthreads();
+  const float inv[2] = {As[l32], As[32 + l32]};
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const f32x4 x = acc[dt] * inv;
-      bf16x4 r4;
-      r4[0] = (__bf16)x[0]; r4[1] = (__bf16)x[1]; r4[2] = (__bf16)x[2]; r4[3] = (__bf16)x[3];
-      *reinterpret_cast<bf16x4 *>(oh + 16 * dt + 4 * G) = r4;
-    }
+  for (int ht = 0; ht < 2; ++ht) {
+    const int head = 32 * ht + l32;
+    if (head >= H) continue;
+    __bf16 *oh = out + (pos * H + head) * (int64_t)D + d0 + 4 * h2;
+#pragma unroll
+    for (int dt = 0; dt < DTW; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        bf16x4 r4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r4[i] = (__bf16)(o[dt][ht][4 * a + i] * inv[ht]);
+        *reinterpret_cast<bf16x4 *>(oh + 32 * dt + 8 * a) = r4;
+      }
   }
 }
 

@@ -307,7 +307,7 @@ int bsa_layout_adaptive(const void *q, const void *k, int32_t H, int32_t Hkv, in
  *   q     device bf16 [B, M, H, d];  kv device bf16 [B, N, d]
  *   idx   device int32 [B, M, topk]; attn_sink device fp32 [H] or NULL
  *   H in [1, 64]; d in {128, 256, 512}; topk >= 1 (no alignment needed); one batch's kv
- *   (N * d * 2 bytes) at most 4 GiB - 1
+ *   (N * d * 2 bytes) at most 4 GiB - 1 KiB
  *   out   device bf16 [B, M, H, d], written
  * Errors: BSA_ERR_INVALID_ARG, BSA_ERR_UNSUPPORTED, BSA_ERR_MISALIGNED,
  * BSA_ERR_HIP.

@@ -163,6 +163,9 @@ def test_topk_validation(lib):
     assert call(d=192) == UNSUPPORTED
     assert call(kv=ctypes.c_void_p(0x10004)) == MISALIGNED
     assert call(sink=ctypes.c_void_p(0x10001)) == MISALIGNED
+    # one batch of kv may span at most 4 GiB - 1 KiB (row offsets of -1 slots wrap past it)
+    assert call(N=(1 << 22), d=512) == UNSUPPORTED      # 4 GiB
+    assert call(N=(1 << 23) - 1, d=256) == UNSUPPORTED  # 4 GiB - 512 B
 
 
 def test_status_strings(lib):
