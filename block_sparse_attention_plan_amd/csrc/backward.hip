@@ -521,6 +521,264 @@ bwd_dkdv_kernel(const T *__restrict__ q, const T *__restrict__ k,
     }
 }
 
+// Block size 16: one wave per work item and 16x16 tiles.
+//   bwd_dq16_kernel    S^T = K Q^T and dP^T = V dO^T (16x16x32; K and V rows
+//                      from LDS, Q^T and dO^T in registers), then
+//                      dQ^T += K^T dS^T (16x16x16; K^T by transpose reads,
+//                      dS^T straight from the accumulators as the B operand)
+//   bwd_dkdv16_kernel  S = Q K^T and dP = dO V^T, then dV^T += dO^T P and
+//                      dK^T += Q^T dS the same way
+// Tiles sit in LDS row-major with rows padded by 16 bytes.
+template <int D> constexpr int kStr16 = D + 8;
+
+// A 16 x D tile into LDS (rows at or past `rows` become zeros); one wave.
+template <int D, typename T>
+__device__ __forceinline__ void stage16(const T *src, __bf16 *dst, int lane, int rows) {
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int i = lane; i < 16 * CPR; i += 64) {
+    const int row = i / CPR, ch = i % CPR;
+    const bf16x8 x = row < rows ? BIo<T>::load8(src + row * D + ch * 8) : bf16x8{};
+    *reinterpret_cast<bf16x8 *>(dst + row * kStr16<D> + ch * 8) = x;
+  }
+}
+
+// Row operand of a 16x16x32 product: tile row `row`, elements 32 c + 8 G ..
+template <int D>
+__device__ __forceinline__ bf16x8 row16(const __bf16 *tile, int row, int c, int G) {
+  return *reinterpret_cast<const bf16x8 *>(tile + row * kStr16<D> + 32 * c + 8 * G);
+}
+
+// Transposed operand of a 16x16x16 product: tile rows 4G .. 4G+3 (the
+// contraction index) of column d0 + l16.
+template <int D>
+__device__ __forceinline__ bf16x4 tr16(const __bf16 *tile, int d0, int G, int l16) {
+  return lds_read_tr4(tile + (4 * G + l16 / 4) * kStr16<D> + d0 + 4 * (l16 % 4));
+}
+
+__device__ __forceinline__ bf16x4 to_bf16x4(float a, float b, float c, float d) {
+  bf16x4 r;
+  r[0] = (__bf16)a; r[1] = (__bf16)b; r[2] = (__bf16)c; r[3] = (__bf16)d;
+  return r;
+}
+
+template <int D, typename T, bool MASK>
+__global__ void __launch_bounds__(64)
+bwd_dq16_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+                const T *__restrict__ dout, const float *__restrict__ lse2,
+                const float *__restrict__ Dv, const int32_t *__restrict__ row_ptr,
+                const int32_t *__restrict__ col_idx, const int32_t *__restrict__ row_order,
+                int32_t B, int32_t H, int32_t Mb, int32_t Nb, float scale_log2, float scale,
+                const FwdOptions opt, T *__restrict__ dq) {
+  constexpr int QC = D / 32;   // 32-wide k steps of the score products
+  constexpr int DT = D / 16;   // 16-wide d tiles of dQ^T
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[16 * kStr16<D>];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[16 * kStr16<D>];
+
+  const int64_t W = (int64_t)B * H * Mb;
+  const int64_t per = (W + 7) / 8;
+  const int64_t w = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (w >= W) return;
+  const int64_t HM = (int64_t)H * Mb;
+  const int b = (int)(w / HM);
+  const int r = row_order[w % HM];
+  const int h = r / Mb;
+  const int m = r % Mb;
+  const int beg = row_ptr[r];
+  const int end = row_ptr[r + 1];
+
+  const int lane = threadIdx.x;
+  const int G = lane / 16, l16 = lane % 16;
+  const int64_t bh = (int64_t)b * H + h;
+  const int64_t Sq = opt.sq, Sk = opt.sk;
+  const int64_t bkv = (int64_t)b * (H / opt.kv_group) + h / opt.kv_group;
+  const T *kh = k + bkv * Sk * D;
+  const T *vh = v + bkv * Sk * D;
+  const int64_t i_row = (int64_t)m * 16 + l16;   // this lane's query (a column of S^T)
+  const bool q_ok = !MASK || i_row < Sq;
+  const int qsg = (MASK && opt.qseg && q_ok) ? opt.qseg[(int64_t)b * Sq + i_row] : 0;
+  const float l2 = q_ok ? lse2[bh * Sq + i_row] : __builtin_inff();
+  const float dd = q_ok ? Dv[bh * Sq + i_row] : 0.f;
+
+  bf16x8 qf[QC], gf[QC];
+#pragma unroll
+  for (int c = 0; c < QC; ++c) {
+    qf[c] = q_ok ? BIo<T>::load8(q + (bh * Sq + i_row) * D + 32 * c + 8 * G) : bf16x8{};
+    gf[c] = q_ok ? BIo<T>::load8(dout + (bh * Sq + i_row) * D + 32 * c + 8 * G) : bf16x8{};
+  }
+  f32x4 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int t = beg; t < end; ++t) {
+    const int ncol = col_idx[t];
+    if (MASK && opt.causal && ncol > m) continue;   // every key after every query
+    __syncthreads();                                // previous tile fully read
+    const int kv = MASK ? (int)min((int64_t)16, Sk - (int64_t)ncol * 16) : 16;  // keys that exist
+    stage16<D, T>(kh + (int64_t)ncol * 16 * D, Ks, lane, kv);
+    stage16<D, T>(vh + (int64_t)ncol * 16 * D, Vs, lane, kv);
+    __syncthreads();
+    const bool diag = MASK && opt.causal && ncol == m;
+    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < QC; ++c) {
+      s = mfma16(row16<D>(Ks, l16, c, G), qf[c], s);
+      dp = mfma16(row16<D>(Vs, l16, c, G), gf[c], dp);
+    }
+    // S^T[key][query]: key 4G + e, query l16
+    float ds[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int key = 4 * G + e;
+      const Weight wt = weight<MASK>(s[e], scale_log2, l2, opt);
+      float p = wt.p;
+      if (diag && key > l16) p = 0.f;
+      if (MASK && key >= kv) p = 0.f;
+      if (MASK && opt.qseg && key < kv &&
+          opt.kseg[(int64_t)b * Sk + (int64_t)ncol * 16 + key] != qsg)
+        p = 0.f;
+      ds[e] = p * (dp[e] - dd) * wt.slope;
+    }
+    const bf16x4 dsb = to_bf16x4(ds[0], ds[1], ds[2], ds[3]);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma16k16(tr16<D>(Ks, 16 * dt, G, l16), dsb, acc[dt]);
+  }
+  if (!q_ok) return;
+  T *dqh = dq + (bh * Sq + i_row) * D + 4 * G;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    BIo<T>::store4(dqh + 16 * dt, scale * acc[dt][0], scale * acc[dt][1], scale * acc[dt][2],
+                   scale * acc[dt][3]);
+}
+
+template <int D, typename T, bool MASK>
+__global__ void __launch_bounds__(64)
+bwd_dkdv16_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+                  const T *__restrict__ dout, const float *__restrict__ lse2,
+                  const float *__restrict__ Dv, const int32_t *__restrict__ col_ptr,
+                  const int32_t *__restrict__ row_idx, const int32_t *__restrict__ col_order,
+                  int32_t B, int32_t H, int32_t Hkv, int32_t Mb, int32_t Nb, float scale_log2,
+                  float scale, const FwdOptions opt, T *__restrict__ dk, T *__restrict__ dv) {
+  constexpr int QC = D / 32;
+  constexpr int DT = D / 16;
+  __shared__ __attribute__((aligned(16))) __bf16 Qs[16 * kStr16<D>];
+  __shared__ __attribute__((aligned(16))) __bf16 Gs[16 * kStr16<D>];   // dO tile
+  __shared__ float Ls[16], Ds[16];
+  __shared__ int32_t Gq[16];
+
+  const int64_t W = (int64_t)B * Hkv * Nb;
+  const int64_t per = (W + 7) / 8;
+  const int64_t w = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (w >= W) return;
+  const int64_t KN = (int64_t)Hkv * Nb;
+  const int b = (int)(w / KN);
+  const int item = col_order[w % KN];
+  const int kvh = item / Nb;
+  const int n = item % Nb;
+  const int g = H / Hkv;
+
+  const int lane = threadIdx.x;
+  const int G = lane / 16, l16 = lane % 16;
+  const int64_t Sq = opt.sq, Sk = opt.sk;
+  const int64_t bkv = (int64_t)b * Hkv + kvh;
+  const int64_t j_row = (int64_t)n * 16 + l16;   // this lane's key (a column of S)
+  const bool k_ok = !MASK || j_row < Sk;
+  const int ksg = (MASK && opt.kseg && k_ok) ? opt.kseg[(int64_t)b * Sk + j_row] : 0;
+
+  bf16x8 kf[QC], vf[QC];
+#pragma unroll
+  for (int c = 0; c < QC; ++c) {
+    kf[c] = k_ok ? BIo<T>::load8(k + (bkv * Sk + j_row) * D + 32 * c + 8 * G) : bf16x8{};
+    vf[c] = k_ok ? BIo<T>::load8(v + (bkv * Sk + j_row) * D + 32 * c + 8 * G) : bf16x8{};
+  }
+  f32x4 ak[DT], av[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) ak[dt] = av[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int hh = 0; hh < g; ++hh) {
+    const int h = kvh * g + hh;
+    const int64_t bh = (int64_t)b * H + h;
+    const int beg = col_ptr[h * Nb + n];
+    const int end = col_ptr[h * Nb + n + 1];
+    for (int t = beg; t < end; ++t) {
+      const int m = row_idx[t];
+      if (MASK && opt.causal && m < n) continue;    // every key after every query
+      __syncthreads();                              // previous tile fully read
+      const int qv = MASK ? (int)min((int64_t)16, Sq - (int64_t)m * 16) : 16;  // rows that exist
+      stage16<D, T>(q + (bh * Sq + (int64_t)m * 16) * D, Qs, lane, qv);
+      stage16<D, T>(dout + (bh * Sq + (int64_t)m * 16) * D, Gs, lane, qv);
+      if (lane < 16) {
+        // rows past a cut last block: weight exp2(s - inf) = 0
+        Ls[lane] = lane < qv ? lse2[bh * Sq + (int64_t)m * 16 + lane] : __builtin_inff();
+        Ds[lane] = lane < qv ? Dv[bh * Sq + (int64_t)m * 16 + lane] : 0.f;
+        if (MASK && opt.qseg) Gq[lane] = lane < qv ? opt.qseg[(int64_t)b * Sq + (int64_t)m * 16 + lane] : 0;
+      }
+      __syncthreads();
+      const bool diag = MASK && opt.causal && m == n;
+      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < QC; ++c) {
+        s = mfma16(row16<D>(Qs, l16, c, G), kf[c], s);
+        dp = mfma16(row16<D>(Gs, l16, c, G), vf[c], dp);
+      }
+      // S[query][key]: query 4G + e, key l16
+      float pw[4], ds[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int qr = 4 * G + e;
+        const Weight wt = weight<MASK>(s[e], scale_log2, Ls[qr], opt);
+        float p = wt.p;
+        if (diag && l16 > qr) p = 0.f;
+        if (!k_ok) p = 0.f;
+        if (MASK && opt.qseg && Gq[qr] != ksg) p = 0.f;
+        pw[e] = p;
+        ds[e] = p * (dp[e] - Ds[qr]) * wt.slope;
+      }
+      const bf16x4 pb = to_bf16x4(pw[0], pw[1], pw[2], pw[3]);
+      const bf16x4 dsb = to_bf16x4(ds[0], ds[1], ds[2], ds[3]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        av[dt] = mfma16k16(tr16<D>(Gs, 16 * dt, G, l16), pb, av[dt]);
+        ak[dt] = mfma16k16(tr16<D>(Qs, 16 * dt, G, l16), dsb, ak[dt]);
+      }
+    }
+  }
+  if (!k_ok) return;
+  T *dkr = dk + (bkv * Sk + j_row) * D + 4 * G;
+  T *dvr = dv + (bkv * Sk + j_row) * D + 4 * G;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    BIo<T>::store4(dkr + 16 * dt, scale * ak[dt][0], scale * ak[dt][1], scale * ak[dt][2],
+                   scale * ak[dt][3]);
+    BIo<T>::store4(dvr + 16 * dt, av[dt][0], av[dt][1], av[dt][2], av[dt][3]);
+  }
+}
+
+template <int D, typename T, bool MASK>
+hipError_t launch_grads16(const BwdArgs &a, hipStream_t stream) {
+  const float scale_log2 = a.scale * kLog2e;
+  {
+    const int64_t W = (int64_t)a.B * a.H * a.Mb;
+    const int64_t grid = (W + 7) / 8 * 8;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_dq16_kernel<D, T, MASK>), dim3((unsigned)grid), dim3(64), 0, stream,
+                       (const T *)a.q, (const T *)a.k, (const T *)a.v, (const T *)a.dout, a.lse2,
+                       a.Dv, a.row_ptr, a.col_idx, a.row_order, a.B, a.H, a.Mb, a.Nb, scale_log2,
+                       a.scale, a.opt, (T *)a.dq);
+  }
+  {
+    const int32_t Hkv = a.H / a.opt.kv_group;
+    const int64_t W = (int64_t)a.B * Hkv * a.Nb;
+    const int64_t grid = (W + 7) / 8 * 8;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_dkdv16_kernel<D, T, MASK>), dim3((unsigned)grid), dim3(64), 0, stream,
+                       (const T *)a.q, (const T *)a.k, (const T *)a.v, (const T *)a.dout, a.lse2,
+                       a.Dv, a.col_ptr, a.row_idx, a.col_order, a.B, a.H, Hkv, a.Mb, a.Nb,
+                       scale_log2, a.scale, a.opt, (T *)a.dk, (T *)a.dv);
+  }
+  return hipGetLastError();
+}
+
 template <int BS, int D, typename T, bool MASK>
 hipError_t launch_grads(const BwdArgs &a, hipStream_t stream) {
   const float scale_log2 = a.scale * kLog2e;
@@ -562,7 +820,7 @@ hipError_t launch_pre(const BwdArgs &a, hipStream_t stream) {
 }  // namespace
 
 bool backward_supported(int32_t bs, int32_t d) {
-  return (bs == 32 || bs == 64 || bs == 128) && (d == 32 || d == 64 || d == 128);
+  return (bs == 16 || bs == 32 || bs == 64 || bs == 128) && (d == 32 || d == 64 || d == 128);
 }
 
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
@@ -586,6 +844,14 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
                       : launch_grads<BS_, D_, float, false>(a, stream))                       \
               : (mask ? launch_grads<BS_, D_, __bf16, true>(a, stream)                        \
                       : launch_grads<BS_, D_, __bf16, false>(a, stream));
+#define BSA_BWD16_CASE(D_)                                                                     \
+  if (a.bs == 16 && a.d == D_)                                                                \
+    e = a.f32 ? (mask ? launch_grads16<D_, float, true>(a, stream)                            \
+                      : launch_grads16<D_, float, false>(a, stream))                          \
+              : (mask ? launch_grads16<D_, __bf16, true>(a, stream)                           \
+                      : launch_grads16<D_, __bf16, false>(a, stream));
+  BSA_BWD16_CASE(32) BSA_BWD16_CASE(64) BSA_BWD16_CASE(128)
+#undef BSA_BWD16_CASE
   BSA_BWD_CASE(32, 32) BSA_BWD_CASE(32, 64) BSA_BWD_CASE(32, 128)
   BSA_BWD_CASE(64, 32) BSA_BWD_CASE(64, 64) BSA_BWD_CASE(64, 128)
   BSA_BWD_CASE(128, 32) BSA_BWD_CASE(128, 64) BSA_BWD_CASE(128, 128)

@@ -242,7 +242,7 @@ size_t bsa_backward_workspace_bytes(int32_t B, int32_t H, int32_t Sq);
  *   dk, dv  device [B, Hkv, Sk, d] of dtype, written (every row)
  *   dsink device fp32 [H], written when opts->attn_sink is set; may be NULL
  * Supported: dtype BSA_BF16 or BSA_F32 (fp32 tiles are rounded to bf16 on
- * load, as in the forward; products accumulate in fp32), bs in {32, 64, 128},
+ * load, as in the forward; products accumulate in fp32), bs in {16, 32, 64, 128},
  * d in {32, 64, 128}.
  * Deterministic: no atomics, so repeated calls give identical bits.
  * Errors: as bsa_forward_ex, plus BSA_ERR_UNSUPPORTED for bs = 16,

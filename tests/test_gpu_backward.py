@@ -75,7 +75,8 @@ OPTION_SETS = {
     "gqa": dict(Hkv=2),
     "all": dict(sink_mean=1.0, soft_cap=2.0, causal=True, Hkv=2),
 }
-BWD_CASES = [(32, 32), (32, 128), (64, 64), (64, 128), (128, 32), (128, 128)]
+BWD_CASES = [(16, 32), (16, 128), (32, 32), (32, 128), (64, 64), (64, 128), (128, 32),
+             (128, 128)]
 
 
 def _forward_backward(gpu, x, opts, plan, pc, dout):
@@ -171,7 +172,8 @@ def test_backward_full_workload(gpu):
 
 @pytest.mark.parametrize("opt_name", ["plain", "all"])
 @pytest.mark.parametrize("bs,d,Sq,Sk", [(32, 32, 160, 224), (64, 128, 320, 256),
-                                        (128, 64, 256, 384), (64, 64, 250, 190)])
+                                        (128, 64, 256, 384), (64, 64, 250, 190),
+                                        (16, 32, 96, 80), (16, 64, 75, 90)])
 def test_backward_f32(gpu, bs, d, Sq, Sk, opt_name):
     """fp32 I/O: tiles are rounded to bf16 on load (as in the forward) and the
     gradients come back in fp32; compared with the oracle's gradients at the
@@ -204,3 +206,23 @@ def test_backward_f32(gpu, bs, d, Sq, Sk, opt_name):
     compare_grad(to64(dq), rq, f"dq f32 {opt_name} bs={bs} d={d}")
     compare_grad(to64(dk), rk, f"dk f32 {opt_name} bs={bs} d={d}")
     compare_grad(to64(dv), rv, f"dv f32 {opt_name} bs={bs} d={d}")
+
+
+def test_backward_band_f32_config(gpu):
+    """The fp32 band workload (B1 H2 S256 bs16 d32, layout |m - n| <= 1):
+    every gradient entry against the oracle's dense gradients."""
+    name = "band1_h2_s256_bs16_d32_f32"
+    x = W.make_workload(name)
+    dout = torch.from_numpy(np.random.default_rng(3).standard_normal(x.q.shape).astype(np.float32))
+    say(f"[backward] {name}")
+    plan, _ = check_plan(gpu, x.layout)
+    pc = check_plan_cols(gpu, x.layout, x.layout.shape[0])
+    q, k, v = (t.to(gpu) for t in (x.q, x.k, x.v))
+    out, lse = bsa.bsa_forward(q, k, v, plan, x.scale)
+    dq, dk, dv, _ = bsa.bsa_backward(q, k, v, out, dout.to(gpu), lse, plan, pc, x.scale)
+    torch.cuda.synchronize()
+    rq, rk, rv, _ = O.attention_backward_dense(to64(x.q), to64(x.k), to64(x.v), to64(dout),
+                                               x.layout, x.bs, x.scale)
+    compare_grad(to64(dq), rq, f"dq {name}")
+    compare_grad(to64(dk), rk, f"dk {name}")
+    compare_grad(to64(dv), rv, f"dv {name}")

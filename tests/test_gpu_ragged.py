@@ -83,7 +83,8 @@ def test_forward_ragged(gpu, bs, d, dtype, Sq, Sk, causal, sink):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("bs,d,Sq,Sk", [(32, 64, 3 * 32 - 5, 4 * 32 - 31), (64, 128, 200, 150),
-                                        (128, 128, 3 * 128 - 1, 2 * 128 + 3), (128, 32, 129, 300)])
+                                        (128, 128, 3 * 128 - 1, 2 * 128 + 3), (128, 32, 129, 300),
+                                        (16, 32, 3 * 16 - 7, 5 * 16 + 1)])
 def test_backward_ragged(gpu, bs, d, Sq, Sk, causal):
     H, Hkv, B = 4, 2, 2
     Mb, Nb = -(-Sq // bs), -(-Sk // bs)
