@@ -25,8 +25,10 @@
 //   bsa_fwd32_kernel    bs = 32 and fp32 I/O: 32 rows per wave, 32x32x16 MFMA,
 //                       register-staged tiles, two key halves per row group
 //                       when bs >= 64
-//   bsa_fwd_dma_kernel  bf16, bs >= 64: as above with tiles copied from HBM
-//                       straight into double-buffered, XOR-swizzled LDS
+//   bsa_fwd_dma_kernel  bf16, bs >= 64: one wave per 32-row group, each live
+//                       tile streamed as two pieces of bs/2 keys copied from
+//                       HBM straight into double-buffered, XOR-swizzled LDS
+//                       (two workgroups per CU)
 //
 // Optional terms, from the arguments of the ejkernel BlockSparseAttention
 // operation: grouped K/V heads (query head h reads K/V head h / kv_group), a
@@ -50,6 +52,15 @@ constexpr float kLazy = 8.0f;  // tolerated staleness of the running max (log2 u
 #define BSA_DMA_KEY_SPLIT 2
 #endif
 constexpr int kDmaKeySplit = BSA_DMA_KEY_SPLIT;  // waves per 32-row group in the bf16 bs=128 kernel
+#ifndef BSA_DMA_PIECES
+#define BSA_DMA_PIECES 2
+#endif
+// pieces per tile in the bf16 bs=128 kernel with one wave per 32-row group
+constexpr int kDmaPieces = BSA_DMA_PIECES;
+#ifndef BSA_DMA_PIECES64
+#define BSA_DMA_PIECES64 2
+#endif
+constexpr int kDmaPieces64 = BSA_DMA_PIECES64;  // the same for bs=64
 #ifndef BSA_READ_AHEAD_K
 #define BSA_READ_AHEAD_K 4
 #endif
@@ -639,8 +650,9 @@ template <int D> struct VSwz {
   }
 };
 
-template <int BS, int D, int KSPLIT, bool MASK>
-__global__ void __launch_bounds__(BS * 2 * KSPLIT) __attribute__((amdgpu_waves_per_eu(KSPLIT)))
+template <int BS, int D, int KSPLIT, int PIECES, bool MASK>
+__global__ void __launch_bounds__(BS * 2 * KSPLIT)
+__attribute__((amdgpu_waves_per_eu(KSPLIT * PIECES)))
 bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
                    const __bf16 *__restrict__ v, const int32_t *__restrict__ row_ptr,
                    const int32_t *__restrict__ col_idx, const int32_t *__restrict__ row_order,
@@ -648,9 +660,10 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
                    __bf16 *__restrict__ out, float *__restrict__ lse, const FwdOptions opt) {
   constexpr int NRG = BS / 32;           // 32-row groups
   constexpr int NW = NRG * KSPLIT;       // waves per workgroup
-  constexpr int KW = BS / KSPLIT;        // keys per wave per tile
+  constexpr int PB = BS / PIECES;        // keys per piece (a tile is streamed in PIECES pieces)
+  constexpr int KW = PB / KSPLIT;        // keys per wave per piece
   constexpr int CPR = D / 8;             // 16-byte chunks per row
-  constexpr int TILE = BS * D;           // elements per K or V tile
+  constexpr int TILE = PB * D;           // elements per K or V buffer (one piece)
   constexpr int NI = TILE * 2 / 1024;    // 1 KiB load instructions per tile
   constexpr int IPW = NI / NW;           // load instructions per wave per tile
   constexpr int RPI = 64 / CPR;          // rows per load instruction
@@ -659,8 +672,12 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   constexpr int DT = D / 32;
   constexpr int HALF = DT * 8 * 64;      // merge floats per row group and buffer
   static_assert(NI % NW == 0 && IPW >= 1, "tile loads must split evenly over waves");
-  static_assert(NRG * HALF * 4 == TILE * 2, "merge halves fill one tile buffer each");
-  static_assert((RPI * NW) % CPR == 0, "per-wave K swizzle must be lane-constant");
+  static_assert(KSPLIT == 1 || NRG * HALF * 4 == TILE * 2, "merge halves fill one tile buffer each");
+  static_assert(KSPLIT == 1 || PIECES == 1, "the key split merges whole tiles");
+  // The K swizzle of the rows a lane copies repeats every NSW copy
+  // instructions of its wave (NSW = 1 when RPI * NW is a multiple of CPR).
+  constexpr int NSW = (RPI * NW) % CPR == 0 ? 1 : CPR / ((RPI * NW) % CPR);
+  static_assert((RPI * NW * NSW) % CPR == 0 && IPW % NSW == 0, "K swizzle pattern must repeat");
 
   // Four distinct LDS objects, so that the compiler can tell the tile being
   // read from the tile being filled and need not wait for the copy in flight.
@@ -719,29 +736,42 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   // Load instruction j of this wave covers tile rows RPI*(wid + NW*j) ..;
   // lane l writes physical chunk l % CPR of row RPI*i + l / CPR.
   const int lrow = lane / CPR, lph = lane % CPR;
-  const int row0 = RPI * wid + lrow;  // row % CPR and f(row) are the same for every j
-  const int k_src = lrow * D + (lph ^ (row0 & (CPR - 1))) * 8;
+  const int row0 = RPI * wid + lrow;  // f(row) of the V swizzle is the same for every j
+  int k_src[NSW];                     // row % CPR repeats every NSW instructions
+#pragma unroll
+  for (int p = 0; p < NSW; ++p)
+    k_src[p] = lrow * D + (lph ^ ((row0 + RPI * NW * p) & (CPR - 1))) * 8;
   const int v_src = lrow * D + (lph ^ VSwz<D>::f(row0)) * 8;
   // (MASK instances: a cut last tile's resource ends at the sequence end, so
   // the rows past it read as zeros.  The range check of a raw buffer load
   // covers the per-lane offset, not the scalar one, so those instances carry
   // the row offset per lane.)
-  auto dma = [&](const __bf16 *src_tile, const int src_off, __bf16 *dst_tile, uint32_t bytes) {
+  auto dma = [&](const __bf16 *src_tile, auto src_off_of, __bf16 *dst_tile, uint32_t bytes) {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(src_tile, bytes);
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
       const int i = wid + NW * j;
+      const int src_off = src_off_of(j);
       if constexpr (MASK)
         copy16_to_lds(rs, dst_tile + i * 512, (uint32_t)(src_off * 2 + i * RPI * D * 2), 0u);
       else
         copy16_to_lds(rs, dst_tile + i * 512, (uint32_t)(src_off * 2), (uint32_t)(i * RPI * D * 2));
     }
   };
-  auto tile_bytes = [&](int n) -> uint32_t {
-    return MASK ? (uint32_t)(min((int64_t)BS, Sk - (int64_t)n * BS) * D * 2) : (uint32_t)(TILE * 2);
+  // piece `half` of tile n: keys n*BS + half*PB .. + PB - 1 (rows past Sk read as zeros)
+  auto tile_bytes = [&](int n, int half) -> uint32_t {
+    return MASK ? (uint32_t)(max((int64_t)0, min((int64_t)PB, Sk - (int64_t)n * BS - half * PB)) * D * 2)
+                : (uint32_t)(TILE * 2);
   };
-  auto load_k = [&](int n, __bf16 *dst) { dma(kh + (int64_t)n * TILE, k_src, dst, tile_bytes(n)); };
-  auto load_v = [&](int n, __bf16 *dst) { dma(vh + (int64_t)n * TILE, v_src, dst, tile_bytes(n)); };
+  auto piece_src = [&](const __bf16 *base, int n, int half) {
+    return base + (int64_t)n * BS * D + (int64_t)half * PB * D;
+  };
+  auto load_k = [&](int n, int half, __bf16 *dst) {
+    dma(piece_src(kh, n, half), [&](int j) { return k_src[j % NSW]; }, dst, tile_bytes(n, half));
+  };
+  auto load_v = [&](int n, int half, __bf16 *dst) {
+    dma(piece_src(vh, n, half), [&](int) { return v_src; }, dst, tile_bytes(n, half));
+  };
 
   // Per-lane element offsets of the K operand reads (one per k chunk).
   const int key0 = ks * KW;
@@ -769,8 +799,9 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   // Options on a fresh score tile of column ncol (MASK instances only): tanh
   // logit cap, then the causal mask when the tile reaches past the diagonal
   // (key row key0 + 32jt + 8(e/4) + 4h2 + e%4, query row 32rg + l32).
-  auto apply_opts = [&](f32x16 (&s)[JT], int ncol) {
+  auto apply_opts = [&](f32x16 (&s)[JT], int ncol, int half) {
     if constexpr (!MASK) return;
+    const int kb0 = key0 + half * PB;   // this wave's first key inside the tile
     if (opt.cap_k != 0.f) {
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt)
@@ -778,7 +809,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
         for (int e = 0; e < 16; ++e) s[jt][e] = capped_score(s[jt][e], opt.cap_k, opt.cap_b);
     }
     if (opt.causal && ncol >= m) {
-      const int dq = (m - ncol) * BS + 32 * rg + l32 - key0 - 4 * h2;
+      const int dq = (m - ncol) * BS + 32 * rg + l32 - kb0 - 4 * h2;
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
@@ -786,7 +817,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
           if (32 * jt + 8 * (e / 4) + (e % 4) > dq) s[jt][e] = -__builtin_inff();
     }
     if ((int64_t)(ncol + 1) * BS > Sk) {  // keys past a cut last block
-      const int kv = (int)(Sk - (int64_t)ncol * BS) - key0 - 4 * h2;
+      const int kv = (int)(Sk - (int64_t)ncol * BS) - kb0 - 4 * h2;
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
@@ -877,9 +908,11 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   // steps ahead (lane 0: K column for M_{t+2}, lane 1: V column for S_{t+2});
   // a scalar load in flight would force every LDS wait in between to drain
   // completely.
-  const int n = end - beg;
+  // Piece u = 0 .. n-1 is piece u % PIECES of live tile u / PIECES.
+  const int n = (end - beg) * PIECES;
   const int32_t *cols = col_idx + beg;
-  auto col_at = [&](int u) -> int { return cols[min(u, n - 1)]; };
+  auto col_at = [&](int u) -> int { return cols[min(u, n - 1) / PIECES]; };
+  auto half_at = [&](int u) -> int { return min(u, n - 1) % PIECES; };
   auto fetch_cols = [&](int kpos, int vpos) -> int { return col_at(lane == 0 ? kpos : vpos); };
   constexpr int kVmInFlight = 2 * IPW;
   constexpr int kVmWait = (kVmInFlight & 15) | (7 << 4) | (15 << 8) | ((kVmInFlight >> 4) << 14);
@@ -893,18 +926,18 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   float mx_a = 0.f, mx_b = 0.f;
   int cv0 = fetch_cols(3, 1);  // for S_0 / M_0
   int cv1 = fetch_cols(4, 2);  // for S_1 / M_1
-  load_k(col_at(0), K0);
-  load_v(col_at(0), V0);
-  load_k(col_at(1), K1);
+  load_k(col_at(0), half_at(0), K0);
+  load_v(col_at(0), half_at(0), V0);
+  load_k(col_at(1), half_at(1), K1);
   const int k2 = col_at(2);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   qk(K0, s_a);
-  apply_opts(s_a, col_at(0));
+  apply_opts(s_a, col_at(0), half_at(0));
   mx_a = tile_max(s_a);
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();  // M_{-1}: K0 free
-  load_k(k2, K0);
+  load_k(k2, half_at(2), K0);
 
   // One step; Kq is K[(t+1)%2], Vn is V[(t+1)%2], Vc is V[t%2].  MORE:
   // tile t+1 exists (every step but the row's last).
@@ -918,7 +951,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     const int kcol = __builtin_amdgcn_readlane(cv, 0);  // column of tile t+3
     const int vcol = __builtin_amdgcn_readlane(cv, 1);  // column of tile t+1
     cv = fetch_cols(t + 5, t + 3);
-    load_v(vcol, Vn);
+    load_v(vcol, half_at(t + 1), Vn);
     rescale(mx_cur);
     bf16x8 pf[2 * JT];
     if constexpr (MORE) qk(Kq, s_nxt);
@@ -927,10 +960,10 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     __builtin_amdgcn_s_waitcnt(kVmWait);  // V_t landed
     __builtin_amdgcn_sched_barrier(0);
     block_barrier();
-    load_k(kcol, Kq);
+    load_k(kcol, half_at(t + 3), Kq);
     pv(pf, Vc);
     if constexpr (MORE) {
-      apply_opts(s_nxt, vcol);
+      apply_opts(s_nxt, vcol, half_at(t + 1));
       mx_nxt = tile_max(s_nxt);
       sched_interleave<JT * 2 * DT, 4 * JT * DT, kReadAheadV, 1>();
     } else {
@@ -1016,8 +1049,9 @@ hipError_t launch_one(const void *q, const void *k, const void *v, const int32_t
                        row_order, B, H, Mb, Nb, scale * kLog2e, (T *)out, lse, opt);
   } else if constexpr (BS >= 64 && std::is_same<T, __bf16>::value) {
     if (opt.qseg == nullptr) {
-      constexpr int KS = BS == 128 ? kDmaKeySplit : 2;
-      hipLaunchKernelGGL((bsa_fwd_dma_kernel<BS, D, KS, MASK>), dim3((unsigned)grid),
+      constexpr int PC = BS == 128 ? kDmaPieces : kDmaPieces64;
+      constexpr int KS = PC == 2 ? 1 : BS == 128 ? kDmaKeySplit : 2;
+      hipLaunchKernelGGL((bsa_fwd_dma_kernel<BS, D, KS, PC, MASK>), dim3((unsigned)grid),
                          dim3(BS * 2 * KS), 0, stream, (const __bf16 *)q, (const __bf16 *)k,
                          (const __bf16 *)v, row_ptr, col_idx, row_order, B, H, Mb, Nb,
                          scale * kLog2e, (__bf16 *)out, lse, opt);
