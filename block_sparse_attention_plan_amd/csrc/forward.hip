@@ -650,7 +650,7 @@ template <int D> struct VSwz {
   }
 };
 
-template <int BS, int D, int KSPLIT, int PIECES, bool MASK>
+template <int BS, int D, int KSPLIT, int PIECES, bool MASK, bool SEG = false>
 __global__ void __launch_bounds__(BS * 2 * KSPLIT)
 __attribute__((amdgpu_waves_per_eu(KSPLIT * PIECES)))
 bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
@@ -685,6 +685,11 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   __shared__ __attribute__((aligned(1024))) __bf16 K1[TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 V0[TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 V1[TILE];
+  // segment ids of the keys of the pieces in K0 and K1 (SEG instances:
+  // MASK instances for calls with segment ids)
+  static_assert(MASK || !SEG, "segment ids come with the other masks");
+  __shared__ __attribute__((aligned(16))) int32_t KG0[SEG ? PB : 4];
+  __shared__ __attribute__((aligned(16))) int32_t KG1[SEG ? PB : 4];
 
   const int64_t W = (int64_t)B * H * Mb;
   const int64_t per = (W + 7) / 8;
@@ -718,6 +723,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   float *lh = lse ? lse + bh * Sq : nullptr;
   const int64_t i_row = (int64_t)m * BS + 32 * rg + l32;
   const bool q_ok = !MASK || i_row < Sq;  // rows past a cut last block
+  const int qsg = (SEG && q_ok) ? opt.qseg[(int64_t)b * Sq + i_row] : 0;
 
   if (beg == end) {
     if (ks == 0 && q_ok) {
@@ -766,8 +772,18 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   auto piece_src = [&](const __bf16 *base, int n, int half) {
     return base + (int64_t)n * BS * D + (int64_t)half * PB * D;
   };
-  auto load_k = [&](int n, int half, __bf16 *dst) {
+  // SEG instances also copy the piece's key segment ids, 16 per wave with
+  // one 4-byte-per-lane copy: every wave issues the same number of copies.
+  constexpr int IDW = PB / NW;  // ids per wave
+  static_assert(!SEG || (IDW >= 1 && IDW <= 64 && PB % NW == 0), "id copies split over waves");
+  auto load_k = [&](int n, int half, __bf16 *dst, int32_t *ids) {
     dma(piece_src(kh, n, half), [&](int j) { return k_src[j % NSW]; }, dst, tile_bytes(n, half));
+    if constexpr (SEG) {
+      const int64_t k0 = (int64_t)n * BS + half * PB + wid * IDW;  // first key of this wave's ids
+      const uint32_t nb = (uint32_t)(max((int64_t)0, min((int64_t)IDW, Sk - k0)) * 4);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(opt.kseg + (int64_t)b * Sk + k0, nb);
+      if (lane < IDW) copy4_to_lds(rs, ids + wid * IDW, (uint32_t)(lane * 4), 0u);
+    }
   };
   auto load_v = [&](int n, int half, __bf16 *dst) {
     dma(piece_src(vh, n, half), [&](int) { return v_src; }, dst, tile_bytes(n, half));
@@ -799,7 +815,27 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   // Options on a fresh score tile of column ncol (MASK instances only): tanh
   // logit cap, then the causal mask when the tile reaches past the diagonal
   // (key row key0 + 32jt + 8(e/4) + 4h2 + e%4, query row 32rg + l32).
-  auto apply_opts = [&](f32x16 (&s)[JT], int ncol, int half) {
+  // Bit 16 jt + e set: score e of block jt belongs to a key of another
+  // segment.  Read from the piece's ids in the phase that computed its
+  // scores, before the next barrier lets its buffer be refilled.
+  auto seg_bits = [&](const int32_t *ids) -> uint32_t {
+    uint32_t bits = 0;
+    if constexpr (SEG) {
+      {
+        const int32_t *kst = ids + key0 + 4 * h2;
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4) {
+            const i32x4 v4 = *reinterpret_cast<const i32x4 *>(kst + 32 * jt + 8 * a4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bits |= (uint32_t)(v4[i] != qsg) << (16 * jt + 4 * a4 + i);
+          }
+      }
+    }
+    return bits;
+  };
+  auto apply_opts = [&](f32x16 (&s)[JT], int ncol, int half, uint32_t segbits) {
     if constexpr (!MASK) return;
     const int kb0 = key0 + half * PB;   // this wave's first key inside the tile
     if (opt.cap_k != 0.f) {
@@ -824,7 +860,13 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
         for (int e = 0; e < 16; ++e)
           if (32 * jt + 8 * (e / 4) + (e % 4) >= kv) s[jt][e] = -__builtin_inff();
     }
-    // (calls with segment ids run the register-staged kernel)
+    if constexpr (SEG) {  // packed sequences: only keys of the query's segment
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if ((segbits >> (16 * jt + e)) & 1u) s[jt][e] = -__builtin_inff();
+    }
   };
 
   float m_run = kMaxFloor;  // running max (log2 units)
@@ -914,7 +956,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   auto col_at = [&](int u) -> int { return cols[min(u, n - 1) / PIECES]; };
   auto half_at = [&](int u) -> int { return min(u, n - 1) % PIECES; };
   auto fetch_cols = [&](int kpos, int vpos) -> int { return col_at(lane == 0 ? kpos : vpos); };
-  constexpr int kVmInFlight = 2 * IPW;
+  constexpr int kVmInFlight = 2 * IPW + (SEG ? 1 : 0);
   constexpr int kVmWait = (kVmInFlight & 15) | (7 << 4) | (15 << 8) | ((kVmInFlight >> 4) << 14);
   static_assert(kVmInFlight < 64, "vmcnt holds 6 bits");
   // Block barrier without the release fence of __syncthreads(), which would
@@ -926,22 +968,22 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   float mx_a = 0.f, mx_b = 0.f;
   int cv0 = fetch_cols(3, 1);  // for S_0 / M_0
   int cv1 = fetch_cols(4, 2);  // for S_1 / M_1
-  load_k(col_at(0), half_at(0), K0);
+  load_k(col_at(0), half_at(0), K0, KG0);
   load_v(col_at(0), half_at(0), V0);
-  load_k(col_at(1), half_at(1), K1);
+  load_k(col_at(1), half_at(1), K1, KG1);
   const int k2 = col_at(2);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   qk(K0, s_a);
-  apply_opts(s_a, col_at(0), half_at(0));
+  apply_opts(s_a, col_at(0), half_at(0), seg_bits(KG0));
   mx_a = tile_max(s_a);
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();  // M_{-1}: K0 free
-  load_k(k2, half_at(2), K0);
+  load_k(k2, half_at(2), K0, KG0);
 
   // One step; Kq is K[(t+1)%2], Vn is V[(t+1)%2], Vc is V[t%2].  MORE:
   // tile t+1 exists (every step but the row's last).
-  auto step = [&](auto more_tag, int t, __bf16 *Kq, __bf16 *Vn, const __bf16 *Vc,
+  auto step = [&](auto more_tag, int t, __bf16 *Kq, int32_t *KGq, __bf16 *Vn, const __bf16 *Vc,
                   f32x16 (&s_cur)[JT], f32x16 (&s_nxt)[JT], float &mx_cur, float &mx_nxt,
                   int &cv) {
     constexpr bool MORE = decltype(more_tag)::value;
@@ -955,15 +997,16 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     rescale(mx_cur);
     bf16x8 pf[2 * JT];
     if constexpr (MORE) qk(Kq, s_nxt);
+    const uint32_t segbits = MORE && SEG ? seg_bits(KGq) : 0u;
     exp_pack(s_cur, pf);
     if constexpr (MORE) sched_interleave<JT * QC, JT * QC, kReadAheadK, 3 * 16 * JT / (JT * QC)>();
     __builtin_amdgcn_s_waitcnt(kVmWait);  // V_t landed
     __builtin_amdgcn_sched_barrier(0);
     block_barrier();
-    load_k(kcol, half_at(t + 3), Kq);
+    load_k(kcol, half_at(t + 3), Kq, KGq);
     pv(pf, Vc);
     if constexpr (MORE) {
-      apply_opts(s_nxt, vcol, half_at(t + 1));
+      apply_opts(s_nxt, vcol, half_at(t + 1), segbits);
       mx_nxt = tile_max(s_nxt);
       sched_interleave<JT * 2 * DT, 4 * JT * DT, kReadAheadV, 1>();
     } else {
@@ -975,14 +1018,14 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   using Last = std::false_type;
   int t = 0;
   for (; t + 2 < n; t += 2) {
-    step(More{}, t, K1, V1, V0, s_a, s_b, mx_a, mx_b, cv0);
-    step(More{}, t + 1, K0, V0, V1, s_b, s_a, mx_b, mx_a, cv1);
+    step(More{}, t, K1, KG1, V1, V0, s_a, s_b, mx_a, mx_b, cv0);
+    step(More{}, t + 1, K0, KG0, V0, V1, s_b, s_a, mx_b, mx_a, cv1);
   }
   if (t + 1 < n) {
-    step(More{}, t, K1, V1, V0, s_a, s_b, mx_a, mx_b, cv0);
-    step(Last{}, t + 1, K0, V0, V1, s_b, s_a, mx_b, mx_a, cv1);
+    step(More{}, t, K1, KG1, V1, V0, s_a, s_b, mx_a, mx_b, cv0);
+    step(Last{}, t + 1, K0, KG0, V0, V1, s_b, s_a, mx_b, mx_a, cv1);
   } else {
-    step(Last{}, t, K1, V1, V0, s_a, s_b, mx_a, mx_b, cv0);
+    step(Last{}, t, K1, KG1, V1, V0, s_a, s_b, mx_a, mx_b, cv0);
   }
   __builtin_amdgcn_s_waitcnt(0);  // no copy may still be landing in the buffers reused below
 
@@ -1048,20 +1091,18 @@ hipError_t launch_one(const void *q, const void *k, const void *v, const int32_t
                        stream, (const T *)q, (const T *)k, (const T *)v, row_ptr, col_idx,
                        row_order, B, H, Mb, Nb, scale * kLog2e, (T *)out, lse, opt);
   } else if constexpr (BS >= 64 && std::is_same<T, __bf16>::value) {
+    constexpr int PC = BS == 128 ? kDmaPieces : kDmaPieces64;
+    constexpr int KS = PC == 2 ? 1 : BS == 128 ? kDmaKeySplit : 2;
     if (opt.qseg == nullptr) {
-      constexpr int PC = BS == 128 ? kDmaPieces : kDmaPieces64;
-      constexpr int KS = PC == 2 ? 1 : BS == 128 ? kDmaKeySplit : 2;
       hipLaunchKernelGGL((bsa_fwd_dma_kernel<BS, D, KS, PC, MASK>), dim3((unsigned)grid),
                          dim3(BS * 2 * KS), 0, stream, (const __bf16 *)q, (const __bf16 *)k,
                          (const __bf16 *)v, row_ptr, col_idx, row_order, B, H, Mb, Nb,
                          scale * kLog2e, (__bf16 *)out, lse, opt);
-    } else {
-      // segment ids are staged beside each K tile by the register-staged
-      // kernel; the copy kernel's fixed-count waits have no slot for them
-      hipLaunchKernelGGL((bsa_fwd32_kernel<BS, D, T, 2, MASK>), dim3((unsigned)grid),
-                         dim3(BS * 4), 0, stream, (const T *)q, (const T *)k, (const T *)v,
-                         row_ptr, col_idx, row_order, B, H, Mb, Nb, scale * kLog2e, (T *)out, lse,
-                         opt);
+    } else {  // segment ids: the instance that also copies the key ids
+      hipLaunchKernelGGL((bsa_fwd_dma_kernel<BS, D, KS, PC, true, true>), dim3((unsigned)grid),
+                         dim3(BS * 2 * KS), 0, stream, (const __bf16 *)q, (const __bf16 *)k,
+                         (const __bf16 *)v, row_ptr, col_idx, row_order, B, H, Mb, Nb,
+                         scale * kLog2e, (__bf16 *)out, lse, opt);
     }
   } else {
     constexpr int KSPLIT = BS >= 64 ? 2 : 1;

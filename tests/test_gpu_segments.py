@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 
 FWD = [(16, 64, "bf16", 160, 160), (16, 32, "f32", 100, 93), (32, 64, "bf16", 256, 256),
        (64, 128, "f32", 320, 320), (64, 128, "bf16", 300, 300), (128, 128, "bf16", 512, 512),
-       (128, 64, "bf16", 500, 450)]
+       (128, 64, "bf16", 500, 450), (64, 64, "bf16", 250, 256), (128, 32, "bf16", 384, 300)]
 
 
 @pytest.mark.parametrize("causal", [False, True])
