@@ -27,8 +27,8 @@ Last, the content-adaptive layout producer runs on the same q and k (block
 means, cosine scores, threshold) under kernels.bsa_layout_adaptive, reported
 against HBM bandwidth for the q and k bytes it must read.  Then two more
 forms of the hot path on the same inputs: the forward over packed sequences
-(segment ids, sequence lengths uniform in [1024, 8192]; it runs the
-register-staged kernel) under kernels.bsa_forward_segments, and the top-k
+(segment ids, sequence lengths uniform in [1024, 8192]) under
+kernels.bsa_forward_segments, and the top-k
 kernel at head size 256 (same indices and sink, fresh q and kv) under
 kernels.topk_sparse_attn_d256.  Last, the second block-sparse workload
 (causal local + global + strided, B2 H16 S16384 bs64 d128) is planned and
