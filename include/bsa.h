@@ -160,8 +160,8 @@ typedef struct {
  *                  h / (H / Hkv) (grouped-query attention);
  *   segment ids:   (the operation's q_segment_ids / kv_segment_ids, for
  *                  several sequences packed into one) s_ij = -inf also where
- *                  q_segment_ids[b, i] != kv_segment_ids[b, j].  bf16 calls
- *                  with bs >= 64 then run the register-staged kernel.
+ *                  q_segment_ids[b, i] != kv_segment_ids[b, j] (int32
+ *                  arrays [B, Sq] and [B, Sk] in device memory).
  * Arguments, layouts and ownership as for bsa_forward; opts is a host pointer
  * read during the call.  Errors as for bsa_forward, plus BSA_ERR_INVALID_ARG
  * for kv_heads < 0 or not dividing H, a soft_cap that is negative or not
