@@ -30,7 +30,9 @@ forms of the hot path on the same inputs: the forward over packed sequences
 (segment ids, sequence lengths uniform in [1024, 8192]) under
 kernels.bsa_forward_segments, and the top-k
 kernel at head size 256 (same indices and sink, fresh q and kv) under
-kernels.topk_sparse_attn_d256.  Last, the second block-sparse workload
+kernels.topk_sparse_attn_d256, and the forward over S - 77 tokens with the
+same layout (every last block cut) under kernels.bsa_forward_ragged, its
+rate counted on whole tiles.  Last, the second block-sparse workload
 (causal local + global + strided, B2 H16 S16384 bs64 d128) is planned and
 its forward timed warm, under kernels.bsa_forward_lgs, and both block-sparse
 workloads are timed cold: before each timed launch a 1 GiB fill evicts L2
@@ -43,7 +45,7 @@ budget per kernel), --copy-calibration (also run one plain elementwise copy
 of 1 GiB, for HBM counter scaling under a profiler), --option-steps N (launches
 of the forward with options; 0 skips that leg), --backward-steps N (calls of
 the backward; 0 skips that leg), --adaptive-steps N (calls of the adaptive
-layout producer; 0 skips that leg), --variant-steps N (calls of each of the two
+layout producer; 0 skips that leg), --variant-steps N (calls of each of the three
 forms above; 0 skips them), --config-steps N (launches of the second workload
 and of each cold-cache leg; 0 skips them).
 
@@ -424,7 +426,7 @@ def main(argv=None) -> int:
         log(f"[bench] adaptive layout: {t_ad:.4f} ms")
 
     def timed(fn, n):
-        for _ in range(2):
+        for _ in range(5):
             fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -435,7 +437,7 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
-    seg_leg = d256_leg = None
+    seg_leg = d256_leg = rag_leg = None
     if args.variant_steps > 0:
         seg = W.packed_segment_ids(B, S, 1024, 8192, seed=7).to(dev)
         plan = bsa.bsa_plan(layout, buf=pbuf)
@@ -462,6 +464,22 @@ def main(argv=None) -> int:
                     "algorithmic_gbs": round(b256 / (t_256 * 1e-3) / 1e9, 1),
                     "pct_hbm_peak": round(100 * b256 / (t_256 * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
         log(f"[bench] top-k at d 256: {t_256:.4f} ms")
+        # lengths that are not a multiple of bs: the same layout over
+        # S' = S - 77 tokens, so every block row and column ends in a cut block
+        S_r = S - 77
+        qr, kr, vr = (t[:, :, :S_r].contiguous() for t in (q, k, v))
+        out_r = torch.empty_like(qr)
+        lse_r = torch.empty((B, H, S_r), dtype=torch.float32, device=dev)
+        plan = bsa.bsa_plan(layout, buf=pbuf)
+        t_rag = timed(lambda: bsa.bsa_forward(qr, kr, vr, plan, fwd.scale, out=out_r, lse=lse_r,
+                                              bs=fwd.bs),
+                      args.variant_steps)
+        rag_tf = f_flops / (t_rag * 1e-3) / 1e12
+        rag_leg = {"avg_ms": round(t_rag, 5), "calls": args.variant_steps,
+                   "seq_len": S_r, "tflops_on_whole_tiles": round(rag_tf, 2),
+                   "pct_bf16_peak": round(100 * rag_tf / PEAK_BF16_TFLOPS, 2)}
+        log(f"[bench] forward with cut last blocks (S = {S_r}): {t_rag:.4f} ms")
+        del qr, kr, vr, out_r, lse_r
 
     def timed_cold(fn, n, flush):
         """Per-launch ms of fn with L2 and the Infinity Cache evicted before each."""
@@ -560,6 +578,8 @@ def main(argv=None) -> int:
         kernels["bsa_forward_segments"] = seg_leg
     if d256_leg is not None:
         kernels["topk_sparse_attn_d256"] = d256_leg
+    if rag_leg is not None:
+        kernels["bsa_forward_ragged"] = rag_leg
     if lgs_leg is not None:
         kernels["bsa_forward_lgs"] = lgs_leg
     if cold_legs is not None:
