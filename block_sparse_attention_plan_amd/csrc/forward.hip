@@ -679,8 +679,8 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   constexpr int NSW = (RPI * NW) % CPR == 0 ? 1 : CPR / ((RPI * NW) % CPR);
   static_assert((RPI * NW * NSW) % CPR == 0 && IPW % NSW == 0, "K swizzle pattern must repeat");
 
-  // Four distinct LDS objects, so that the compiler can tell the tile being
-  // read from the tile being filled and need not wait for the copy in flight.
+  // Four distinct LDS objects, so that the compiler can tell the piece being
+  // read from the piece being filled and need not wait for the copy in flight.
   __shared__ __attribute__((aligned(1024))) __bf16 K0[TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 K1[TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 V0[TILE];
@@ -931,24 +931,25 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
         }
       }
   };
-  // Software pipeline over the row's live tiles u = 0 .. n-1: tile u's K
-  // sits in K0 (u even) or K1 (u odd), its V likewise in V0 / V1.  Step t
-  // has two phases separated by block barriers:
+  // Software pipeline over the row's pieces u = 0 .. n-1 (the live tiles'
+  // pieces in order): piece u's K sits in K0 (u even) or K1 (u odd), its V
+  // likewise in V0 / V1.  Step t has two phases separated by block barriers:
   //   S_t: K_{t+1} has landed; copy V_{t+1} into the V buffer PV(t-1) freed;
-  //        then QK^T of tile t+1 beside the exponentials of tile t.
+  //        then QK^T of piece t+1 beside the exponentials of piece t.
   //   M_t: V_t has landed; copy K_{t+3} into the K buffer QK(t+1) freed;
-  //        then PV of tile t beside the row max of tile t+1.
+  //        then PV of piece t beside the row max of piece t+1.
   // Each copy thus has one and a half steps to land.  Every phase issues
-  // IPW copies (indices past the row's end are clamped, so the last copies
-  // are redundant but harmless) and S_t also a column fetch, so the copy a
-  // phase needs is followed by 2*IPW copies and at most two fetches: waiting
-  // until at most 2*IPW vector-memory loads are in flight proves it has
-  // landed, since loads complete in issue order.  (The count leaves the
-  // fetches out because the compiler deletes those whose result is dead, in
-  // a row's last steps; a spill store in between cannot loosen the wait, as
-  // it only adds to the count.)  Column indices come from a vector load two
-  // steps ahead (lane 0: K column for M_{t+2}, lane 1: V column for S_{t+2});
-  // a scalar load in flight would force every LDS wait in between to drain
+  // IPW copies (SEG instances: IPW + 1 in M_t, the key ids) -- indices past
+  // the row's end are clamped, so the last copies are redundant but
+  // harmless -- and S_t also a column fetch, so the copy a phase needs is
+  // followed by kVmInFlight copies and at most two fetches: waiting until at
+  // most kVmInFlight vector-memory loads are in flight proves it has landed,
+  // since loads complete in issue order.  (The count leaves the fetches out
+  // because the compiler deletes those whose result is dead, in a row's last
+  // steps; a spill store in between cannot loosen the wait, as it only adds
+  // to the count.)  Column indices come from a vector load two steps ahead
+  // (lane 0: K column for M_{t+2}, lane 1: V column for S_{t+2}); a scalar
+  // load in flight would force every LDS wait in between to drain
   // completely.
   // Piece u = 0 .. n-1 is piece u % PIECES of live tile u / PIECES.
   const int n = (end - beg) * PIECES;
@@ -981,8 +982,8 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   __syncthreads();  // M_{-1}: K0 free
   load_k(k2, half_at(2), K0, KG0);
 
-  // One step; Kq is K[(t+1)%2], Vn is V[(t+1)%2], Vc is V[t%2].  MORE:
-  // tile t+1 exists (every step but the row's last).
+  // One step; Kq is K[(t+1)%2] (KGq its key ids), Vn is V[(t+1)%2], Vc is
+  // V[t%2].  MORE: piece t+1 exists (every step but the row's last).
   auto step = [&](auto more_tag, int t, __bf16 *Kq, int32_t *KGq, __bf16 *Vn, const __bf16 *Vc,
                   f32x16 (&s_cur)[JT], f32x16 (&s_nxt)[JT], float &mx_cur, float &mx_nxt,
                   int &cv) {
@@ -990,8 +991,8 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     __builtin_amdgcn_s_waitcnt(kVmWait);  // K_{t+1} landed (this wave's part)
     __builtin_amdgcn_sched_barrier(0);
     block_barrier();
-    const int kcol = __builtin_amdgcn_readlane(cv, 0);  // column of tile t+3
-    const int vcol = __builtin_amdgcn_readlane(cv, 1);  // column of tile t+1
+    const int kcol = __builtin_amdgcn_readlane(cv, 0);  // column of piece t+3's tile
+    const int vcol = __builtin_amdgcn_readlane(cv, 1);  // column of piece t+1's tile
     cv = fetch_cols(t + 5, t + 3);
     load_v(vcol, half_at(t + 1), Vn);
     rescale(mx_cur);
