@@ -13,9 +13,9 @@
 //          fixed order, then the unit vector (zero for a zero sum) into the
 //          workspace.  Reads q and k once: bound by HBM.
 //   score  one workgroup per (head, 16 block rows, 64 block columns): the
-//          unit vectors staged in LDS (rows padded by one float), one fp32
-//          dot product per block pair, the threshold, and optionally the
-//          scores themselves.  Under the causal rule, a tile wholly above
+//          unit vectors staged in LDS with 16-byte copies (rows padded by
+//          four floats), each thread 2 x 2 fp32 dot products from 16-byte
+//          reads, the threshold, and optionally the scores themselves.  Under the causal rule, a tile wholly above
 //          the diagonal only writes zeros when no scores are asked for.
 #include "bsa_device.h"
 #include "bsa_internal.h"
@@ -91,9 +91,9 @@ __global__ void __launch_bounds__(256) adaptive_score_kernel(const float *__rest
                                                              int32_t keep_diagonal,
                                                              int32_t *__restrict__ layout,
                                                              float *__restrict__ scores) {
-  constexpr int STR = D + 1;
-  __shared__ float qs[kTileM * STR];
-  __shared__ float ks[kTileN * STR];
+  constexpr int STR = D + 4;   // rows 16-byte aligned; 4 floats of padding keep reads conflict-free
+  __shared__ __attribute__((aligned(16))) float qs[kTileM * STR];
+  __shared__ __attribute__((aligned(16))) float ks[kTileN * STR];
   const int h = blockIdx.z;
   const int m0 = blockIdx.y * kTileM, n0 = blockIdx.x * kTileN;
   const int tid = threadIdx.x;
@@ -107,39 +107,49 @@ __global__ void __launch_bounds__(256) adaptive_score_kernel(const float *__rest
   }
   const float *qu = unit + ((int64_t)h * Mb) * D;
   const float *ku = unit + ((int64_t)H * Mb + (int64_t)(h / g) * Nb) * D;
-  for (int i = tid; i < kTileM * D; i += 256) {
-    const int r = i / D, c = i % D;
-    qs[r * STR + c] = m0 + r < Mb ? qu[(int64_t)(m0 + r) * D + c] : 0.f;
+  for (int i = tid; i < kTileM * D / 4; i += 256) {
+    const int r = i / (D / 4), c4 = i % (D / 4);
+    *reinterpret_cast<f32x4 *>(&qs[r * STR + 4 * c4]) =
+        m0 + r < Mb ? *reinterpret_cast<const f32x4 *>(&qu[(int64_t)(m0 + r) * D + 4 * c4]) : f32x4{};
   }
-  for (int i = tid; i < kTileN * D; i += 256) {
-    const int r = i / D, c = i % D;
-    ks[r * STR + c] = n0 + r < Nb ? ku[(int64_t)(n0 + r) * D + c] : 0.f;
+  for (int i = tid; i < kTileN * D / 4; i += 256) {
+    const int r = i / (D / 4), c4 = i % (D / 4);
+    *reinterpret_cast<f32x4 *>(&ks[r * STR + 4 * c4]) =
+        n0 + r < Nb ? *reinterpret_cast<const f32x4 *>(&ku[(int64_t)(n0 + r) * D + 4 * c4]) : f32x4{};
   }
   __syncthreads();
-  const int nl = tid % kTileN, ml = tid / kTileN;   // block rows ml, ml+4, ml+8, ml+12
-  const int n = n0 + nl;
-  if (n >= Nb) return;
-  // each key element read from LDS serves the four block rows (the query
-  // elements are the same address across the wave: a broadcast)
-  float dots[kTileM / 4] = {};
-#pragma unroll 8
-  for (int c = 0; c < D; ++c) {
-    const float kc = ks[nl * STR + c];
+  // thread: block rows 2rg, 2rg + 1 and block columns cg, cg + 32 of the tile
+  const int cg = tid % 32, rg = tid / 32;
+  float dots[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+#pragma unroll 4
+  for (int c4 = 0; c4 < D / 4; ++c4) {
+    f32x4 qv[2], kv[2];
 #pragma unroll
-    for (int j = 0; j < kTileM / 4; ++j) dots[j] = fmaf(qs[(ml + 4 * j) * STR + c], kc, dots[j]);
+    for (int i = 0; i < 2; ++i) {
+      qv[i] = *reinterpret_cast<const f32x4 *>(&qs[(2 * rg + i) * STR + 4 * c4]);
+      kv[i] = *reinterpret_cast<const f32x4 *>(&ks[(cg + 32 * i) * STR + 4 * c4]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dots[i][j] = fmaf(qv[i][e], kv[j][e], dots[i][j]);
   }
 #pragma unroll
-  for (int j = 0; j < kTileM / 4; ++j) {
-    const int m = m0 + ml + 4 * j;
-    if (m >= Mb) break;
-    const float dot = dots[j];
-    bool live = dot >= tau;
-    if (causal && n > m) live = false;
-    if (keep_diagonal && n == m) live = true;
-    const int64_t o = ((int64_t)h * Mb + m) * Nb + n;
-    layout[o] = live ? 1 : 0;
-    if (scores) scores[o] = dot;
-  }
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int m = m0 + 2 * rg + i, n = n0 + cg + 32 * j;
+      if (m >= Mb || n >= Nb) continue;
+      const float dot = dots[i][j];
+      bool live = dot >= tau;
+      if (causal && n > m) live = false;
+      if (keep_diagonal && n == m) live = true;
+      const int64_t o = ((int64_t)h * Mb + m) * Nb + n;
+      layout[o] = live ? 1 : 0;
+      if (scores) scores[o] = dot;
+    }
 }
 
 template <typename T, int D>
