@@ -25,13 +25,13 @@ namespace {
 
 template <typename T> __device__ __forceinline__ void load8f(const T *p, float (&x)[8]);
 template <> __device__ __forceinline__ void load8f<__bf16>(const __bf16 *p, float (&x)[8]) {
-  const bf16x8 v = *reinterpret_cast<const bf16x8 *>(p);
+  const bf16x8 v = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(p));
 #pragma unroll
   for (int i = 0; i < 8; ++i) x[i] = (float)v[i];
 }
 template <> __device__ __forceinline__ void load8f<float>(const float *p, float (&x)[8]) {
-  const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
-  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+  const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+  const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p + 4));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     x[i] = a[i];
