@@ -12,9 +12,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define BSA_LDS __attribute__((address_space(3)))
 
@@ -65,21 +63,6 @@ __device__ __forceinline__ float sum_xor32(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// LDS transpose read of 4 bf16 values.  Inside each group of 16 lanes, lane
-// s supplies the address of a 4-element (8-byte) chunk; lane t receives
-// element t%4 of the chunks supplied by lanes 4e + t/4 (e = 0..3) of its
-// group.  With lane s = 4e' + c pointing at row (k0 + e') and columns
-// (n0 + 4c .. n0 + 4c + 3) of a row-major [k][n] tile, lane t receives
-// tile[k0 + e][n0 + t] for e = 0..3: four consecutive k of column t.
-// acc + x[2i] + x[2i+1] for a packed bf16 pair of x (v_dot2c_f32_bf16 with
-// a ones vector: products are exact, the sum is taken in fp32).
-__device__ __forceinline__ float sum2_bf16(bf16x8 x, int i, float acc) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t pair = {x[2 * i], x[2 * i + 1]};
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(pair, ones, acc, false);
-}
-
 // The tanh logit cap applied to a raw score s (before scaling): returns
 // s' with scale * s' = cap * tanh(scale * s / cap), given k2 =
 // 2 * scale * log2(e) / cap and b = cap / scale; tanh(y) = 1 - 2 / (e^(2y) + 1)
@@ -122,6 +105,12 @@ __device__ __forceinline__ void copy4_to_lds(__amdgpu_buffer_rsrc_t rs, void *ld
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (BSA_LDS void *)lds_base, 4, voff, soff, 0, 0);
 }
 
+// LDS transpose read of 4 bf16 values.  Inside each group of 16 lanes, lane
+// s supplies the address of a 4-element (8-byte) chunk; lane t receives
+// element t%4 of the chunks supplied by lanes 4e + t/4 (e = 0..3) of its
+// group.  With lane s = 4e' + c pointing at row (k0 + e') and columns
+// (n0 + 4c .. n0 + 4c + 3) of a row-major [k][n] tile, lane t receives
+// tile[k0 + e][n0 + t] for e = 0..3: four consecutive k of column t.
 __device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16 *lds_ptr) {
   i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BSA_LDS i16x4 *)(lds_ptr));
   return __builtin_bit_cast(bf16x4, r);
@@ -134,15 +123,11 @@ __device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
   return r;
 }
 
-}  // namespace bsa
-
-namespace bsa {
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
 // D = A * B + C with 16x16x16 bf16 operands (4 k-values per lane, lane l
 // holds k = 4*(l/16) .. +3); result layout as for mfma16.
 __device__ __forceinline__ f32x4 mfma16k16(bf16x4 a, bf16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
-                                                   __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                   __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
 }
 // Schedule pattern for one straight-line region: N MFMAs, each followed by
 // V VALU instructions and R LDS reads, with P reads issued ahead of the
