@@ -1,4 +1,5 @@
-"""Seeded randomized parity sweep of the forward and the backward.
+"""Seeded randomized parity sweep of the forward, the backward and the top-k
+gathered attention.
 
 Each case draws every free choice at once from a fixed seed: kernel family
 (block size, head dim, dtype), batch, query heads and a dividing number of
@@ -8,7 +9,9 @@ cap, causal mask, packed-sequence segment ids).  The combinations the
 hand-picked tests do not name are where a kernel's instance selection or an
 option's interaction with a cut block can go wrong.  Every case is checked
 against the fp64 oracle with the tolerances of the whole-block tests; the
-case's parameters are printed before it runs.
+case's parameters are printed before it runs.  The top-k cases draw head
+size, head count (1..64), batch, positions, table size, top-k, the share of
+-1 slots, the sink, repeated indices and entries outside [0, N).
 """
 
 import numpy as np
@@ -135,3 +138,49 @@ def test_backward_sweep(gpu, seed):
         assert np.all(np.abs(dsink.cpu().numpy() - rs) <= bound + 1e-6)
     else:
         assert dsink is None
+
+
+TOPK_SEEDS = list(range(9700, 9736))
+
+
+def draw_topk_case(seed: int):
+    r = np.random.default_rng(seed)
+    d = int(r.choice([128, 256, 512]))
+    H = int(r.integers(1, 65))
+    B, M = int(r.integers(1, 3)), int(r.integers(1, 6))
+    N = int(r.integers(1, 600))
+    topk = int(r.integers(1, N + 1))
+    drop = float(r.choice([0.0, 0.1, 0.5, 0.95]))
+    with_sink = bool(r.random() < 0.6)
+    dups = bool(r.random() < 0.3)       # indices drawn with replacement
+    wild = bool(r.random() < 0.3)       # some entries outside [0, N) other than -1
+    return dict(d=d, H=H, B=B, M=M, N=N, topk=topk, drop=drop, with_sink=with_sink, dups=dups,
+                wild=wild)
+
+
+@pytest.mark.parametrize("seed", TOPK_SEEDS)
+def test_topk_sweep(gpu, seed):
+    c = draw_topk_case(seed)
+    say(f"[sweep] topk seed={seed} {c}")
+    t = W.make_topk("sweep_topk", B=c["B"], M=c["M"], H=c["H"], d=c["d"], N=c["N"],
+                    topk=c["topk"], seed=seed, drop=0.0, with_sink=c["with_sink"])
+    r = np.random.default_rng(seed + 1)
+    if c["dups"]:
+        idx = r.integers(0, c["N"], size=(c["B"], c["M"], c["topk"])).astype(np.int32)
+    else:
+        idx = t.idx.numpy().copy()
+    idx[r.random(idx.shape) < c["drop"]] = -1
+    if c["wild"]:
+        wild = r.random(idx.shape) < 0.1
+        idx[wild] = r.choice([-7, c["N"], c["N"] + 3, 2 ** 31 - 1], size=int(wild.sum()))
+    sink = t.sink.to(gpu) if c["with_sink"] else None
+    out = bsa.topk_sparse_attn(t.q.to(gpu), t.kv.to(gpu), torch.from_numpy(idx).to(gpu), sink,
+                               t.scale)
+    torch.cuda.synchronize()
+    ref_idx = idx.copy()
+    ref_idx[(ref_idx < 0) | (ref_idx >= c["N"])] = -1
+    ref = O.topk_attention(to64(t.q), to64(t.kv), ref_idx,
+                           t.sink.numpy() if c["with_sink"] else None, t.scale)
+    compare(to64(out), ref, f"topk sweep {seed}")
+    empty = (ref_idx < 0).all(axis=-1)       # positions without a valid slot give zeros
+    assert torch.all(out.cpu()[torch.from_numpy(empty)] == 0)
