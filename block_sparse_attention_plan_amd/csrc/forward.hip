@@ -818,6 +818,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   // Bit 16 jt + e set: score e of block jt belongs to a key of another
   // segment.  Read from the piece's ids in the phase that computed its
   // scores, before the next barrier lets its buffer be refilled.
+  constexpr uint32_t kSegAllOther = JT * 16 >= 32 ? 0xffffffffu : (1u << (JT * 16)) - 1u;
   auto seg_bits = [&](const int32_t *ids) -> uint32_t {
     uint32_t bits = 0;
     if constexpr (SEG) {
@@ -986,7 +987,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   // V[t%2].  MORE: piece t+1 exists (every step but the row's last).
   auto step = [&](auto more_tag, int t, __bf16 *Kq, int32_t *KGq, __bf16 *Vn, const __bf16 *Vc,
                   f32x16 (&s_cur)[JT], f32x16 (&s_nxt)[JT], float &mx_cur, float &mx_nxt,
-                  int &cv) {
+                  bool &sk_cur, bool &sk_nxt, int &cv) {
     constexpr bool MORE = decltype(more_tag)::value;
     __builtin_amdgcn_s_waitcnt(kVmWait);  // K_{t+1} landed (this wave's part)
     __builtin_amdgcn_sched_barrier(0);
@@ -997,36 +998,62 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     load_v(vcol, half_at(t + 1), Vn);
     rescale(mx_cur);
     bf16x8 pf[2 * JT];
-    if constexpr (MORE) qk(Kq, s_nxt);
-    const uint32_t segbits = MORE && SEG ? seg_bits(KGq) : 0u;
-    exp_pack(s_cur, pf);
-    if constexpr (MORE) sched_interleave<JT * QC, JT * QC, kReadAheadK, 3 * 16 * JT / (JT * QC)>();
+    uint32_t segbits = 0u;
+    if constexpr (SEG) {
+      // With segment ids, a piece none of whose keys shares a segment with
+      // any of this wave's queries has only -inf scores: its weights are
+      // exactly zero, so its score and output products are skipped (a wave
+      // vote; the copies still run, as every wave shares them).
+      if constexpr (MORE) {
+        segbits = seg_bits(KGq);
+        sk_nxt = !__any(segbits != kSegAllOther);
+        if (!sk_nxt) qk(Kq, s_nxt);
+        if (!sk_cur) exp_pack(s_cur, pf);
+      } else {
+        if (!sk_cur) exp_pack(s_cur, pf);
+      }
+    } else {
+      if constexpr (MORE) qk(Kq, s_nxt);
+      exp_pack(s_cur, pf);
+      if constexpr (MORE) sched_interleave<JT * QC, JT * QC, kReadAheadK, 3 * 16 * JT / (JT * QC)>();
+    }
     __builtin_amdgcn_s_waitcnt(kVmWait);  // V_t landed
     __builtin_amdgcn_sched_barrier(0);
     block_barrier();
     load_k(kcol, half_at(t + 3), Kq, KGq);
-    pv(pf, Vc);
-    if constexpr (MORE) {
-      apply_opts(s_nxt, vcol, half_at(t + 1), segbits);
-      mx_nxt = tile_max(s_nxt);
-      sched_interleave<JT * 2 * DT, 4 * JT * DT, kReadAheadV, 1>();
+    if constexpr (SEG) {
+      const bool opts_nxt = MORE && !sk_nxt;
+      if (!sk_cur) pv(pf, Vc);
+      if (opts_nxt) {
+        apply_opts(s_nxt, vcol, half_at(t + 1), segbits);
+        mx_nxt = tile_max(s_nxt);
+      }
+      if (MORE && sk_nxt) mx_nxt = -__builtin_inff();   // no rescale for a skipped piece
     } else {
-      sched_interleave<JT * 2 * DT, 4 * JT * DT, kReadAheadV, 0>();
+      pv(pf, Vc);
+      if constexpr (MORE) {
+        apply_opts(s_nxt, vcol, half_at(t + 1), segbits);
+        mx_nxt = tile_max(s_nxt);
+        sched_interleave<JT * 2 * DT, 4 * JT * DT, kReadAheadV, 1>();
+      } else {
+        sched_interleave<JT * 2 * DT, 4 * JT * DT, kReadAheadV, 0>();
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
   using More = std::true_type;
   using Last = std::false_type;
   int t = 0;
+  bool sk_a = false, sk_b = false;   // piece skipped (segment ids only); piece 0 never is
   for (; t + 2 < n; t += 2) {
-    step(More{}, t, K1, KG1, V1, V0, s_a, s_b, mx_a, mx_b, cv0);
-    step(More{}, t + 1, K0, KG0, V0, V1, s_b, s_a, mx_b, mx_a, cv1);
+    step(More{}, t, K1, KG1, V1, V0, s_a, s_b, mx_a, mx_b, sk_a, sk_b, cv0);
+    step(More{}, t + 1, K0, KG0, V0, V1, s_b, s_a, mx_b, mx_a, sk_b, sk_a, cv1);
   }
   if (t + 1 < n) {
-    step(More{}, t, K1, KG1, V1, V0, s_a, s_b, mx_a, mx_b, cv0);
-    step(Last{}, t + 1, K0, KG0, V0, V1, s_b, s_a, mx_b, mx_a, cv1);
+    step(More{}, t, K1, KG1, V1, V0, s_a, s_b, mx_a, mx_b, sk_a, sk_b, cv0);
+    step(Last{}, t + 1, K0, KG0, V0, V1, s_b, s_a, mx_b, mx_a, sk_b, sk_a, cv1);
   } else {
-    step(Last{}, t, K1, KG1, V1, V0, s_a, s_b, mx_a, mx_b, cv0);
+    step(Last{}, t, K1, KG1, V1, V0, s_a, s_b, mx_a, mx_b, sk_a, sk_b, cv0);
   }
   __builtin_amdgcn_s_waitcnt(0);  // no copy may still be landing in the buffers reused below
 
