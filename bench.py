@@ -110,6 +110,23 @@ def measured_traffic(kernel: str):
     return ent.get("bytes_per_launch")
 
 
+def same_segment_tiles(layout: np.ndarray, seg: np.ndarray, bs: int) -> int:
+    """Live tiles (over the batch) whose query and key blocks can share a
+    segment: the id ranges of the two blocks overlap.  For packed sequences
+    (ids non-decreasing along a row) these are exactly the tiles with a
+    same-segment (query, key) pair; the others are wholly masked."""
+    B, S = seg.shape
+    nb = -(-S // bs)
+    pad = np.concatenate([seg, np.repeat(seg[:, -1:], nb * bs - S, axis=1)], axis=1)
+    blocks = pad.reshape(B, nb, bs)
+    lo, hi = blocks.min(-1), blocks.max(-1)
+    total = 0
+    for b in range(B):
+        overlap = (hi[b][None, :] >= lo[b][:, None]) & (lo[b][None, :] <= hi[b][:, None])
+        total += int((layout.astype(bool) & overlap[None, :layout.shape[1], :layout.shape[2]]).sum())
+    return total
+
+
 def percentiles(ms) -> dict:
     """p10 / median / p90 of per-launch times (ms)."""
     a = np.asarray(ms, dtype=np.float64)
@@ -445,10 +462,13 @@ def main(argv=None) -> int:
                                               q_segment_ids=seg, kv_segment_ids=seg),
                       args.variant_steps)
         seg_tf = f_flops / (t_seg * 1e-3) / 1e12
+        same = same_segment_tiles(fwd.layout, seg.cpu().numpy(), fwd.bs)
         seg_leg = {"avg_ms": round(t_seg, 5), "calls": args.variant_steps,
                    "segments": "packed, lengths uniform in [1024, 8192]",
                    "tflops": round(seg_tf, 2),
-                   "pct_bf16_peak": round(100 * seg_tf / PEAK_BF16_TFLOPS, 2)}
+                   "pct_bf16_peak": round(100 * seg_tf / PEAK_BF16_TFLOPS, 2),
+                   "live_tiles_with_same_segment_keys": same,
+                   "share_of_live_tiles": round(same / (int(fwd.layout.sum()) * B), 4)}
         log(f"[bench] forward with segment ids: {t_seg:.4f} ms")
         rng = np.random.default_rng(8)
         q256 = torch.from_numpy(rng.standard_normal((Bq, M, Hq, 256), dtype=np.float32)).to(

@@ -80,3 +80,16 @@ def test_summarize_counters_scales_by_the_calibration_copy(tmp_path):
     assert res["topk_sparse_attn"]["read_bytes"] == pytest.approx(10.0 * 1024 * 2.0)
     assert json.loads(out.read_text())["bsa_forward"]["source_sha"] == \
         bench.source_hash(bench.KERNEL_SOURCES["bsa_forward"])
+
+
+def test_same_segment_tiles_by_hand():
+    # bs 2, blocks of ids [0 0] [0 1] [1 1]: block 0 and block 2 share no segment
+    seg = np.array([[0, 0, 0, 1, 1, 1]], dtype=np.int32)
+    full = np.ones((1, 3, 3), dtype=np.int32)
+    assert bench.same_segment_tiles(full, seg, 2) == 7
+    lower = np.tril(np.ones((3, 3), dtype=np.int32))[None]
+    assert bench.same_segment_tiles(lower, seg, 2) == 5
+    # a cut last block takes the last id; two batch items add up: blocks
+    # [0 0] [1 1] [2 2] overlap only themselves, a single segment everything
+    seg2 = np.array([[0, 0, 1, 1, 2], [5, 5, 5, 5, 5]], dtype=np.int32)
+    assert bench.same_segment_tiles(full, seg2, 2) == 3 + 9
