@@ -83,3 +83,35 @@ def test_backward_segments(gpu, bs, d, S, causal):
     w = np.exp(sk64[None, :, None] - l64)
     bound = 2.0 * 2.0 ** -9 * (w * np.abs(to64(dout) * o64).sum(-1)).sum(axis=(0, 2))
     assert np.all(np.abs(dsink.cpu().numpy() - rs) <= bound + 1e-6)
+
+
+@pytest.mark.parametrize("bs,d,lengths", [(128, 128, (256, 384, 128, 256)),
+                                          (64, 128, (64, 320, 192, 448)),
+                                          (64, 64, (128, 64, 64, 256, 512))])
+def test_forward_segments_equal_reduced_layout(gpu, bs, d, lengths):
+    """Segments that start and end on block boundaries mask exactly the tiles
+    between different segments, so the forward with segment ids (which skips
+    the pieces whose keys all lie in other segments) equals the forward
+    without them on the layout with those tiles removed."""
+    S = sum(lengths)
+    H, nb = 2, S // bs
+    seg = np.repeat(np.arange(len(lengths), dtype=np.int32), lengths)[None]     # [1, S]
+    rng = np.random.default_rng(S + bs)
+    lay = (rng.random((H, nb, nb)) < 0.6).astype(np.int32)
+    lay[:, np.arange(nb), np.arange(nb)] = 1
+    blk = seg[0, ::bs]
+    reduced = lay * (blk[:, None] == blk[None, :])[None].astype(np.int32)
+    x = W.make_bsa("segments_reduced", B=1, H=H, S=S, bs=bs, d=d, dtype="bf16",
+                   layout="given", layout_array=lay, seed=S)
+    say(f"[segments] reduced layout bs={bs} d={d} lengths={lengths}")
+    q, k, v = x.q.to(gpu), x.k.to(gpu), x.v.to(gpu)
+    sg = torch.from_numpy(seg).to(gpu)
+    plan, _ = check_plan(gpu, lay)
+    plan_r, _ = check_plan(gpu, reduced)
+    out, lse = bsa.bsa_forward(q, k, v, plan, x.scale, bs=bs, q_segment_ids=sg, kv_segment_ids=sg)
+    out_r, lse_r = bsa.bsa_forward(q, k, v, plan_r, x.scale, bs=bs)
+    torch.cuda.synchronize()
+    assert torch.allclose(out.float(), out_r.float(), atol=2 ** -8, rtol=0)
+    assert torch.allclose(lse, lse_r, atol=1e-5, rtol=0)
+    ref, _ = O.attention_live_tiles(to64(x.q), to64(x.k), to64(x.v), reduced, bs, x.scale)
+    compare(to64(out), ref, f"segments reduced bs={bs} d={d}")
