@@ -387,7 +387,7 @@ int topk_sparse_attn(const void *q, const void *kv, const int32_t *idx, const fl
   if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 16) || !aligned(idx, 4) ||
       (attn_sink != nullptr && !aligned(attn_sink, 4)))
     return fail(BSA_ERR_MISALIGNED, "topk_sparse_attn: tensors must be 16-byte aligned");
-  if ((int64_t)B * M > 0x7fffffffLL)
+  if ((int64_t)B * M > 0x7fffffffLL || ((int64_t)H + 63) / 64 > 65535)
     return fail(BSA_ERR_UNSUPPORTED, "topk_sparse_attn: problem too large");
   if ((int64_t)N * d * 2 > 0xfffffc00LL)  // the kernel's row offsets wrap past this for -1
     return fail(BSA_ERR_UNSUPPORTED, "topk_sparse_attn: one batch of kv exceeds 4 GiB - 1 KiB");

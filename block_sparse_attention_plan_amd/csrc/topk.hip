@@ -26,6 +26,9 @@
 //   after a block barrier, accumulates O^T += KV^T P^T for d columns
 //     w*d/4 .. (w+1)*d/4 - 1 of all 64 heads (32x32x16 MFMA, KV^T by LDS
 //     transpose reads of its quarter of the chunk only).
+// A workgroup serves 64 heads; with more heads the grid's second dimension
+// runs over groups of 64 (heads 64g .. 64g+63), each gathering the
+// position's rows for its own heads.
 // Splitting the output product over d rather than heads transposes each
 // gathered element once per workgroup instead of once per wave; the LDS
 // transpose reads were what bounded the head-split form.  The two chunk
@@ -69,12 +72,14 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
 
   const int64_t pos = blockIdx.x;  // b * M + m
   const int64_t b = pos / M;
+  const int hb = 64 * blockIdx.y;  // first head of this workgroup's group
   const int tid = threadIdx.x, lane = tid % 64;
   const int wid = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform, kept in SGPRs
   const int G = lane / 16, li = lane % 16;
   const int h2 = lane / 32, l32 = lane % 32;
-  const int h = 16 * wid + li;
-  const bool wave_active = 16 * wid < H;
+  const int h = 16 * wid + li;          // head inside the group (LDS rows of P, factors)
+  const int hg = hb + h;                // head index in q, out and sink
+  const bool wave_active = hb + 16 * wid < H;
   const int d0 = wid * DW;
 
   const __bf16 *kvb = kv + b * (int64_t)N * D;
@@ -87,8 +92,8 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
   bf16x8 qf[QC];
 #pragma unroll
   for (int c = 0; c < QC; ++c) {
-    if (h < H)
-      qf[c] = *reinterpret_cast<const bf16x8 *>(q + (pos * H + h) * (int64_t)D + 32 * c + 8 * G);
+    if (hg < H)
+      qf[c] = *reinterpret_cast<const bf16x8 *>(q + (pos * H + hg) * (int64_t)D + 32 * c + 8 * G);
     else
       qf[c] = bf16x8{};
   }
@@ -234,13 +239,13 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
   // 1/l of each head (with the sink) through As, then each wave writes its
   // d columns of every head.
   float l_tot = sum_xor32(sum_xor16(l_run));
-  if (sink != nullptr && h < H) l_tot += fast_exp2(fmaf(sink[h], kLog2e, -m_run));
+  if (sink != nullptr && hg < H) l_tot += fast_exp2(fmaf(sink[hg], kLog2e, -m_run));
   if (wave_active && G == 0) As[h] = l_tot > 0.f ? 1.f / l_tot : 0.f;
   __syncthreads();
   const float inv[2] = {As[l32], As[32 + l32]};
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
-    const int head = 32 * ht + l32;
+    const int head = hb + 32 * ht + l32;
     if (head >= H) continue;
     __bf16 *oh = out + (pos * H + head) * (int64_t)D + d0 + 4 * h2;
 #pragma unroll
@@ -258,7 +263,7 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
 }  // namespace
 
 bool topk_supported(int32_t H, int32_t d) {
-  return H >= 1 && H <= 64 && (d == 128 || d == 256 || d == 512);
+  return H >= 1 && (d == 128 || d == 256 || d == 512);
 }
 
 hipError_t launch_topk(const void *q, const void *kv, const int32_t *idx, const float *sink,
@@ -266,9 +271,11 @@ hipError_t launch_topk(const void *q, const void *kv, const int32_t *idx, const 
                        float scale, void *out, hipStream_t stream) {
   if (!topk_supported(H, d)) return hipErrorInvalidValue;
   const int64_t grid = (int64_t)B * M;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t groups = ((int64_t)H + 63) / 64;  // 64 heads per workgroup
+  if (grid > 0x7fffffff || groups > 65535) return hipErrorInvalidValue;
 #define BSA_TOPK_LAUNCH(D_)                                                                    \
-  hipLaunchKernelGGL(topk_kernel<D_>, dim3((unsigned)grid), dim3(256), 0, stream,              \
+  hipLaunchKernelGGL(topk_kernel<D_>, dim3((unsigned)grid, (unsigned)groups), dim3(256), 0,    \
+                     stream,                                                                   \
                      (const __bf16 *)q, (const __bf16 *)kv, idx, sink, M, N, H, topk,           \
                      scale * kLog2e, (__bf16 *)out)
   if (d == 512) BSA_TOPK_LAUNCH(512);

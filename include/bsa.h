@@ -245,8 +245,8 @@ size_t bsa_backward_workspace_bytes(int32_t B, int32_t H, int32_t Sq);
  * load, as in the forward; products accumulate in fp32), bs in {16, 32, 64, 128},
  * d in {32, 64, 128}.
  * Deterministic: no atomics, so repeated calls give identical bits.
- * Errors: as bsa_forward_ex, plus BSA_ERR_UNSUPPORTED for bs = 16,
- * BSA_ERR_BUFFER_TOO_SMALL for a short workspace.
+ * Errors: as bsa_forward_ex, plus BSA_ERR_BUFFER_TOO_SMALL for a short
+ * workspace.
  */
 int bsa_backward(const void *q, const void *k, const void *v, const void *out, const void *dout,
                  const float *lse, const bsa_plan_t *plan, const bsa_plan_cols_t *plan_cols,
@@ -306,8 +306,10 @@ int bsa_layout_adaptive(const void *q, const void *k, int32_t H, int32_t Hkv, in
  *
  *   q     device bf16 [B, M, H, d];  kv device bf16 [B, N, d]
  *   idx   device int32 [B, M, topk]; attn_sink device fp32 [H] or NULL
- *   H in [1, 64]; d in {128, 256, 512}; topk >= 1 (no alignment needed); one batch's kv
- *   (N * d * 2 bytes) at most 4 GiB - 1 KiB
+ *   any H >= 1 (up to 64 * 65535; heads are served in groups of 64, each
+ *   group gathering the position's rows once); d in {128, 256, 512};
+ *   topk >= 1 (no alignment needed); one batch's kv (N * d * 2 bytes) at
+ *   most 4 GiB - 1 KiB
  *   out   device bf16 [B, M, H, d], written
  * Errors: BSA_ERR_INVALID_ARG, BSA_ERR_UNSUPPORTED, BSA_ERR_MISALIGNED,
  * BSA_ERR_HIP.

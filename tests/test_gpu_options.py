@@ -6,8 +6,8 @@ scores, a causal mask on top of the layout and grouped K/V heads.  Each is
 checked alone and all together on every kernel family (bs 16; bs 32; bs >= 64
 fp32; bs >= 64 bf16 with tile copies), with rows that the causal mask empties
 completely, rows with no live tile and a non-square block grid; then all of
-them at once on the 32-head, 32768-token, bs-128 causal workload, on sampled
-row blocks, with two launches bit-identical.  Tolerances as in the plain
+them at once on the 32-head, 32768-token, bs-128 causal workload, on every
+row, with two launches bit-identical.  Tolerances as in the plain
 parity tests.
 """
 
@@ -19,8 +19,9 @@ import block_sparse_attention_plan_amd as bsa
 from block_sparse_attention_plan_amd import workloads as W
 from oracle import bsa_oracle as O
 
-from test_gpu_parity import (_sample_row_blocks, bf16_rounded, check_plan, compare, compare_lse,
-                             say, to64)
+import parity_full as PF
+from test_gpu_parity import (bf16_rounded, check_full, check_plan, compare, compare_lse, say,
+                             to64)
 
 pytestmark = pytest.mark.gpu
 
@@ -114,7 +115,7 @@ def test_forward_options_cap_saturates(gpu):
 
 def test_forward_options_full_workload(gpu):
     """All options at the full 32-head, 32768-token, bs-128 causal workload
-    (eight K/V heads), sampled row blocks against the oracle."""
+    (eight K/V heads); the oracle checks every row."""
     name = "causal_bernoulli_h32_s32768_bs128_d128"
     opts = dict(sink_mean=3.0, soft_cap=1.0, causal=True, Hkv=8)
     say(f"[options] full {name} {opts}: generating inputs")
@@ -125,12 +126,7 @@ def test_forward_options_full_workload(gpu):
     out2, lse2 = _run(gpu, x, plan, opts, 8)
     torch.cuda.synchronize()
     assert torch.equal(out, out2) and torch.equal(lse, lse2), "forward is not deterministic"
-    rows = _sample_row_blocks(x.layout, 1, 40, np.random.default_rng(1))
-    ref, ref_lse = _oracle(x, opts, rows=rows)
-    bs = x.bs
-    sel_o = np.concatenate([to64(out[b, h, m * bs:(m + 1) * bs]) for b, h, m in rows])
-    sel_r = np.concatenate([ref[b, h, m * bs:(m + 1) * bs] for b, h, m in rows])
-    compare(sel_o, sel_r, f"{name} options ({len(rows)} sampled row blocks)")
-    sel_l = np.concatenate([lse[b, h, m * bs:(m + 1) * bs].cpu().numpy() for b, h, m in rows])
-    sel_rl = np.concatenate([ref_lse[b, h, m * bs:(m + 1) * bs] for b, h, m in rows])
-    compare_lse(sel_l, sel_rl, f"{name} options")
+    say(f"[options] full {name}: oracle on every row")
+    agg = PF.bsa_full(x.q, x.k, x.v, x.layout, x.bs, x.scale, out, lse, sink=x.sink,
+                      soft_cap=1.0, causal=True)
+    check_full(agg, f"{name} options")

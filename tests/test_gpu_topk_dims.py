@@ -1,7 +1,8 @@
 """GPU parity of the top-k gathered attention at head sizes 128 and 256 (the
 page's kernel takes d as a parameter) against the fp64 oracle, with the same
 cases as the d = 512 tests: sinks, -1 slots, out-of-range entries, head
-counts that are not multiples of 16, and a position with no valid slot."""
+counts that are not multiples of 16, and a position with no valid slot; and
+head counts above 64 at every head size."""
 
 import numpy as np
 import pytest
@@ -38,3 +39,24 @@ def test_topk_head_dims(gpu, d, H, topk, N, with_sink, drop):
                            t.sink.numpy() if with_sink else None, t.scale)
     compare(to64(out), ref, f"topk d={d} H={H}")
     assert torch.all(out[0, 0] == 0)
+
+
+@pytest.mark.parametrize("d", [128, 256, 512])
+@pytest.mark.parametrize("H,with_sink", [(65, True), (96, False), (128, True), (200, True)])
+def test_topk_many_heads(gpu, d, H, with_sink):
+    """More than 64 heads: the heads are served in groups of 64 (the last
+    group partial), each group gathering the position's rows itself.  Every
+    head of every position against the oracle, including a position with no
+    valid slot and the sink of heads past the first group."""
+    t = W.make_topk("topk_heads", B=2, M=5, H=H, d=d, N=150, topk=90, seed=H + d, drop=0.1,
+                    with_sink=with_sink)
+    idx = t.idx.clone()
+    idx[0, 3] = -1
+    say(f"[topk] many heads d={d} H={H} sink={with_sink}")
+    sink = t.sink.to(gpu) if with_sink else None
+    out = bsa.topk_sparse_attn(t.q.to(gpu), t.kv.to(gpu), idx.to(gpu), sink, t.scale)
+    torch.cuda.synchronize()
+    ref = O.topk_attention(to64(t.q), to64(t.kv), idx.numpy(),
+                           t.sink.numpy() if with_sink else None, t.scale)
+    compare(to64(out), ref, f"topk d={d} H={H}")
+    assert torch.all(out[0, 3] == 0)
