@@ -21,3 +21,13 @@ def gpu():
     import block_sparse_attention_plan_amd as bsa
     bsa.load_library()  # raises when the library is missing: no fallback
     return torch.device("cuda:0")
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Print the statistics of every full-size parity check that ran, so that
+    they appear in the run's output even when test output is captured."""
+    import parity_full
+    if parity_full.REPORT:
+        terminalreporter.section("full-size parity (every row / position against the oracle)")
+        for line in parity_full.REPORT:
+            terminalreporter.write_line(line)

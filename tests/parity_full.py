@@ -27,6 +27,9 @@ import numpy as np
 
 from oracle import bsa_oracle as O
 
+# One line per full-size check that ran (printed in the run's summary).
+REPORT: List[str] = []
+
 # Worker processes: at most 12, within the host cores this process may use.
 MAX_WORKERS = 12
 

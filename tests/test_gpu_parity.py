@@ -169,9 +169,11 @@ def _sample_row_blocks(layout, B, k, rng):
 
 def check_full(agg, what: str, with_lse: bool = True):
     """Aggregate statistics of parity_full against the benchmark spec's bounds."""
-    say(f"  {what}: every row, {agg['slices']} slices: max_abs={agg['max']:.3e} "
-        f"mean_abs={agg['mean']:.3e} worst slice {agg['worst']}"
-        + (f" lse max_abs={agg['lse_max']:.3e}" if with_lse else ""))
+    line = (f"{what}: all {agg['slices']} slices: max_abs={agg['max']:.3e} "
+            f"mean_abs={agg['mean']:.3e} (worst slice {agg['worst']})"
+            + (f", lse max_abs={agg['lse_max']:.3e}" if with_lse else ""))
+    say("  " + line)
+    PF.REPORT.append(line)
     assert agg["finite"], f"{what}: non-finite output"
     assert agg["max"] <= MAX_ABS, what
     assert agg["mean"] <= MEAN_ABS, what
