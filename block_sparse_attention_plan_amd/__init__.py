@@ -12,6 +12,7 @@ missing, every call raises.
     bsa_plan_cols(layout, kv_heads)       -> PlanCols (per-column CSR, backward)
     bsa_backward(q, k, v, out, dout, lse, plan, plan_cols, scale, *, options)
                                           -> (dq, dk, dv, dsink)
+    bsa_backward_noalloc(..., dq=, dk=, dv=, dsink=)  (no allocation; static scratch)
     bsa_layout_adaptive(q, k, bs, tau, causal, keep_diagonal) -> (layout, scores)
     topk_sparse_attn(q, kv, idx, attn_sink, scale) -> out
 """
@@ -35,6 +36,7 @@ __all__ = [
     "PlanCols",
     "bsa_plan_cols",
     "bsa_backward",
+    "bsa_backward_noalloc",
     "bsa_layout_adaptive",
     "topk_sparse_attn",
     "library_path",
@@ -113,6 +115,12 @@ def load_library():
                                  f32, ctypes.POINTER(_FwdOptsT), vp, ctypes.c_size_t, vp, vp, vp,
                                  vp, vp]
     lib.bsa_backward.restype = ctypes.c_int
+    lib.bsa_backward_noalloc_max_rows.argtypes = []
+    lib.bsa_backward_noalloc_max_rows.restype = ctypes.c_size_t
+    lib.bsa_backward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(_PlanT),
+                                         ctypes.POINTER(_PlanColsT), i32, i32, i32, i32, i32, i32,
+                                         i32, f32, ctypes.POINTER(_FwdOptsT), vp, vp, vp, vp, vp]
+    lib.bsa_backward_noalloc.restype = ctypes.c_int
     lib.bsa_layout_adaptive_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.bsa_layout_adaptive_workspace_bytes.restype = ctypes.c_size_t
     lib.bsa_layout_adaptive.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, i32,
@@ -400,21 +408,10 @@ def bsa_plan_cols(layout: torch.Tensor, kv_heads: Optional[int] = None,
     return PlanCols(buf, raw, H, Hkv, Mb, Nb)
 
 
-def bsa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
-                 dout: torch.Tensor, lse: torch.Tensor, plan: Plan, plan_cols: PlanCols,
-                 scale: Optional[float] = None, *, attn_sink: Optional[torch.Tensor] = None,
-                 soft_cap: Optional[float] = None, causal: bool = False,
-                 dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-                 dv: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None, bs: Optional[int] = None,
-                 q_segment_ids: Optional[torch.Tensor] = None,
-                 kv_segment_ids: Optional[torch.Tensor] = None):
-    """Gradients of bsa_forward for the upstream gradient dout.
-
-    q, k, v, scale and the options must be those of the forward call that
-    produced out and lse.  Returns (dq, dk, dv, dsink): dq like q, dk and dv
-    like k, dsink fp32 [H] (None without a sink).  bf16 or fp32 I/O.
-    """
+def _backward_args(q, k, v, out, dout, lse, plan, scale, attn_sink, soft_cap, causal, dq, dk,
+                   dv, dsink, bs, q_segment_ids, kv_segment_ids):
+    """Checks of a backward call; returns the sizes, the outputs (allocated
+    where not given) and the marshalled options."""
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("lse", lse)):
         _require_gpu(name, t)
     if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype) or \
@@ -437,7 +434,6 @@ def bsa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
             raise ValueError("attn_sink must be fp32 [H]")
     if soft_cap is not None and not (math.isfinite(soft_cap) and soft_cap > 0):
         raise ValueError("soft_cap must be finite and > 0")
-    lib = load_library()
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -445,26 +441,84 @@ def bsa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
         _require_gpu(name, t)
         if t.shape != like.shape or t.dtype != like.dtype:
             raise ValueError(f"{name} must match {'q' if like is q else 'k'}")
+    if attn_sink is None:
+        dsink = None
+    elif dsink is None:
+        dsink = torch.empty(H, dtype=torch.float32, device=q.device)
+    else:
+        _require_gpu("dsink", dsink)
+        if dsink.dtype != torch.float32 or tuple(dsink.shape) != (H,):
+            raise ValueError("dsink must be fp32 [H]")
+    qsp, ksp = _segment_args(q_segment_ids, kv_segment_ids, B, Sq, Sk)
+    opts = _FwdOptsT(ctypes.c_void_p(attn_sink.data_ptr() if attn_sink is not None else 0),
+                     float(soft_cap or 0.0), 1 if causal else 0, Hkv, ctypes.c_void_p(qsp),
+                     ctypes.c_void_p(ksp))
+    dtype = BSA_BF16 if q.dtype == torch.bfloat16 else BSA_F32
+    return (B, H, Sq, Sk, bs, d, float(scale), dtype), (dq, dk, dv, dsink), opts
+
+
+def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+
+
+def bsa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                 dout: torch.Tensor, lse: torch.Tensor, plan: Plan, plan_cols: PlanCols,
+                 scale: Optional[float] = None, *, attn_sink: Optional[torch.Tensor] = None,
+                 soft_cap: Optional[float] = None, causal: bool = False,
+                 dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                 dv: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, bs: Optional[int] = None,
+                 q_segment_ids: Optional[torch.Tensor] = None,
+                 kv_segment_ids: Optional[torch.Tensor] = None,
+                 dsink: Optional[torch.Tensor] = None):
+    """Gradients of bsa_forward for the upstream gradient dout.
+
+    q, k, v, scale and the options must be those of the forward call that
+    produced out and lse.  Returns (dq, dk, dv, dsink): dq like q, dk and dv
+    like k, dsink fp32 [H] (None without a sink).  bf16 or fp32 I/O.
+    """
+    sizes, (dq, dk, dv, dsink), opts = _backward_args(
+        q, k, v, out, dout, lse, plan, scale, attn_sink, soft_cap, causal, dq, dk, dv, dsink, bs,
+        q_segment_ids, kv_segment_ids)
+    B, H, Sq, Sk, bs, d, scale, dtype = sizes
+    lib = load_library()
     wbytes = lib.bsa_backward_workspace_bytes(B, H, Sq)
     if workspace is None:
         workspace = torch.empty(wbytes // 4, dtype=torch.float32, device=q.device)
     elif workspace.numel() * workspace.element_size() < wbytes:
         raise ValueError("workspace too small")
-    dsink = torch.empty(H, dtype=torch.float32, device=q.device) if attn_sink is not None else None
-    qsp, ksp = _segment_args(q_segment_ids, kv_segment_ids, B, Sq, Sk)
-    opts = _FwdOptsT(ctypes.c_void_p(attn_sink.data_ptr() if attn_sink is not None else 0),
-                     float(soft_cap or 0.0), 1 if causal else 0, Hkv, ctypes.c_void_p(qsp),
-                     ctypes.c_void_p(ksp))
     _check(lib.bsa_backward(
-        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
-        ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()),
-        ctypes.c_void_p(dout.data_ptr()), ctypes.c_void_p(lse.data_ptr()),
-        ctypes.byref(plan._raw), ctypes.byref(plan_cols._raw), B, H, Sq, Sk, bs, d,
-        BSA_BF16 if q.dtype == torch.bfloat16 else BSA_F32,
-        float(scale), ctypes.byref(opts), ctypes.c_void_p(workspace.data_ptr()),
-        workspace.numel() * workspace.element_size(), ctypes.c_void_p(dq.data_ptr()),
-        ctypes.c_void_p(dk.data_ptr()), ctypes.c_void_p(dv.data_ptr()),
-        ctypes.c_void_p(dsink.data_ptr() if dsink is not None else 0), _stream(q)))
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+        ctypes.byref(plan._raw), ctypes.byref(plan_cols._raw), B, H, Sq, Sk, bs, d, dtype,
+        scale, ctypes.byref(opts), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsink), _stream(q)))
+    return dq, dk, dv, dsink
+
+
+def bsa_backward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                         dout: torch.Tensor, lse: torch.Tensor, plan: Plan, plan_cols: PlanCols,
+                         scale: Optional[float] = None, *, dq: torch.Tensor, dk: torch.Tensor,
+                         dv: torch.Tensor, dsink: Optional[torch.Tensor] = None,
+                         attn_sink: Optional[torch.Tensor] = None,
+                         soft_cap: Optional[float] = None, causal: bool = False,
+                         bs: Optional[int] = None, q_segment_ids: Optional[torch.Tensor] = None,
+                         kv_segment_ids: Optional[torch.Tensor] = None):
+    """bsa_backward for callers that cannot allocate: the outputs dq, dk, dv
+    (and dsink with a sink) are the caller's, and the library's per-row
+    scratch lives in a static device array (at most
+    bsa_backward_noalloc_max_rows() query rows, B*H*Sq).  Calls that overlap
+    on one GPU share that array and race.  Returns (dq, dk, dv, dsink)."""
+    if attn_sink is not None and dsink is None:
+        raise ValueError("bsa_backward_noalloc: pass dsink (fp32 [H]) with attn_sink")
+    sizes, (dq, dk, dv, dsink), opts = _backward_args(
+        q, k, v, out, dout, lse, plan, scale, attn_sink, soft_cap, causal, dq, dk, dv, dsink, bs,
+        q_segment_ids, kv_segment_ids)
+    B, H, Sq, Sk, bs, d, scale, dtype = sizes
+    lib = load_library()
+    _check(lib.bsa_backward_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+        ctypes.byref(plan._raw), ctypes.byref(plan_cols._raw), B, H, Sq, Sk, bs, d, dtype,
+        scale, ctypes.byref(opts), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsink), _stream(q)))
     return dq, dk, dv, dsink
 
 

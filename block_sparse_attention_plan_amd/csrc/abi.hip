@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "bsa.h"
 #include "bsa_internal.h"
@@ -89,6 +90,133 @@ int make_options(const bsa_forward_opts_t *opts, int32_t H, float scale, bsa::Fw
     return fail(BSA_ERR_MISALIGNED, "%s: segment ids must be 4-byte aligned", who);
   fo->qseg = opts->q_segment_ids;
   fo->kseg = opts->kv_segment_ids;
+  return BSA_OK;
+}
+
+}  // namespace
+
+// Scratch of bsa_backward_noalloc: the D and lse*log2(e) values the backward
+// keeps per query row, in a file-scope device array instead of a caller's
+// workspace.  Every GPU the library runs on holds its own copy until the
+// process ends.  Host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device (the array's name is a
+// host-side stand-in, not a device address).
+static constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;  // 2^21 query rows
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current and kept for later calls.
+int scratch_address(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "bsa_backward_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_backward_noalloc: device %d beyond %d", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                      "bsa_backward_noalloc: hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BSA_OK;
+}
+
+// The backward behind both entry points.  With use_scratch the D / lse
+// values go to the static scratch (workspace and workspace_bytes unused);
+// otherwise to the caller's workspace.  Every check runs before any HIP call.
+int backward_impl(const char *who, const void *q, const void *k, const void *v, const void *out,
+                  const void *dout, const float *lse, const bsa_plan_t *plan,
+                  const bsa_plan_cols_t *plan_cols, int32_t B, int32_t H, int32_t Sq, int32_t Sk,
+                  int32_t bs, int32_t d, bsa_dtype_t dtype, float scale,
+                  const bsa_forward_opts_t *opts, bool use_scratch, void *workspace,
+                  size_t workspace_bytes, void *dq, void *dk, void *dv, float *dsink,
+                  void *stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr ||
+      lse == nullptr || dq == nullptr || dk == nullptr || dv == nullptr ||
+      (!use_scratch && workspace == nullptr))
+    return fail(BSA_ERR_INVALID_ARG, "%s: NULL tensor pointer", who);
+  bsa::PlanGeometry g;
+  int st = check_plan(plan, &g);
+  if (st != BSA_OK) return st;
+  bsa::PlanColsGeometry gc;
+  st = check_plan_cols(plan_cols, &gc);
+  if (st != BSA_OK) return st;
+  if (B <= 0 || H <= 0 || Sq <= 0 || Sk <= 0 || bs <= 0 || d <= 0)
+    return fail(BSA_ERR_INVALID_ARG, "%s: sizes must be positive", who);
+  if (H != plan->H || blocks(Sq, bs) != plan->Mb || blocks(Sk, bs) != plan->Nb)
+    return fail(BSA_ERR_PLAN_MISMATCH,
+                "%s: H=%d Sq=%d Sk=%d bs=%d do not match plan H=%d Mb=%d Nb=%d", who, H, Sq,
+                Sk, bs, plan->H, plan->Mb, plan->Nb);
+  if (dtype != BSA_BF16 && dtype != BSA_F32)
+    return fail(BSA_ERR_INVALID_ARG, "%s: unknown dtype %d", who, (int)dtype);
+  if (!(std::isfinite(scale) && scale > 0.f))
+    return fail(BSA_ERR_INVALID_ARG, "%s: scale must be finite and > 0", who);
+  bsa::FwdOptions fo;
+  st = make_options(opts, H, scale, &fo, who);
+  if (st != BSA_OK) return st;
+  fo.sq = Sq;
+  fo.sk = Sk;
+  if (plan_cols->H != H || plan_cols->Mb != plan->Mb || plan_cols->Nb != plan->Nb ||
+      plan_cols->Hkv != H / fo.kv_group)
+    return fail(BSA_ERR_PLAN_MISMATCH,
+                "%s: column plan H=%d Hkv=%d Mb=%d Nb=%d does not match H=%d Hkv=%d "
+                "Mb=%d Nb=%d", who, plan_cols->H, plan_cols->Hkv, plan_cols->Mb, plan_cols->Nb, H,
+                H / fo.kv_group, plan->Mb, plan->Nb);
+  if (!bsa::backward_supported(bs, d))
+    return fail(BSA_ERR_UNSUPPORTED, "%s: no kernel for bs=%d d=%d", who, bs, d);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || (!use_scratch && !aligned(workspace, 16)) ||
+      (dsink != nullptr && !aligned(dsink, 4)))
+    return fail(BSA_ERR_MISALIGNED, "%s: tensors must be 16-byte aligned", who);
+  const size_t ws = bsa_backward_workspace_bytes(B, H, Sq);
+  if (use_scratch) {
+    if (ws > kNoAllocScratchBytes)
+      return fail(BSA_ERR_UNSUPPORTED,
+                  "%s: B*H*Sq = %lld query rows need %zu bytes of scratch; the static scratch "
+                  "holds %zu bytes (%zu rows)", who, (long long)B * H * Sq, ws,
+                  kNoAllocScratchBytes, kNoAllocScratchBytes / (2 * sizeof(float)));
+  } else if (workspace_bytes < ws) {
+    return fail(BSA_ERR_BUFFER_TOO_SMALL, "%s: workspace is %zu bytes, needs %zu", who,
+                workspace_bytes, ws);
+  }
+  const int64_t work = (int64_t)B * H * plan->Mb;
+  const int64_t rows = (int64_t)B * H * Sq;
+  if (work > 0x7ffffff0LL || (int64_t)B * H * plan->Nb > 0x7ffffff0LL)
+    return fail(BSA_ERR_UNSUPPORTED, "%s: problem too large", who);
+  if (use_scratch) {
+    st = scratch_address(&workspace);
+    if (st != BSA_OK) return st;
+  }
+  bsa::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse;
+  a.row_ptr = at<int32_t>(plan->dev_buf, g.off_row_ptr);
+  a.col_idx = at<int32_t>(plan->dev_buf, g.off_col_idx);
+  a.row_order = at<int32_t>(plan->dev_buf, g.off_row_order);
+  a.col_ptr = at<int32_t>(plan_cols->dev_buf, gc.off_col_ptr);
+  a.row_idx = at<int32_t>(plan_cols->dev_buf, gc.off_row_idx);
+  a.col_order = at<int32_t>(plan_cols->dev_buf, gc.off_col_order);
+  a.B = B; a.H = H; a.Mb = plan->Mb; a.Nb = plan->Nb; a.bs = bs; a.d = d;
+  a.f32 = dtype == BSA_F32;
+  a.scale = scale;
+  a.opt = fo;
+  a.Dv = static_cast<float *>(workspace);
+  a.lse2 = static_cast<float *>(workspace) + rows;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.dsink = fo.sink != nullptr ? dsink : nullptr;
+  hipError_t e = bsa::launch_backward(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, who);
   return BSA_OK;
 }
 
@@ -263,69 +391,22 @@ int bsa_backward(const void *q, const void *k, const void *v, const void *out, c
                  bsa_dtype_t dtype, float scale, const bsa_forward_opts_t *opts, void *workspace,
                  size_t workspace_bytes, void *dq, void *dk, void *dv, float *dsink,
                  void *stream) {
-  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr ||
-      lse == nullptr || dq == nullptr || dk == nullptr || dv == nullptr || workspace == nullptr)
-    return fail(BSA_ERR_INVALID_ARG, "bsa_backward: NULL tensor pointer");
-  bsa::PlanGeometry g;
-  int st = check_plan(plan, &g);
-  if (st != BSA_OK) return st;
-  bsa::PlanColsGeometry gc;
-  st = check_plan_cols(plan_cols, &gc);
-  if (st != BSA_OK) return st;
-  if (B <= 0 || H <= 0 || Sq <= 0 || Sk <= 0 || bs <= 0 || d <= 0)
-    return fail(BSA_ERR_INVALID_ARG, "bsa_backward: sizes must be positive");
-  if (H != plan->H || blocks(Sq, bs) != plan->Mb || blocks(Sk, bs) != plan->Nb)
-    return fail(BSA_ERR_PLAN_MISMATCH,
-                "bsa_backward: H=%d Sq=%d Sk=%d bs=%d do not match plan H=%d Mb=%d Nb=%d", H, Sq,
-                Sk, bs, plan->H, plan->Mb, plan->Nb);
-  if (dtype != BSA_BF16 && dtype != BSA_F32)
-    return fail(BSA_ERR_INVALID_ARG, "bsa_backward: unknown dtype %d", (int)dtype);
-  if (!(std::isfinite(scale) && scale > 0.f))
-    return fail(BSA_ERR_INVALID_ARG, "bsa_backward: scale must be finite and > 0");
-  bsa::FwdOptions fo;
-  st = make_options(opts, H, scale, &fo, "bsa_backward");
-  if (st != BSA_OK) return st;
-  fo.sq = Sq;
-  fo.sk = Sk;
-  if (plan_cols->H != H || plan_cols->Mb != plan->Mb || plan_cols->Nb != plan->Nb ||
-      plan_cols->Hkv != H / fo.kv_group)
-    return fail(BSA_ERR_PLAN_MISMATCH,
-                "bsa_backward: column plan H=%d Hkv=%d Mb=%d Nb=%d does not match H=%d Hkv=%d "
-                "Mb=%d Nb=%d", plan_cols->H, plan_cols->Hkv, plan_cols->Mb, plan_cols->Nb, H,
-                H / fo.kv_group, plan->Mb, plan->Nb);
-  if (!bsa::backward_supported(bs, d))
-    return fail(BSA_ERR_UNSUPPORTED, "bsa_backward: no kernel for bs=%d d=%d", bs, d);
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
-      !aligned(lse, 4) || !aligned(workspace, 16) || (dsink != nullptr && !aligned(dsink, 4)))
-    return fail(BSA_ERR_MISALIGNED, "bsa_backward: tensors must be 16-byte aligned");
-  const size_t ws = bsa_backward_workspace_bytes(B, H, Sq);
-  if (workspace_bytes < ws)
-    return fail(BSA_ERR_BUFFER_TOO_SMALL, "bsa_backward: workspace is %zu bytes, needs %zu",
-                workspace_bytes, ws);
-  const int64_t work = (int64_t)B * H * plan->Mb;
-  const int64_t rows = (int64_t)B * H * Sq;
-  if (work > 0x7ffffff0LL || (int64_t)B * H * plan->Nb > 0x7ffffff0LL)
-    return fail(BSA_ERR_UNSUPPORTED, "bsa_backward: problem too large");
-  bsa::BwdArgs a;
-  a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse;
-  a.row_ptr = at<int32_t>(plan->dev_buf, g.off_row_ptr);
-  a.col_idx = at<int32_t>(plan->dev_buf, g.off_col_idx);
-  a.row_order = at<int32_t>(plan->dev_buf, g.off_row_order);
-  a.col_ptr = at<int32_t>(plan_cols->dev_buf, gc.off_col_ptr);
-  a.row_idx = at<int32_t>(plan_cols->dev_buf, gc.off_row_idx);
-  a.col_order = at<int32_t>(plan_cols->dev_buf, gc.off_col_order);
-  a.B = B; a.H = H; a.Mb = plan->Mb; a.Nb = plan->Nb; a.bs = bs; a.d = d;
-  a.f32 = dtype == BSA_F32;
-  a.scale = scale;
-  a.opt = fo;
-  a.Dv = static_cast<float *>(workspace);
-  a.lse2 = static_cast<float *>(workspace) + rows;
-  a.dq = dq; a.dk = dk; a.dv = dv;
-  a.dsink = fo.sink != nullptr ? dsink : nullptr;
-  hipError_t e = bsa::launch_backward(a, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "bsa_backward launch");
-  return BSA_OK;
+  return backward_impl("bsa_backward", q, k, v, out, dout, lse, plan, plan_cols, B, H, Sq, Sk,
+                       bs, d, dtype, scale, opts, false, workspace, workspace_bytes, dq, dk, dv,
+                       dsink, stream);
+}
+
+size_t bsa_backward_noalloc_max_rows(void) { return kNoAllocScratchBytes / (2 * sizeof(float)); }
+
+int bsa_backward_noalloc(const void *q, const void *k, const void *v, const void *out,
+                         const void *dout, const float *lse, const bsa_plan_t *plan,
+                         const bsa_plan_cols_t *plan_cols, int32_t B, int32_t H, int32_t Sq,
+                         int32_t Sk, int32_t bs, int32_t d, bsa_dtype_t dtype, float scale,
+                         const bsa_forward_opts_t *opts, void *dq, void *dk, void *dv,
+                         float *dsink, void *stream) {
+  return backward_impl("bsa_backward_noalloc", q, k, v, out, dout, lse, plan, plan_cols, B, H,
+                       Sq, Sk, bs, d, dtype, scale, opts, true, nullptr, 0, dq, dk, dv, dsink,
+                       stream);
 }
 
 size_t bsa_layout_adaptive_workspace_bytes(int32_t H, int32_t Hkv, int32_t Mb, int32_t Nb,

@@ -255,6 +255,36 @@ int bsa_backward(const void *q, const void *k, const void *v, const void *out, c
                  size_t workspace_bytes, void *dq, void *dk, void *dv, float *dsink,
                  void *stream);
 
+/* Query rows (B * H * Sq) bsa_backward_noalloc can serve: 2^21. */
+size_t bsa_backward_noalloc_max_rows(void);
+
+/*
+ * bsa_backward without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving or training loops, harnesses that forbid hipMalloc.  It
+ * computes exactly what bsa_backward computes, with the same kernels; the
+ * per-row D and lse values go to a static device array of 16 MiB that the
+ * library holds on each GPU it runs on until the process ends (looked up on
+ * the first call made with that device current).  The caller still passes
+ * every input and output, as for bsa_backward.
+ *
+ *   arguments  as bsa_backward, minus workspace and workspace_bytes
+ *   limit      B * H * Sq <= bsa_backward_noalloc_max_rows() (2^21 rows);
+ *              larger calls return BSA_ERR_UNSUPPORTED before any HIP call
+ * Nothing in the array needs to start at zero: every value is written by the
+ * call before it is read.  All calls on one GPU share its array, so calls that
+ * overlap on one GPU (on different streams, or from different threads without
+ * ordering) race and give wrong gradients; calls ordered on one stream do not.
+ * Errors: as bsa_backward, plus BSA_ERR_HIP when the array's address cannot be
+ * obtained.
+ */
+int bsa_backward_noalloc(const void *q, const void *k, const void *v, const void *out,
+                         const void *dout, const float *lse, const bsa_plan_t *plan,
+                         const bsa_plan_cols_t *plan_cols, int32_t B, int32_t H, int32_t Sq,
+                         int32_t Sk, int32_t bs, int32_t d, bsa_dtype_t dtype, float scale,
+                         const bsa_forward_opts_t *opts, void *dq, void *dk, void *dv,
+                         float *dsink, void *stream);
+
 /* Bytes of the adaptive-layout workspace: (H*Mb + Hkv*Nb) * d floats. */
 size_t bsa_layout_adaptive_workspace_bytes(int32_t H, int32_t Hkv, int32_t Mb, int32_t Nb,
                                            int32_t d);

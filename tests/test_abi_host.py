@@ -168,6 +168,37 @@ def test_topk_validation(lib):
     assert call(N=(1 << 23) - 1, d=256) == UNSUPPORTED  # 4 GiB - 512 B
 
 
+def test_backward_noalloc_validation(lib):
+    """The entry point without a workspace validates like bsa_backward and
+    refuses problems beyond its static scratch (2^21 query rows), all before
+    any HIP call."""
+    assert lib.bsa_backward_noalloc_max_rows() == 1 << 21
+    f = ctypes.c_void_p(0x10000)
+
+    def planned(H, Sq, bs):
+        nb = -(-Sq // bs)
+        p = _plan_struct(H=H, Mb=nb, Nb=nb, lib=lib)
+        pc = bsa._PlanColsT()
+        pc.H, pc.Hkv, pc.Mb, pc.Nb = H, H, nb, nb
+        pc.dev_buf = 0x200000
+        pc.dev_bytes = lib.bsa_plan_cols_buffer_bytes(H, H, nb, nb)
+        return p, pc
+
+    def call(B=1, H=2, Sq=64, bs=16, d=32, dq=f, lse=f, scale=0.5):
+        p, pc = planned(H, Sq, bs)
+        return lib.bsa_backward_noalloc(f, f, f, f, f, lse, ctypes.byref(p), ctypes.byref(pc), B,
+                                        H, Sq, Sq, bs, d, 0, scale, None, dq, f, f, None, None)
+
+    assert call(dq=None) == INVALID
+    assert call(lse=None) == INVALID
+    assert call(scale=0.0) == INVALID
+    assert call(d=48) == UNSUPPORTED
+    assert call(dq=ctypes.c_void_p(0x10008)) == MISALIGNED
+    # one query row past the limit, as several batch items of 32 heads
+    assert call(B=65, H=32, Sq=1024, bs=128, d=128) == UNSUPPORTED
+    assert "static scratch" in lib.bsa_last_error().decode()
+
+
 def test_status_strings(lib):
     for code in (OK, INVALID, UNSUPPORTED, MISALIGNED, MISMATCH, TOO_SMALL, -6):
         s = lib.bsa_status_string(code)
