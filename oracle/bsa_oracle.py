@@ -73,6 +73,8 @@ import numpy as np
 __all__ = [
     "PlanRef",
     "plan",
+    "PlanPairsRef",
+    "plan_pairs",
     "token_mask",
     "attention_dense_masked",
     "attention_live_tiles",
@@ -143,6 +145,72 @@ def plan(layout: np.ndarray) -> PlanRef:
         row_order=row_order.astype(np.int32),
         nnz_total=int(row_ptr[-1]),
     )
+
+
+@dataclass
+class PlanPairsRef:
+    """Pairs of neighbouring block rows with the union of their live columns.
+
+    Pair q = h * Mp + p (Mp = ceil(Mb / 2)) joins block rows 2p and 2p + 1 of
+    head h (only row 2p when Mb is odd and p is the last pair).
+    ``pair_ptr[q]:pair_ptr[q+1]`` delimits in ``pair_cols`` the columns live in
+    either row, ascending; each entry is n + 2^24 * mask, where bit 0 of mask
+    says that row 2p lists column n and bit 1 that row 2p + 1 does.
+    ``pair_order`` lists all pairs head by head, inside each head by union
+    size descending, ties by p ascending.  ``use_pairs`` is 1 when the unions
+    hold at most three quarters of the live tiles (4 * pair_total <= 3 *
+    nnz_total), i.e. when streaming each pair's union once saves at least a
+    quarter of the tile loads; 0 otherwise.
+    """
+
+    H: int
+    Mb: int
+    Nb: int
+    pair_ptr: np.ndarray    # int32 [H*Mp+1]
+    pair_cols: np.ndarray   # int32 [pair_total]
+    pair_order: np.ndarray  # int32 [H*Mp]
+    pair_total: int
+    use_pairs: int
+
+
+def plan_pairs(layout: np.ndarray) -> PlanPairsRef:
+    """Pair plan of a block layout [H, Mb, Nb] (see PlanPairsRef).
+
+    Neighbouring block rows of local, global and strided patterns (the
+    DeepSpeed utils page's local/strided/BigBird layouts; the next.gr
+    tutorial, section 3.2, on local windows and strided patterns) list
+    nearly the same columns; a tile two rows both need is then loaded once
+    for both.  The pair plan is a schedule of the same live tiles: decoding it
+    gives back the layout exactly.
+    """
+    lay = np.asarray(layout)
+    if lay.ndim != 3:
+        raise ValueError("layout must be [H, Mb, Nb]")
+    H, Mb, Nb = lay.shape
+    if Nb >= (1 << 24):
+        raise ValueError("column indices must fit below bit 24")
+    Mp = (Mb + 1) // 2
+    live = np.zeros((H, 2 * Mp, Nb), dtype=bool)
+    live[:, :Mb] = lay != 0
+    first, second = live[:, 0::2], live[:, 1::2]            # rows 2p and 2p+1, [H, Mp, Nb]
+    union = (first | second).reshape(H * Mp, Nb)
+    cnt = union.sum(axis=1).astype(np.int64)
+    pair_ptr = np.zeros(H * Mp + 1, dtype=np.int64)
+    pair_ptr[1:] = np.cumsum(cnt)
+    q, n = np.nonzero(union)                               # n ascending inside each pair
+    mask = first.reshape(H * Mp, Nb)[q, n].astype(np.int64) + \
+        2 * second.reshape(H * Mp, Nb)[q, n].astype(np.int64)
+    cols = n.astype(np.int64) + (mask << 24)
+    order = []
+    for h in range(H):
+        p = np.arange(Mp)
+        order.append(h * Mp + np.lexsort((p, -cnt[h * Mp:(h + 1) * Mp])))
+    pair_order = np.concatenate(order) if order else np.zeros(0, np.int64)
+    pair_total = int(pair_ptr[-1])
+    nnz_total = int((lay != 0).sum())
+    return PlanPairsRef(H=H, Mb=Mb, Nb=Nb, pair_ptr=pair_ptr.astype(np.int32),
+                        pair_cols=cols.astype(np.int32), pair_order=pair_order.astype(np.int32),
+                        pair_total=pair_total, use_pairs=int(4 * pair_total <= 3 * nnz_total))
 
 
 # --------------------------------------------------------------------------

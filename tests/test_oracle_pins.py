@@ -404,6 +404,100 @@ def test_plan_matches_brute_force_and_invariants(seed):
         assert key == sorted(key)
 
 
+def brute_force_pairs(lay):
+    """Pair plan from the brute-force row lists: a two-pointer merge of the
+    sorted column lists of rows 2p and 2p+1, the order by repeated selection
+    of the largest union."""
+    H, Mb, Nb = lay.shape
+    rp, cols, _ = brute_force_plan(lay)
+    row = lambda h, m: cols[rp[h * Mb + m]:rp[h * Mb + m + 1]]  # noqa: E731
+    Mp = (Mb + 1) // 2
+    ptr, out, cnt = [0], [], []
+    for h in range(H):
+        for p in range(Mp):
+            a = row(h, 2 * p)
+            b = row(h, 2 * p + 1) if 2 * p + 1 < Mb else []
+            i = j = 0
+            merged = []
+            while i < len(a) or j < len(b):
+                if j == len(b) or (i < len(a) and a[i] < b[j]):
+                    merged.append(a[i] | (1 << 24))
+                    i += 1
+                elif i == len(a) or b[j] < a[i]:
+                    merged.append(b[j] | (2 << 24))
+                    j += 1
+                else:
+                    merged.append(a[i] | (3 << 24))
+                    i += 1
+                    j += 1
+            out += merged
+            cnt.append(len(merged))
+            ptr.append(ptr[-1] + len(merged))
+    order = []
+    for h in range(H):
+        left = list(range(Mp))
+        while left:
+            best = left[0]
+            for p in left[1:]:
+                if cnt[h * Mp + p] > cnt[h * Mp + best]:
+                    best = p
+            left.remove(best)
+            order.append(h * Mp + best)
+    return ptr, out, order
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_plan_pairs_matches_brute_force_and_round_trips(seed):
+    rng = np.random.default_rng(100 + seed)
+    H, Mb, Nb = int(rng.integers(1, 4)), int(rng.integers(1, 10)), int(rng.integers(1, 70))
+    lay = (rng.random((H, Mb, Nb)) < rng.random()).astype(np.int32) * rng.integers(1, 5, (H, Mb, Nb))
+    if seed == 0:
+        lay[:] = 0
+    if seed == 1:  # rows 2p+1 copy rows 2p: every shared column carries mask 3
+        lay[:, 1::2] = lay[:, 0:Mb - Mb % 2:2]
+    pp = O.plan_pairs(lay)
+    ptr, cols, order = brute_force_pairs(lay)
+    assert pp.pair_ptr.tolist() == ptr and pp.pair_cols.tolist() == cols
+    assert pp.pair_order.tolist() == order
+    assert pp.pair_total == len(cols)
+    nnz = int((lay != 0).sum())
+    assert pp.use_pairs == int(4 * len(cols) <= 3 * nnz)
+    assert pp.pair_ptr.dtype == np.int32 and pp.pair_cols.dtype == np.int32
+    # decoding the pairs gives back the live set exactly
+    Mp = (Mb + 1) // 2
+    back = np.zeros((H, 2 * Mp, Nb), bool)
+    for q in range(H * Mp):
+        h, p = divmod(q, Mp)
+        ent = pp.pair_cols[pp.pair_ptr[q]:pp.pair_ptr[q + 1]]
+        n, mask = ent & 0xFFFFFF, ent >> 24
+        assert np.all(np.diff(n) > 0) and np.all((mask >= 1) & (mask <= 3))
+        back[h, 2 * p, n[(mask & 1) != 0]] = True
+        back[h, 2 * p + 1, n[(mask & 2) != 0]] = True
+    assert not back[:, Mb:].any()
+    assert np.array_equal(back[:, :Mb], lay != 0)
+
+
+def test_plan_pairs_of_the_page_layouts():
+    """A band |i - j| <= w shares all but two columns between neighbouring
+    rows (union of rows 2p, 2p+1 = 2w + 2 inside the grid), so the pairs hold
+    about half the tiles; identical rows pair to exactly half; a diagonal
+    layout shares nothing (the union is the sum) and is not paired."""
+    nb, w = 64, 4
+    i, j = np.meshgrid(np.arange(nb), np.arange(nb), indexing="ij")
+    band = (np.abs(i - j) <= w).astype(np.int32)[None]
+    pp = O.plan_pairs(band)
+    inner = [pp.pair_ptr[p + 1] - pp.pair_ptr[p] for p in range(3, nb // 2 - 3)]
+    assert all(c == 2 * w + 2 for c in inner)
+    assert pp.use_pairs == 1
+    same = np.repeat((np.random.default_rng(3).random((2, 8, 40)) < 0.3).astype(np.int32), 2, axis=1)
+    pp = O.plan_pairs(same)
+    assert 2 * pp.pair_total == int(same.sum()) and pp.use_pairs == 1
+    assert np.all((pp.pair_cols >> 24) == 3)
+    diag = np.eye(16, dtype=np.int32)[None]
+    pp = O.plan_pairs(diag)
+    assert pp.pair_total == 16 and pp.use_pairs == 0
+
+
 def load_golden():
     with open(GOLDEN) as f:
         return json.load(f)
