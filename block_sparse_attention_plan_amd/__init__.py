@@ -91,6 +91,8 @@ def load_library():
     lib.bsa_plan_buffer_bytes.restype = ctypes.c_size_t
     lib.bsa_plan_sections.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.bsa_plan_sections.restype = ctypes.c_int
+    lib.bsa_plan_pair_sections.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.bsa_plan_pair_sections.restype = ctypes.c_int
     lib.bsa_plan.argtypes = [vp, i32, i32, i32, vp, ctypes.c_size_t, ctypes.POINTER(_PlanT), vp]
     lib.bsa_plan.restype = ctypes.c_int
     lib.bsa_plan_nnz.argtypes = [ctypes.POINTER(_PlanT), ctypes.POINTER(ctypes.c_int64), vp]
@@ -200,6 +202,9 @@ class Plan:
         offs = (ctypes.c_size_t * 4)()
         _check(load_library().bsa_plan_sections(H, Mb, Nb, offs))
         self._offs = [int(o) for o in offs]
+        _check(load_library().bsa_plan_pair_sections(H, Mb, Nb, offs))
+        self._offs += [int(o) for o in offs]
+        self.Mp = (Mb + 1) // 2
 
     def _section(self, i: int, count: int) -> torch.Tensor:
         off = self._offs[i]
@@ -223,6 +228,26 @@ class Plan:
 
     def nnz(self) -> int:
         return bsa_plan_nnz(self)
+
+    # Pairs of neighbouring block rows (2p, 2p+1): the union of their live
+    # columns, each entry n | mask << 24 (bit 24: row 2p lists n, bit 25: row
+    # 2p+1 does), and the flag that makes the forward use them.
+    @property
+    def pair_ptr(self) -> torch.Tensor:
+        return self._section(4, self.H * self.Mp + 1)
+
+    @property
+    def pair_order(self) -> torch.Tensor:
+        return self._section(5, self.H * self.Mp)
+
+    @property
+    def pair_info(self) -> torch.Tensor:
+        """int32 [2]: pair_total, use_pairs."""
+        return self._section(6, 2)
+
+    def pair_cols(self, pair_total: Optional[int] = None) -> torch.Tensor:
+        n = int(self.pair_info[0].item()) if pair_total is None else pair_total
+        return self._section(7, n)
 
 
 def plan_buffer(layout_shape, device) -> torch.Tensor:

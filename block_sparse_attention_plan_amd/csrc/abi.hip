@@ -242,6 +242,18 @@ int bsa_plan_sections(int32_t H, int32_t Mb, int32_t Nb, size_t offsets_out[4]) 
   return BSA_OK;
 }
 
+int bsa_plan_pair_sections(int32_t H, int32_t Mb, int32_t Nb, size_t offsets_out[4]) {
+  bsa::PlanGeometry g;
+  if (offsets_out == nullptr) return fail(BSA_ERR_INVALID_ARG, "offsets_out is NULL");
+  if (!bsa::plan_geometry(H, Mb, Nb, &g))
+    return fail(BSA_ERR_INVALID_ARG, "invalid layout dimensions H=%d Mb=%d Nb=%d", H, Mb, Nb);
+  offsets_out[0] = g.off_pair_ptr;
+  offsets_out[1] = g.off_pair_order;
+  offsets_out[2] = g.off_pair_info;
+  offsets_out[3] = g.off_pair_cols;
+  return BSA_OK;
+}
+
 int bsa_plan(const int32_t *layout, int32_t H, int32_t Mb, int32_t Nb, void *dev_buf,
              size_t dev_bytes, bsa_plan_t *plan_out, void *stream) {
   if (layout == nullptr || dev_buf == nullptr || plan_out == nullptr)
@@ -258,7 +270,11 @@ int bsa_plan(const int32_t *layout, int32_t H, int32_t Mb, int32_t Nb, void *dev
   hipError_t e = bsa::launch_plan(layout, H, Mb, Nb, at<int32_t>(dev_buf, g.off_row_ptr),
                                   at<int32_t>(dev_buf, g.off_row_order),
                                   at<int32_t>(dev_buf, g.off_nnz),
-                                  at<int32_t>(dev_buf, g.off_col_idx), (hipStream_t)stream);
+                                  at<int32_t>(dev_buf, g.off_col_idx),
+                                  at<int32_t>(dev_buf, g.off_pair_ptr),
+                                  at<int32_t>(dev_buf, g.off_pair_order),
+                                  at<int32_t>(dev_buf, g.off_pair_info),
+                                  at<int32_t>(dev_buf, g.off_pair_cols), (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "bsa_plan launch");
   plan_out->H = H;
   plan_out->Mb = Mb;
@@ -315,10 +331,15 @@ int bsa_forward_ex(const void *q, const void *k, const void *v, const bsa_plan_t
   if (st != BSA_OK) return st;
   fo.sq = Sq;
   fo.sk = Sk;
-  hipError_t e = bsa::launch_forward(
-      q, k, v, at<int32_t>(plan->dev_buf, g.off_row_ptr), at<int32_t>(plan->dev_buf, g.off_col_idx),
-      at<int32_t>(plan->dev_buf, g.off_row_order), B, plan->H, plan->Mb, plan->Nb, bs, d,
-      dtype == BSA_F32, scale, fo, out, lse, (hipStream_t)stream);
+  const bsa::PlanArrays pa{at<int32_t>(plan->dev_buf, g.off_row_ptr),
+                           at<int32_t>(plan->dev_buf, g.off_col_idx),
+                           at<int32_t>(plan->dev_buf, g.off_row_order),
+                           at<int32_t>(plan->dev_buf, g.off_pair_ptr),
+                           at<int32_t>(plan->dev_buf, g.off_pair_cols),
+                           at<int32_t>(plan->dev_buf, g.off_pair_order),
+                           at<int32_t>(plan->dev_buf, g.off_pair_info)};
+  hipError_t e = bsa::launch_forward(q, k, v, pa, B, plan->H, plan->Mb, plan->Nb, bs, d,
+                                     dtype == BSA_F32, scale, fo, out, lse, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "bsa_forward launch");
   return BSA_OK;
 }

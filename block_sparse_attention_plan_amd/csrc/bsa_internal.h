@@ -6,10 +6,14 @@
 
 namespace bsa {
 
-// Plan buffer geometry: byte offsets of row_ptr, row_order, nnz_total, col_idx
-// and the total size.  All sections start on 256-byte boundaries.
+// Plan buffer geometry: byte offsets of row_ptr, row_order, nnz_total,
+// col_idx, then of the pair sections pair_ptr, pair_order, pair_info
+// (pair_total, use_pairs) and pair_cols, and the total size.  All sections
+// start on 256-byte boundaries.
 struct PlanGeometry {
-  size_t off_row_ptr, off_row_order, off_nnz, off_col_idx, total;
+  size_t off_row_ptr, off_row_order, off_nnz, off_col_idx;
+  size_t off_pair_ptr, off_pair_order, off_pair_info, off_pair_cols;
+  size_t total;
 };
 bool plan_geometry(int32_t H, int32_t Mb, int32_t Nb, PlanGeometry *g);
 
@@ -18,7 +22,8 @@ constexpr int32_t kPlanMaxNb = 16384;
 
 hipError_t launch_plan(const int32_t *layout, int32_t H, int32_t Mb, int32_t Nb,
                        int32_t *row_ptr, int32_t *row_order, int32_t *nnz_total,
-                       int32_t *col_idx, hipStream_t stream);
+                       int32_t *col_idx, int32_t *pair_ptr, int32_t *pair_order,
+                       int32_t *pair_info, int32_t *pair_cols, hipStream_t stream);
 
 // Per-call options of the forward kernels (already validated).
 struct FwdOptions {
@@ -33,12 +38,18 @@ struct FwdOptions {
   const int32_t *kseg;  // [B, sk] segment ids of the keys (set with qseg)
 };
 
+// The plan's device arrays as the forward reads them: the rows, and the pairs
+// of neighbouring rows with their use flag (pair_info[1]).
+struct PlanArrays {
+  const int32_t *row_ptr, *col_idx, *row_order;
+  const int32_t *pair_ptr, *pair_cols, *pair_order, *pair_info;
+};
+
 // Returns hipErrorInvalidValue when no kernel instance matches (bs, d, f32).
-hipError_t launch_forward(const void *q, const void *k, const void *v,
-                          const int32_t *row_ptr, const int32_t *col_idx,
-                          const int32_t *row_order, int32_t B, int32_t H, int32_t Mb,
-                          int32_t Nb, int32_t bs, int32_t d, bool f32, float scale,
-                          const FwdOptions &opt, void *out, float *lse, hipStream_t stream);
+hipError_t launch_forward(const void *q, const void *k, const void *v, const PlanArrays &plan,
+                          int32_t B, int32_t H, int32_t Mb, int32_t Nb, int32_t bs, int32_t d,
+                          bool f32, float scale, const FwdOptions &opt, void *out, float *lse,
+                          hipStream_t stream);
 bool forward_supported(int32_t bs, int32_t d);
 
 // Column plan (backward): byte offsets of col_ptr, col_order, nnz_total,

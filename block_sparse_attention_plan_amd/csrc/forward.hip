@@ -67,6 +67,11 @@ constexpr int kDmaPieces64 = BSA_DMA_PIECES64;  // the same for bs=64
 #ifndef BSA_READ_AHEAD_V
 #define BSA_READ_AHEAD_V 6
 #endif
+#ifndef BSA_PAIR_FORM
+#define BSA_PAIR_FORM 1
+#endif
+// 1: bf16 bs = 64 forwards use the plan's pairs of block rows when its flag is set
+constexpr bool kPairForm = BSA_PAIR_FORM != 0;
 constexpr int kReadAheadK = BSA_READ_AHEAD_K;  // K operand reads issued before the first QK MFMA
 constexpr int kReadAheadV = BSA_READ_AHEAD_V;  // V transpose reads issued before the first PV MFMA
 
@@ -650,14 +655,25 @@ template <int D> struct VSwz {
   }
 };
 
-template <int BS, int D, int KSPLIT, int PIECES, bool MASK, bool SEG = false>
+// GROUP instances serve the pairs of neighbouring block rows of a layout
+// with bs = BS / 2 (the plan's pair lists): a work item is pair p of head h,
+// i.e. query rows p*BS .. p*BS + BS - 1 (block rows 2p and 2p+1), and each
+// list entry names one key block of BS / 2 keys -- one piece -- together with
+// the rows that list it (bits 24 and 25).  The row groups of the block row
+// that does not list a piece give its scores -inf, so its weights are exactly
+// zero: every shared tile is loaded once for both rows.
+// sel / sel_want: with sel set, a launch whose *sel differs from sel_want
+// returns at once (the pair and row forms are launched together and the
+// plan's flag picks one).
+template <int BS, int D, int KSPLIT, int PIECES, bool MASK, bool SEG = false, bool GROUP = false>
 __global__ void __launch_bounds__(BS * 2 * KSPLIT)
 __attribute__((amdgpu_waves_per_eu(KSPLIT * PIECES)))
 bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
                    const __bf16 *__restrict__ v, const int32_t *__restrict__ row_ptr,
                    const int32_t *__restrict__ col_idx, const int32_t *__restrict__ row_order,
                    int32_t B, int32_t H, int32_t Mb, int32_t Nb, float scale_log2,
-                   __bf16 *__restrict__ out, float *__restrict__ lse, const FwdOptions opt) {
+                   __bf16 *__restrict__ out, float *__restrict__ lse, const FwdOptions opt,
+                   const int32_t *__restrict__ sel, int32_t sel_want) {
   constexpr int NRG = BS / 32;           // 32-row groups
   constexpr int NW = NRG * KSPLIT;       // waves per workgroup
   constexpr int PB = BS / PIECES;        // keys per piece (a tile is streamed in PIECES pieces)
@@ -678,6 +694,11 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   // instructions of its wave (NSW = 1 when RPI * NW is a multiple of CPR).
   constexpr int NSW = (RPI * NW) % CPR == 0 ? 1 : CPR / ((RPI * NW) % CPR);
   static_assert((RPI * NW * NSW) % CPR == 0 && IPW % NSW == 0, "K swizzle pattern must repeat");
+  static_assert(!GROUP || (!MASK && KSPLIT == 1 && NRG == 4 && PIECES == 2),
+                "pairs: four row groups (two per block row), plain scores");
+  constexpr int PPE = GROUP ? 1 : PIECES;  // pieces per plan entry
+  constexpr int KBLK = GROUP ? PB : BS;    // keys per layout block column
+  if (sel != nullptr && *sel != sel_want) return;
 
   // Four distinct LDS objects, so that the compiler can tell the piece being
   // read from the piece being filled and need not wait for the copy in flight.
@@ -722,7 +743,8 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   __bf16 *oh = out + bh * Sq * D;
   float *lh = lse ? lse + bh * Sq : nullptr;
   const int64_t i_row = (int64_t)m * BS + 32 * rg + l32;
-  const bool q_ok = !MASK || i_row < Sq;  // rows past a cut last block
+  // rows past a cut last block, or the absent second row of a last pair
+  const bool q_ok = !(MASK || GROUP) || i_row < Sq;
   const int qsg = (SEG && q_ok) ? opt.qseg[(int64_t)b * Sq + i_row] : 0;
 
   if (beg == end) {
@@ -764,13 +786,15 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
         copy16_to_lds(rs, dst_tile + i * 512, (uint32_t)(src_off * 2), (uint32_t)(i * RPI * D * 2));
     }
   };
-  // piece `half` of tile n: keys n*BS + half*PB .. + PB - 1 (rows past Sk read as zeros)
+  // piece `half` of tile n: keys n*BS + half*PB .. + PB - 1 (rows past Sk read as zeros);
+  // GROUP: key block n of PB keys (plan entries carry row bits above bit 24)
   auto tile_bytes = [&](int n, int half) -> uint32_t {
     return MASK ? (uint32_t)(max((int64_t)0, min((int64_t)PB, Sk - (int64_t)n * BS - half * PB)) * D * 2)
                 : (uint32_t)(TILE * 2);
   };
   auto piece_src = [&](const __bf16 *base, int n, int half) {
-    return base + (int64_t)n * BS * D + (int64_t)half * PB * D;
+    if constexpr (GROUP) n &= 0xffffff;
+    return base + (int64_t)n * KBLK * D + (int64_t)half * PB * D;
   };
   // SEG instances also copy the piece's key segment ids, 16 per wave with
   // one 4-byte-per-lane copy: every wave issues the same number of copies.
@@ -837,6 +861,12 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     return bits;
   };
   auto apply_opts = [&](f32x16 (&s)[JT], int ncol, int half, uint32_t segbits) {
+    if constexpr (GROUP) {  // a piece the wave's block row does not list: weights zero
+      if (!((ncol >> (24 + rg / 2)) & 1)) {
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) s[jt] = f32x16{} - __builtin_inff();
+      }
+    }
     if constexpr (!MASK) return;
     const int kb0 = key0 + half * PB;   // this wave's first key inside the tile
     if (opt.cap_k != 0.f) {
@@ -953,10 +983,10 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   // load in flight would force every LDS wait in between to drain
   // completely.
   // Piece u = 0 .. n-1 is piece u % PIECES of live tile u / PIECES.
-  const int n = (end - beg) * PIECES;
+  const int n = (end - beg) * PPE;
   const int32_t *cols = col_idx + beg;
-  auto col_at = [&](int u) -> int { return cols[min(u, n - 1) / PIECES]; };
-  auto half_at = [&](int u) -> int { return min(u, n - 1) % PIECES; };
+  auto col_at = [&](int u) -> int { return cols[min(u, n - 1) / PPE]; };
+  auto half_at = [&](int u) -> int { return min(u, n - 1) % PPE; };
   auto fetch_cols = [&](int kpos, int vpos) -> int { return col_at(lane == 0 ? kpos : vpos); };
   constexpr int kVmInFlight = 2 * IPW + (SEG ? 1 : 0);
   constexpr int kVmWait = (kVmInFlight & 15) | (7 << 4) | (15 << 8) | ((kVmInFlight >> 4) << 14);
@@ -1105,14 +1135,16 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   if (lh && h2 == 0) lh[i_row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
 }
 
+// Workgroups for W work items: a multiple of 8, so that the XCD mapping of
+// the kernels (item = (id % 8) * per + id / 8) covers them.
+int64_t grid_for(int64_t W) { return ((W + 7) / 8) * 8; }
+
 template <int BS, int D, typename T, bool MASK>
-hipError_t launch_one(const void *q, const void *k, const void *v, const int32_t *row_ptr,
-                      const int32_t *col_idx, const int32_t *row_order, int32_t B, int32_t H,
-                      int32_t Mb, int32_t Nb, float scale, const FwdOptions &opt, void *out,
-                      float *lse, hipStream_t stream) {
-  const int64_t W = (int64_t)B * H * Mb;
-  const int64_t per = (W + 7) / 8;
-  const int64_t grid = per * 8;
+hipError_t launch_one(const void *q, const void *k, const void *v, const PlanArrays &pa, int32_t B,
+                      int32_t H, int32_t Mb, int32_t Nb, float scale, const FwdOptions &opt,
+                      void *out, float *lse, hipStream_t stream) {
+  const int32_t *row_ptr = pa.row_ptr, *col_idx = pa.col_idx, *row_order = pa.row_order;
+  const int64_t grid = grid_for((int64_t)B * H * Mb);
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if constexpr (BS == 16) {
     hipLaunchKernelGGL((bsa_fwd_kernel<BS, D, T, MASK>), dim3((unsigned)grid), dim3(BS * 4), 0,
@@ -1121,16 +1153,32 @@ hipError_t launch_one(const void *q, const void *k, const void *v, const int32_t
   } else if constexpr (BS >= 64 && std::is_same<T, __bf16>::value) {
     constexpr int PC = BS == 128 ? kDmaPieces : kDmaPieces64;
     constexpr int KS = PC == 2 ? 1 : BS == 128 ? kDmaKeySplit : 2;
+    const int32_t *sel = nullptr;
+    if constexpr (kPairForm && BS == 64 && !MASK && PC == 2 && KS == 1) {
+      // Pairs of block rows when the plan's flag says so (the unions of
+      // neighbouring rows hold at most 3/4 of the tiles); both forms are
+      // launched and the one the flag does not pick returns at once.
+      if (pa.pair_info != nullptr && opt.qseg == nullptr) {
+        sel = pa.pair_info + 1;
+        const int32_t Mp = (Mb + 1) / 2;
+        const int64_t pgrid = grid_for((int64_t)B * H * Mp);
+        hipLaunchKernelGGL((bsa_fwd_dma_kernel<128, D, 1, 2, false, false, true>),
+                           dim3((unsigned)pgrid), dim3(256), 0, stream, (const __bf16 *)q,
+                           (const __bf16 *)k, (const __bf16 *)v, pa.pair_ptr, pa.pair_cols,
+                           pa.pair_order, B, H, Mp, Nb, scale * kLog2e, (__bf16 *)out, lse, opt,
+                           sel, 1);
+      }
+    }
     if (opt.qseg == nullptr) {
       hipLaunchKernelGGL((bsa_fwd_dma_kernel<BS, D, KS, PC, MASK>), dim3((unsigned)grid),
                          dim3(BS * 2 * KS), 0, stream, (const __bf16 *)q, (const __bf16 *)k,
                          (const __bf16 *)v, row_ptr, col_idx, row_order, B, H, Mb, Nb,
-                         scale * kLog2e, (__bf16 *)out, lse, opt);
+                         scale * kLog2e, (__bf16 *)out, lse, opt, sel, 0);
     } else {  // segment ids: the instance that also copies the key ids
       hipLaunchKernelGGL((bsa_fwd_dma_kernel<BS, D, KS, PC, true, true>), dim3((unsigned)grid),
                          dim3(BS * 2 * KS), 0, stream, (const __bf16 *)q, (const __bf16 *)k,
                          (const __bf16 *)v, row_ptr, col_idx, row_order, B, H, Mb, Nb,
-                         scale * kLog2e, (__bf16 *)out, lse, opt);
+                         scale * kLog2e, (__bf16 *)out, lse, opt, nullptr, 0);
     }
   } else {
     constexpr int KSPLIT = BS >= 64 ? 2 : 1;
@@ -1143,19 +1191,18 @@ hipError_t launch_one(const void *q, const void *k, const void *v, const int32_t
 
 template <typename T>
 hipError_t dispatch(int32_t bs, int32_t d, const void *q, const void *k, const void *v,
-                    const int32_t *rp, const int32_t *ci, const int32_t *ro, int32_t B, int32_t H,
-                    int32_t Mb, int32_t Nb, float scale, const FwdOptions &opt, void *out,
-                    float *lse, hipStream_t s) {
+                    const PlanArrays &pa, int32_t B, int32_t H, int32_t Mb, int32_t Nb,
+                    float scale, const FwdOptions &opt, void *out, float *lse, hipStream_t s) {
   // Score-changing options (cap, causal) and cut last blocks select their own
   // kernel instances, so the plain forward keeps the code it has without them.
   const bool mask = opt.cap_k != 0.f || opt.causal != 0 || opt.sq % bs != 0 || opt.sk % bs != 0 ||
                     opt.qseg != nullptr;
-#define BSA_CASE(BS_, D_)                                                                   \
-  if (bs == BS_ && d == D_)                                                                 \
-    return mask ? launch_one<BS_, D_, T, true>(q, k, v, rp, ci, ro, B, H, Mb, Nb, scale, opt, \
-                                               out, lse, s)                                 \
-                : launch_one<BS_, D_, T, false>(q, k, v, rp, ci, ro, B, H, Mb, Nb, scale, opt, \
-                                                out, lse, s);
+#define BSA_CASE(BS_, D_)                                                                     \
+  if (bs == BS_ && d == D_)                                                                   \
+    return mask ? launch_one<BS_, D_, T, true>(q, k, v, pa, B, H, Mb, Nb, scale, opt, out, lse, \
+                                               s)                                             \
+                : launch_one<BS_, D_, T, false>(q, k, v, pa, B, H, Mb, Nb, scale, opt, out,     \
+                                                lse, s);
   BSA_CASE(16, 32) BSA_CASE(16, 64) BSA_CASE(16, 128)
   BSA_CASE(32, 32) BSA_CASE(32, 64) BSA_CASE(32, 128)
   BSA_CASE(64, 32) BSA_CASE(64, 64) BSA_CASE(64, 128)
@@ -1170,16 +1217,13 @@ bool forward_supported(int32_t bs, int32_t d) {
   return (bs == 16 || bs == 32 || bs == 64 || bs == 128) && (d == 32 || d == 64 || d == 128);
 }
 
-hipError_t launch_forward(const void *q, const void *k, const void *v, const int32_t *row_ptr,
-                          const int32_t *col_idx, const int32_t *row_order, int32_t B, int32_t H,
-                          int32_t Mb, int32_t Nb, int32_t bs, int32_t d, bool f32, float scale,
-                          const FwdOptions &opt, void *out, float *lse, hipStream_t stream) {
+hipError_t launch_forward(const void *q, const void *k, const void *v, const PlanArrays &pa,
+                          int32_t B, int32_t H, int32_t Mb, int32_t Nb, int32_t bs, int32_t d,
+                          bool f32, float scale, const FwdOptions &opt, void *out, float *lse,
+                          hipStream_t stream) {
   if (opt.kv_group < 1 || H % opt.kv_group != 0) return hipErrorInvalidValue;
-  if (f32)
-    return dispatch<float>(bs, d, q, k, v, row_ptr, col_idx, row_order, B, H, Mb, Nb, scale, opt,
-                           out, lse, stream);
-  return dispatch<__bf16>(bs, d, q, k, v, row_ptr, col_idx, row_order, B, H, Mb, Nb, scale, opt,
-                          out, lse, stream);
+  if (f32) return dispatch<float>(bs, d, q, k, v, pa, B, H, Mb, Nb, scale, opt, out, lse, stream);
+  return dispatch<__bf16>(bs, d, q, k, v, pa, B, H, Mb, Nb, scale, opt, out, lse, stream);
 }
 
 }  // namespace bsa

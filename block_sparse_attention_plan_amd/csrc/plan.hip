@@ -6,13 +6,26 @@
 // "Block Sparse Attention Techniques" tutorial (section 3.2), and adds a
 // load-balance order of the rows.  Rows are r = h * Mb + m.
 //
+// Beside the rows, the plan holds the pairs of neighbouring block rows
+// (2p, 2p+1) of each head: for pair q = h * Mp + p the union of the two rows'
+// live columns, ascending, each entry tagged with which of the two rows lists
+// it (n | mask << 24).  Layouts built from local windows, global columns and
+// strides repeat most columns from one block row to the next, so a forward
+// work item that covers a pair loads each shared tile once.  A flag records
+// whether the unions hold at most three quarters of the live tiles, which is
+// when the forward uses the pairs.
+//
 // Four kernels, all stream-ordered:
-//   count  one wave per row: live count by ballot + popcount -> row_ptr[r+1]
-//   scan   one workgroup: in-place inclusive scan of row_ptr[1..R] built from
-//          wavefront prefix scans; writes nnz_total
-//   fill   one wave per row: ballot + mbcnt compaction of the live columns
-//   order  one workgroup per head: stable counting sort of the head's rows by
-//          live count, descending; ties keep m ascending
+//   count  one wave per pair of rows: live counts of both rows and of their
+//          union by ballot + popcount -> row_ptr[r+1], pair_ptr[q+1]
+//   scan   one workgroup per array: in-place inclusive scans of row_ptr[1..R]
+//          and pair_ptr[1..Q] built from wavefront prefix scans; writes
+//          nnz_total and pair_total
+//   fill   one wave per pair of rows: ballot + mbcnt compaction of each row's
+//          live columns and of the union with its row tags
+//   order  one workgroup per head and array: stable counting sort of the
+//          head's rows (pairs) by live (union) count, descending; ties keep m
+//          (p) ascending; then the pair flag
 //
 // The backward's column plan is the same construction on the transposed
 // layout (columns c = h * Nb + n, the live query blocks m of each column in
@@ -23,6 +36,8 @@
 // the K/V head's group.
 // Every step is integer work with no atomics whose order matters, so the plan
 // is bit-for-bit deterministic.
+#include <algorithm>
+
 #include "bsa_device.h"
 #include "bsa_internal.h"
 
@@ -50,34 +65,60 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
+// One wave per pair q = h * Mp + p: rows r0 = h * Mb + 2p and r0 + 1 (the
+// second absent when 2p + 1 == Mb).
 __global__ void __launch_bounds__(256) plan_count_kernel(const int32_t *__restrict__ layout,
-                                                         int32_t R, int32_t Nb,
-                                                         int32_t *__restrict__ row_ptr) {
+                                                         int32_t H, int32_t Mb, int32_t Nb,
+                                                         int32_t *__restrict__ row_ptr,
+                                                         int32_t *__restrict__ pair_ptr) {
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
-  const int64_t r = (int64_t)blockIdx.x * (blockDim.x / kWave) + wave;
-  if (r == 0 && threadIdx.x == 0) row_ptr[0] = 0;
-  if (r >= R) return;
-  const int32_t *row = layout + r * (int64_t)Nb;
-  int cnt = 0;
+  const int Mp = (Mb + 1) / 2;
+  const int64_t q = (int64_t)blockIdx.x * (blockDim.x / kWave) + wave;
+  if (q == 0 && threadIdx.x == 0) {
+    row_ptr[0] = 0;
+    pair_ptr[0] = 0;
+  }
+  if (q >= (int64_t)H * Mp) return;
+  const int64_t h = q / Mp, p = q % Mp;
+  const int64_t r0 = h * Mb + 2 * p;
+  const bool two = 2 * p + 1 < Mb;
+  const int32_t *row0 = layout + r0 * (int64_t)Nb;
+  const int32_t *row1 = row0 + Nb;
+  int c0 = 0, c1 = 0, cu = 0;
   for (int n0 = 0; n0 < Nb; n0 += kWave) {
     const int n = n0 + lane;
-    const bool live = n < Nb && row[n] != 0;
-    cnt += __popcll(__ballot(live));
+    const bool a = n < Nb && row0[n] != 0;
+    const bool b = two && n < Nb && row1[n] != 0;
+    c0 += __popcll(__ballot(a));
+    c1 += __popcll(__ballot(b));
+    cu += __popcll(__ballot(a || b));
   }
-  if (lane == 0) row_ptr[r + 1] = cnt;
+  if (lane == 0) {
+    row_ptr[r0 + 1] = c0;
+    if (two) row_ptr[r0 + 2] = c1;
+    pair_ptr[q + 1] = cu;
+  }
 }
 
-// In-place inclusive scan of row_ptr[1..R] by one workgroup of 1024 threads.
-__global__ void __launch_bounds__(1024) plan_scan_kernel(int32_t R, int32_t *__restrict__ row_ptr,
-                                                         int32_t *__restrict__ nnz_total) {
+// In-place inclusive scan of ptr[1..n]; the total goes to *total.
+struct ScanJob {
+  int32_t n;
+  int32_t *ptr;
+  int32_t *total;
+};
+
+// One workgroup of 1024 threads per job (blockIdx.x selects the job).
+__global__ void __launch_bounds__(1024) plan_scan_kernel(ScanJob j0, ScanJob j1) {
   __shared__ int wave_tot[16];
   __shared__ int carry_s;
+  const ScanJob job = blockIdx.x == 0 ? j0 : j1;
+  const int64_t R = job.n;
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = lane_id();
   if (tid == 0) carry_s = 0;
   __syncthreads();
-  int32_t *a = row_ptr + 1;
+  int32_t *a = job.ptr + 1;
   for (int64_t base = 0; base < R; base += 1024) {
     const int64_t i = base + tid;
     const int x = i < R ? a[i] : 0;
@@ -92,26 +133,42 @@ __global__ void __launch_bounds__(1024) plan_scan_kernel(int32_t R, int32_t *__r
     if (tid == 1023) carry_s = carry + wave_off + incl;
     __syncthreads();
   }
-  if (tid == 0) *nnz_total = carry_s;
+  if (tid == 0) *job.total = carry_s;
 }
 
+// One wave per pair, as the count kernel: each row's live columns, and the
+// union with bit 24 (row 2p) and bit 25 (row 2p + 1) set per column.
 __global__ void __launch_bounds__(256) plan_fill_kernel(const int32_t *__restrict__ layout,
-                                                        int32_t R, int32_t Nb,
+                                                        int32_t H, int32_t Mb, int32_t Nb,
                                                         const int32_t *__restrict__ row_ptr,
-                                                        int32_t *__restrict__ col_idx) {
+                                                        int32_t *__restrict__ col_idx,
+                                                        const int32_t *__restrict__ pair_ptr,
+                                                        int32_t *__restrict__ pair_cols) {
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
-  const int64_t r = (int64_t)blockIdx.x * (blockDim.x / kWave) + wave;
-  if (r >= R) return;
-  const int32_t *row = layout + r * (int64_t)Nb;
-  int pos = row_ptr[r];
+  const int Mp = (Mb + 1) / 2;
+  const int64_t q = (int64_t)blockIdx.x * (blockDim.x / kWave) + wave;
+  if (q >= (int64_t)H * Mp) return;
+  const int64_t h = q / Mp, p = q % Mp;
+  const int64_t r0 = h * Mb + 2 * p;
+  const bool two = 2 * p + 1 < Mb;
+  const int32_t *row0 = layout + r0 * (int64_t)Nb;
+  const int32_t *row1 = row0 + Nb;
+  int pos0 = row_ptr[r0];
+  int pos1 = two ? row_ptr[r0 + 1] : 0;
+  int posu = pair_ptr[q];
   const uint64_t lt = lanemask_lt();
   for (int n0 = 0; n0 < Nb; n0 += kWave) {
     const int n = n0 + lane;
-    const bool live = n < Nb && row[n] != 0;
-    const uint64_t bal = __ballot(live);
-    if (live) col_idx[pos + __popcll(bal & lt)] = n;
-    pos += __popcll(bal);
+    const bool a = n < Nb && row0[n] != 0;
+    const bool b = two && n < Nb && row1[n] != 0;
+    const uint64_t ba = __ballot(a), bb = __ballot(b), bu = __ballot(a || b);
+    if (a) col_idx[pos0 + __popcll(ba & lt)] = n;
+    if (b) col_idx[pos1 + __popcll(bb & lt)] = n;
+    if (a || b) pair_cols[posu + __popcll(bu & lt)] = n | ((a ? 1 : 0) << 24) | ((b ? 1 : 0) << 25);
+    pos0 += __popcll(ba);
+    pos1 += __popcll(bb);
+    posu += __popcll(bu);
   }
 }
 
@@ -120,15 +177,31 @@ __global__ void __launch_bounds__(256) plan_fill_kernel(const int32_t *__restric
 // the extent ptr[(s g + j) items + i + 1] - ptr[(s g + j) items + i] (the live
 // count of a row for g = 1, of a key block summed over a head group for the
 // column plan).  Writes order[s items + rank] = s items + i.
+struct OrderJob {
+  int32_t segs, items, max_key, g;
+  const int32_t *ptr;
+  int32_t *order;
+};
+
+// The use-pairs flag: 1 when 4 * pair_total <= 3 * nnz_total.
+struct PairFlag {
+  const int32_t *nnz_total, *pair_total;
+  int32_t *flag;  // nullptr: no flag to write
+};
+
+// One workgroup per segment of job 0, then per segment of job 1.
 // Dynamic LDS: start[max_key+1] (bucket start, then running position) as int.
-__global__ void __launch_bounds__(256) plan_order_kernel(int32_t items, int32_t max_key, int32_t g,
-                                                         const int32_t *__restrict__ ptr,
-                                                         int32_t *__restrict__ order) {
+__global__ void __launch_bounds__(256) plan_order_kernel(OrderJob j0, OrderJob j1, PairFlag pf) {
   extern __shared__ int start[];
-  const int seg = blockIdx.x;
+  const bool first = (int)blockIdx.x < j0.segs;
+  const OrderJob job = first ? j0 : j1;
+  const int seg = first ? blockIdx.x : blockIdx.x - j0.segs;
+  const int items = job.items, max_key = job.max_key, g = job.g;
   const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && tid == 0 && pf.flag != nullptr)
+    *pf.flag = 4 * (int64_t)*pf.pair_total <= 3 * (int64_t)*pf.nnz_total ? 1 : 0;
   const int nkeys = max_key + 1;
-  const int32_t *sp = ptr + (int64_t)seg * g * items;
+  const int32_t *sp = job.ptr + (int64_t)seg * g * items;
   auto key_of = [&](int i) {
     int key = 0;
     for (int j = 0; j < g; ++j) key += sp[(int64_t)j * items + i + 1] - sp[(int64_t)j * items + i];
@@ -168,7 +241,7 @@ __global__ void __launch_bounds__(256) plan_order_kernel(int32_t items, int32_t 
       }
       const int rank = __popcll(same & lt);
       const int base = act ? start[key] : 0;
-      if (act) order[(int64_t)seg * items + base + rank] = seg * items + i;
+      if (act) job.order[(int64_t)seg * items + base + rank] = seg * items + i;
       // the lowest lane of each key group advances that key's position
       const bool leader = act && (same & lt) == 0;
       __builtin_amdgcn_wave_barrier();
@@ -207,16 +280,16 @@ __global__ void __launch_bounds__(256) plan_col_fill_kernel(const int32_t *__res
     if (col[(int64_t)m * Nb] != 0) row_idx[pos++] = m;
 }
 
-hipError_t launch_order(int32_t segs, int32_t items, int32_t max_key, int32_t g,
-                        const int32_t *ptr, int32_t *order, hipStream_t stream) {
-  const size_t lds = (size_t)(max_key + 1) * sizeof(int);
+hipError_t launch_order(const OrderJob &j0, const OrderJob &j1, const PairFlag &pf,
+                        hipStream_t stream) {
+  const size_t lds = (size_t)(std::max(j0.max_key, j1.max_key) + 1) * sizeof(int);
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void *)plan_order_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(plan_order_kernel, dim3(segs), dim3(256), lds, stream, items, max_key, g,
-                     ptr, order);
+  hipLaunchKernelGGL(plan_order_kernel, dim3(j0.segs + j1.segs), dim3(256), lds, stream, j0, j1,
+                     pf);
   return hipGetLastError();
 }
 
@@ -229,25 +302,37 @@ bool plan_geometry(int32_t H, int32_t Mb, int32_t Nb, PlanGeometry *g) {
   const int64_t tiles = (int64_t)H * Mb * Nb;
   if (tiles >= (int64_t(1) << 31)) return false;
   const size_t R = (size_t)H * Mb;
+  const size_t Q = (size_t)H * ((Mb + 1) / 2);
   g->off_row_ptr = 0;
   g->off_row_order = align256(g->off_row_ptr + (R + 1) * 4);
   g->off_nnz = align256(g->off_row_order + R * 4);
   g->off_col_idx = align256(g->off_nnz + 4);
-  g->total = align256(g->off_col_idx + (size_t)tiles * 4);
+  g->off_pair_ptr = align256(g->off_col_idx + (size_t)tiles * 4);
+  g->off_pair_order = align256(g->off_pair_ptr + (Q + 1) * 4);
+  g->off_pair_info = align256(g->off_pair_order + Q * 4);
+  g->off_pair_cols = align256(g->off_pair_info + 8);
+  g->total = align256(g->off_pair_cols + Q * (size_t)Nb * 4);
   return true;
 }
 
 hipError_t launch_plan(const int32_t *layout, int32_t H, int32_t Mb, int32_t Nb,
                        int32_t *row_ptr, int32_t *row_order, int32_t *nnz_total,
-                       int32_t *col_idx, hipStream_t stream) {
+                       int32_t *col_idx, int32_t *pair_ptr, int32_t *pair_order,
+                       int32_t *pair_info, int32_t *pair_cols, hipStream_t stream) {
   const int32_t R = H * Mb;
-  const int rows_per_block = 256 / kWave;
-  const int nblk = (R + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL(plan_count_kernel, dim3(nblk), dim3(256), 0, stream, layout, R, Nb, row_ptr);
-  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, R, row_ptr, nnz_total);
-  hipLaunchKernelGGL(plan_fill_kernel, dim3(nblk), dim3(256), 0, stream, layout, R, Nb,
-                     (const int32_t *)row_ptr, col_idx);
-  return launch_order(H, Mb, Nb, 1, row_ptr, row_order, stream);
+  const int32_t Mp = (Mb + 1) / 2;
+  const int32_t Q = H * Mp;
+  const int pairs_per_block = 256 / kWave;
+  const int nblk = (Q + pairs_per_block - 1) / pairs_per_block;
+  hipLaunchKernelGGL(plan_count_kernel, dim3(nblk), dim3(256), 0, stream, layout, H, Mb, Nb,
+                     row_ptr, pair_ptr);
+  hipLaunchKernelGGL(plan_scan_kernel, dim3(2), dim3(1024), 0, stream,
+                     ScanJob{R, row_ptr, nnz_total}, ScanJob{Q, pair_ptr, pair_info});
+  hipLaunchKernelGGL(plan_fill_kernel, dim3(nblk), dim3(256), 0, stream, layout, H, Mb, Nb,
+                     (const int32_t *)row_ptr, col_idx, (const int32_t *)pair_ptr, pair_cols);
+  return launch_order(OrderJob{H, Mb, Nb, 1, row_ptr, row_order},
+                      OrderJob{H, Mp, Nb, 1, pair_ptr, pair_order},
+                      PairFlag{nnz_total, pair_info, pair_info + 1}, stream);
 }
 
 bool plan_cols_geometry(int32_t H, int32_t Hkv, int32_t Mb, int32_t Nb, PlanColsGeometry *g) {
@@ -270,11 +355,14 @@ hipError_t launch_plan_cols(const int32_t *layout, int32_t H, int32_t Hkv, int32
   const int nblk = (C + 255) / 256;
   hipLaunchKernelGGL(plan_col_count_kernel, dim3(nblk), dim3(256), 0, stream, layout, H, Mb, Nb,
                      col_ptr);
-  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, C, col_ptr, nnz_total);
+  const ScanJob scan{C, col_ptr, nnz_total};
+  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, scan, scan);
   hipLaunchKernelGGL(plan_col_fill_kernel, dim3(nblk), dim3(256), 0, stream, layout, H, Mb, Nb,
                      (const int32_t *)col_ptr, row_idx);
   const int32_t g = H / Hkv;
-  return launch_order(Hkv, Nb, g * Mb, g, col_ptr, col_order, stream);
+  const OrderJob order{Hkv, Nb, g * Mb, g, col_ptr, col_order};
+  return launch_order(order, OrderJob{0, 0, 0, 1, nullptr, nullptr}, PairFlag{nullptr, nullptr, nullptr},
+                      stream);
 }
 
 }  // namespace bsa

@@ -55,6 +55,22 @@ typedef enum { BSA_BF16 = 0, BSA_F32 = 1 } bsa_dtype_t;
  *   nnz_total int32 [1]         number of live tiles (= row_ptr[H*Mb])
  *   col_idx   int32 [H*Mb*Nb]   live block columns of each row, ascending;
  *                               only the first nnz_total entries are written
+ * and the pairs of neighbouring block rows (offsets returned by
+ * bsa_plan_pair_sections), pair q = h * Mp + p, Mp = ceil(Mb / 2), joining
+ * rows 2p and 2p + 1 of head h (the second absent when Mb is odd):
+ *   pair_ptr   int32 [H*Mp + 1] exclusive prefix sum of the union counts
+ *   pair_order int32 [H*Mp]     pairs head by head, by union count
+ *                               descending, ties by p ascending
+ *   pair_info  int32 [2]        pair_total (= pair_ptr[H*Mp]); use_pairs:
+ *                               1 when 4 * pair_total <= 3 * nnz_total
+ *   pair_cols  int32 [H*Mp*Nb]  the union of the two rows' live columns,
+ *                               ascending, each entry n + 2^24 * mask
+ *                               (mask bit 0: row 2p lists n; bit 1: row
+ *                               2p + 1 does); pair_total entries written
+ * Layouts made of local windows, global columns and strides list nearly the
+ * same columns in neighbouring block rows; when use_pairs is set, bsa_forward
+ * (bf16, bs = 64, no score-changing option) runs one work item per pair and
+ * loads each tile the two rows share once.
  */
 typedef struct {
   int32_t H, Mb, Nb;
@@ -72,6 +88,11 @@ size_t bsa_plan_buffer_bytes(int32_t H, int32_t Mb, int32_t Nb);
  * BSA_ERR_INVALID_ARG for bad dimensions or a null output pointer. */
 int bsa_plan_sections(int32_t H, int32_t Mb, int32_t Nb, size_t offsets_out[4]);
 
+/* Byte offsets of the four pair sections (pair_ptr, pair_order, pair_info,
+ * pair_cols) inside the plan buffer.  Host-only; errors as
+ * bsa_plan_sections. */
+int bsa_plan_pair_sections(int32_t H, int32_t Mb, int32_t Nb, size_t offsets_out[4]);
+
 /*
  * Build the plan of a block layout.
  *
@@ -80,7 +101,8 @@ int bsa_plan_sections(int32_t H, int32_t Mb, int32_t Nb, size_t offsets_out[4]);
  * live b x b tile of Q K^T.  Storing only the live tiles with their column
  * indices is the CSR form of the next.gr "Block Sparse Attention Techniques"
  * tutorial, section 3.2.  Per-row counts, their prefix scan and the per-row
- * column lists follow from it; row_order adds the load-balance order.
+ * column lists follow from it; row_order adds the load-balance order, and the
+ * pair sections the same lists for pairs of neighbouring block rows.
  *
  *   layout    device, int32 [H, Mb, Nb], read only
  *   dev_buf   device, caller-owned, >= bsa_plan_buffer_bytes(H, Mb, Nb) bytes,

@@ -38,6 +38,8 @@ def to64(t: torch.Tensor) -> np.ndarray:
 
 
 def check_plan(dev, layout: np.ndarray):
+    """The GPU plan against the oracle's, bit for bit: rows, and the pairs of
+    neighbouring rows with their use flag."""
     ref = O.plan(layout)
     p = bsa.bsa_plan(torch.from_numpy(np.ascontiguousarray(layout, dtype=np.int32)).to(dev))
     nnz = p.nnz()
@@ -45,6 +47,12 @@ def check_plan(dev, layout: np.ndarray):
     assert torch.equal(p.row_ptr.cpu(), torch.from_numpy(ref.row_ptr))
     assert torch.equal(p.row_order.cpu(), torch.from_numpy(ref.row_order))
     assert torch.equal(p.col_idx(nnz).cpu(), torch.from_numpy(ref.col_idx))
+    pref = O.plan_pairs(layout)
+    info = p.pair_info.cpu().tolist()
+    assert info == [pref.pair_total, pref.use_pairs]
+    assert torch.equal(p.pair_ptr.cpu(), torch.from_numpy(pref.pair_ptr))
+    assert torch.equal(p.pair_order.cpu(), torch.from_numpy(pref.pair_order))
+    assert torch.equal(p.pair_cols(pref.pair_total).cpu(), torch.from_numpy(pref.pair_cols))
     return p, ref
 
 

@@ -92,7 +92,11 @@ def test_forward_segments_equal_reduced_layout(gpu, bs, d, lengths):
     """Segments that start and end on block boundaries mask exactly the tiles
     between different segments, so the forward with segment ids (which skips
     the pieces whose keys all lie in other segments) equals the forward
-    without them on the layout with those tiles removed."""
+    without them on the layout with those tiles removed.  At bs = 64 the
+    reduced layout's neighbouring rows share tiles, so its forward runs in the
+    paired form (64-key pieces instead of 32), whose bf16 weights and rescale
+    points differ: there the two agree to the rounding of the bf16 output and
+    weights (2^-8 absolute plus 2^-7 relative), and both meet the oracle."""
     S = sum(lengths)
     H, nb = 2, S // bs
     seg = np.repeat(np.arange(len(lengths), dtype=np.int32), lengths)[None]     # [1, S]
@@ -111,7 +115,9 @@ def test_forward_segments_equal_reduced_layout(gpu, bs, d, lengths):
     out, lse = bsa.bsa_forward(q, k, v, plan, x.scale, bs=bs, q_segment_ids=sg, kv_segment_ids=sg)
     out_r, lse_r = bsa.bsa_forward(q, k, v, plan_r, x.scale, bs=bs)
     torch.cuda.synchronize()
-    assert torch.allclose(out.float(), out_r.float(), atol=2 ** -8, rtol=0)
+    diff = (out.float() - out_r.float()).abs().max().item()
+    say(f"  segment ids vs reduced layout: max |diff| {diff:.3e}")
+    assert torch.allclose(out.float(), out_r.float(), atol=2 ** -8, rtol=2 ** -7 if bs == 64 else 0)
     assert torch.allclose(lse, lse_r, atol=1e-5, rtol=0)
     ref, _ = O.attention_live_tiles(to64(x.q), to64(x.k), to64(x.v), reduced, bs, x.scale)
     compare(to64(out), ref, f"segments reduced bs={bs} d={d}")
