@@ -46,8 +46,9 @@ of 1 GiB, for HBM counter scaling under a profiler), --option-steps N (launches
 of the forward with options; 0 skips that leg), --backward-steps N (calls of
 the backward; 0 skips that leg), --adaptive-steps N (calls of the adaptive
 layout producer; 0 skips that leg), --variant-steps N (calls of each of the three
-forms above; 0 skips them), --config-steps N (launches of the second workload
-and of each cold-cache leg; 0 skips them).
+forms above; 0 skips them), --config-steps N (launches of each cold-cache leg;
+0 skips them and the second workload), --config-warm-steps N (warm launches of
+the second workload, after 5 warm-up launches).
 
 --summarize-counters FETCH_CSV WRITE_CSV (no GPU needed) turns the counter
 files of two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of
@@ -290,7 +291,8 @@ def main(argv=None) -> int:
     ap.add_argument("--backward-steps", type=int, default=10)
     ap.add_argument("--adaptive-steps", type=int, default=20)
     ap.add_argument("--variant-steps", type=int, default=10)
-    ap.add_argument("--config-steps", type=int, default=10)
+    ap.add_argument("--config-steps", type=int, default=20)
+    ap.add_argument("--config-warm-steps", type=int, default=100)
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
@@ -532,10 +534,10 @@ def main(argv=None) -> int:
         l_lse = torch.empty((lB, lH, lS), dtype=torch.float32, device=dev)
         l_plan = bsa.bsa_plan(l_layout)
         fn = lambda: bsa.bsa_forward(lq, lk, lv, l_plan, lw.scale, out=l_out, lse=l_lse)  # noqa: E731
-        for _ in range(3):
+        for _ in range(5):
             fn()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.config_steps)]
+              for _ in range(max(1, args.config_warm_steps))]
         torch.cuda.synchronize()
         for a, b in ev:
             a.record()
@@ -548,7 +550,7 @@ def main(argv=None) -> int:
         t_l = sum(warm) / len(warm)
         l_tf = l_flops / (t_l * 1e-3) / 1e12
         lgs_leg = {"workload": LGS_WORKLOAD, "avg_ms": round(t_l, 5), **percentiles(warm),
-                   "launches": args.config_steps, "live_tiles": l_tiles, "flops": l_flops,
+                   "launches": len(warm), "live_tiles": l_tiles, "flops": l_flops,
                    "tflops": round(l_tf, 2), "pct_bf16_peak": round(100 * l_tf / PEAK_BF16_TFLOPS, 2),
                    "algorithmic_bytes": l_bytes,
                    "algorithmic_gbs": round(l_bytes / (t_l * 1e-3) / 1e9, 1),
