@@ -1,10 +1,13 @@
 """Build libbsa.so (gfx950) in-tree with hipcc.
 
-    python -m block_sparse_attention_plan_amd.build [--jobs N]
+    python -m block_sparse_attention_plan_amd.build [--jobs N] [--sanitize]
 
 Each csrc/*.hip file is compiled to an object under _build/ and the objects
 are linked into block_sparse_attention_plan_amd/libbsa.so.  Every call
-rebuilds from scratch, so the library always matches the sources.
+rebuilds from scratch, so the library always matches the sources.  With
+--sanitize the host code is built with AddressSanitizer and
+UndefinedBehaviorSanitizer into _build/asan/libbsa.so instead, for the host
+ABI checks (tests/abi_host_check.cpp).
 """
 
 from __future__ import annotations
@@ -56,33 +59,52 @@ def _run(cmd: list) -> None:
         print(out, file=sys.stderr)
 
 
-def build(jobs: int = 8, verbose: bool = False) -> str:
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for the C ABI
+# layer (argument validation, plan geometry, error reporting).  Each
+# -fsanitize= applies to the host compilation only: device code is built as
+# in the release library.  The shared library leaves the sanitizer runtime
+# to the executable that loads it.
+SANITIZE_FLAGS = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all",
+]
+SANITIZED_LIB = os.path.join(BUILD_DIR, "asan", "libbsa.so")
+
+
+def build(jobs: int = 8, verbose: bool = False, sanitize: bool = False) -> str:
+    """Build the release library (in the package), or with sanitize=True the
+    host-sanitized one under _build/asan/ (for the host ABI checks)."""
     cc = hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    out_dir = os.path.dirname(SANITIZED_LIB) if sanitize else BUILD_DIR
+    lib_path = SANITIZED_LIB if sanitize else LIB_PATH
+    extra = SANITIZE_FLAGS if sanitize else []
+    os.makedirs(out_dir, exist_ok=True)
     srcs = sources()
-    objs = [os.path.join(BUILD_DIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    objs = [os.path.join(out_dir, os.path.basename(s)[:-4] + ".o") for s in srcs]
 
     def compile_one(pair):
         src, obj = pair
-        cmd = [cc, *HIPCC_FLAGS, "-c", src, "-o", obj]
+        cmd = [cc, *HIPCC_FLAGS, *extra, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), file=sys.stderr)
         _run(cmd)
 
     with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
         list(ex.map(compile_one, zip(srcs, objs)))
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--jobs", type=int, default=8)
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--sanitize", action="store_true",
+                    help="host-side ASan/UBSan build under _build/asan/ (not the package library)")
     args = ap.parse_args(argv)
-    path = build(args.jobs, args.verbose)
+    path = build(args.jobs, args.verbose, sanitize=args.sanitize)
     print(path)
     return 0
 

@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <mutex>
 
 #include "bsa.h"
@@ -25,6 +26,16 @@ int hip_fail(hipError_t e, const char *where) {
 }
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// The integer a caller passed as a bsa_dtype_t.  A C caller may pass any int;
+// reading it through the enum type would be undefined for values outside the
+// enumerators, so the bits are copied out instead.
+int dtype_code(const bsa_dtype_t &d) {
+  int v;
+  static_assert(sizeof(v) == sizeof(d), "bsa_dtype_t is int-sized");
+  std::memcpy(&v, &d, sizeof(v));
+  return v;
+}
 
 // Blocks covering S tokens: the last one is cut where S is not a multiple.
 int64_t blocks(int32_t S, int32_t bs) { return ((int64_t)S + bs - 1) / bs; }
@@ -138,7 +149,7 @@ int scratch_address(void **out) {
 int backward_impl(const char *who, const void *q, const void *k, const void *v, const void *out,
                   const void *dout, const float *lse, const bsa_plan_t *plan,
                   const bsa_plan_cols_t *plan_cols, int32_t B, int32_t H, int32_t Sq, int32_t Sk,
-                  int32_t bs, int32_t d, bsa_dtype_t dtype, float scale,
+                  int32_t bs, int32_t d, int dtype, float scale,
                   const bsa_forward_opts_t *opts, bool use_scratch, void *workspace,
                   size_t workspace_bytes, void *dq, void *dk, void *dv, float *dsink,
                   void *stream) {
@@ -159,7 +170,7 @@ int backward_impl(const char *who, const void *q, const void *k, const void *v, 
                 "%s: H=%d Sq=%d Sk=%d bs=%d do not match plan H=%d Mb=%d Nb=%d", who, H, Sq,
                 Sk, bs, plan->H, plan->Mb, plan->Nb);
   if (dtype != BSA_BF16 && dtype != BSA_F32)
-    return fail(BSA_ERR_INVALID_ARG, "%s: unknown dtype %d", who, (int)dtype);
+    return fail(BSA_ERR_INVALID_ARG, "%s: unknown dtype %d", who, dtype);
   if (!(std::isfinite(scale) && scale > 0.f))
     return fail(BSA_ERR_INVALID_ARG, "%s: scale must be finite and > 0", who);
   bsa::FwdOptions fo;
@@ -300,10 +311,14 @@ int bsa_plan_nnz(const bsa_plan_t *plan, int64_t *nnz_host, void *stream) {
   return BSA_OK;
 }
 
-int bsa_forward_ex(const void *q, const void *k, const void *v, const bsa_plan_t *plan,
-                   int32_t B, int32_t H, int32_t Sq, int32_t Sk, int32_t bs, int32_t d,
-                   bsa_dtype_t dtype, float scale, const bsa_forward_opts_t *opts, void *out,
-                   float *lse, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward behind bsa_forward and bsa_forward_ex (dtype as the caller's int).
+int forward_impl(const void *q, const void *k, const void *v, const bsa_plan_t *plan, int32_t B,
+                 int32_t H, int32_t Sq, int32_t Sk, int32_t bs, int32_t d, int dtype, float scale,
+                 const bsa_forward_opts_t *opts, void *out, float *lse, void *stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
     return fail(BSA_ERR_INVALID_ARG, "bsa_forward: NULL tensor pointer");
   bsa::PlanGeometry g;
@@ -316,7 +331,7 @@ int bsa_forward_ex(const void *q, const void *k, const void *v, const bsa_plan_t
                 "bsa_forward: H=%d Sq=%d Sk=%d bs=%d do not match plan H=%d Mb=%d Nb=%d", H, Sq,
                 Sk, bs, plan->H, plan->Mb, plan->Nb);
   if (dtype != BSA_BF16 && dtype != BSA_F32)
-    return fail(BSA_ERR_INVALID_ARG, "bsa_forward: unknown dtype %d", (int)dtype);
+    return fail(BSA_ERR_INVALID_ARG, "bsa_forward: unknown dtype %d", dtype);
   if (!(std::isfinite(scale) && scale > 0.f))
     return fail(BSA_ERR_INVALID_ARG, "bsa_forward: scale must be finite and > 0");
   if (!bsa::forward_supported(bs, d))
@@ -344,11 +359,23 @@ int bsa_forward_ex(const void *q, const void *k, const void *v, const bsa_plan_t
   return BSA_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int bsa_forward_ex(const void *q, const void *k, const void *v, const bsa_plan_t *plan,
+                   int32_t B, int32_t H, int32_t Sq, int32_t Sk, int32_t bs, int32_t d,
+                   bsa_dtype_t dtype, float scale, const bsa_forward_opts_t *opts, void *out,
+                   float *lse, void *stream) {
+  return forward_impl(q, k, v, plan, B, H, Sq, Sk, bs, d, dtype_code(dtype), scale, opts, out,
+                      lse, stream);
+}
+
 int bsa_forward(const void *q, const void *k, const void *v, const bsa_plan_t *plan, int32_t B,
                 int32_t H, int32_t Sq, int32_t Sk, int32_t bs, int32_t d, bsa_dtype_t dtype,
                 float scale, void *out, float *lse, void *stream) {
-  return bsa_forward_ex(q, k, v, plan, B, H, Sq, Sk, bs, d, dtype, scale, nullptr, out, lse,
-                        stream);
+  return forward_impl(q, k, v, plan, B, H, Sq, Sk, bs, d, dtype_code(dtype), scale, nullptr, out,
+                      lse, stream);
 }
 
 size_t bsa_plan_cols_buffer_bytes(int32_t H, int32_t Hkv, int32_t Mb, int32_t Nb) {
@@ -413,8 +440,8 @@ int bsa_backward(const void *q, const void *k, const void *v, const void *out, c
                  size_t workspace_bytes, void *dq, void *dk, void *dv, float *dsink,
                  void *stream) {
   return backward_impl("bsa_backward", q, k, v, out, dout, lse, plan, plan_cols, B, H, Sq, Sk,
-                       bs, d, dtype, scale, opts, false, workspace, workspace_bytes, dq, dk, dv,
-                       dsink, stream);
+                       bs, d, dtype_code(dtype), scale, opts, false, workspace, workspace_bytes,
+                       dq, dk, dv, dsink, stream);
 }
 
 size_t bsa_backward_noalloc_max_rows(void) { return kNoAllocScratchBytes / (2 * sizeof(float)); }
@@ -426,8 +453,8 @@ int bsa_backward_noalloc(const void *q, const void *k, const void *v, const void
                          const bsa_forward_opts_t *opts, void *dq, void *dk, void *dv,
                          float *dsink, void *stream) {
   return backward_impl("bsa_backward_noalloc", q, k, v, out, dout, lse, plan, plan_cols, B, H,
-                       Sq, Sk, bs, d, dtype, scale, opts, true, nullptr, 0, dq, dk, dv, dsink,
-                       stream);
+                       Sq, Sk, bs, d, dtype_code(dtype), scale, opts, true, nullptr, 0, dq, dk,
+                       dv, dsink, stream);
 }
 
 size_t bsa_layout_adaptive_workspace_bytes(int32_t H, int32_t Hkv, int32_t Mb, int32_t Nb,
@@ -451,8 +478,9 @@ int bsa_layout_adaptive(const void *q, const void *k, int32_t H, int32_t Hkv, in
   if (Sq % bs != 0 || Sk % bs != 0)
     return fail(BSA_ERR_INVALID_ARG, "bsa_layout_adaptive: Sq=%d and Sk=%d must be multiples of "
                 "bs=%d", Sq, Sk, bs);
-  if (dtype != BSA_BF16 && dtype != BSA_F32)
-    return fail(BSA_ERR_INVALID_ARG, "bsa_layout_adaptive: unknown dtype %d", (int)dtype);
+  const int dt = dtype_code(dtype);
+  if (dt != BSA_BF16 && dt != BSA_F32)
+    return fail(BSA_ERR_INVALID_ARG, "bsa_layout_adaptive: unknown dtype %d", dt);
   if (!std::isfinite(tau))
     return fail(BSA_ERR_INVALID_ARG, "bsa_layout_adaptive: tau must be finite");
   if (!bsa::adaptive_supported(bs, d))
@@ -467,7 +495,7 @@ int bsa_layout_adaptive(const void *q, const void *k, int32_t H, int32_t Hkv, in
   if (workspace_bytes < ws)
     return fail(BSA_ERR_BUFFER_TOO_SMALL, "bsa_layout_adaptive: workspace is %zu bytes, needs %zu",
                 workspace_bytes, ws);
-  hipError_t e = bsa::launch_adaptive(q, k, H, Hkv, Mb, Nb, bs, d, dtype == BSA_F32, tau,
+  hipError_t e = bsa::launch_adaptive(q, k, H, Hkv, Mb, Nb, bs, d, dt == BSA_F32, tau,
                                       causal != 0, keep_diagonal != 0,
                                       static_cast<float *>(workspace), layout_out, scores_out,
                                       (hipStream_t)stream);
