@@ -15,6 +15,8 @@ missing, every call raises.
     bsa_backward_noalloc(..., dq=, dk=, dv=, dsink=)  (no allocation; static scratch)
     bsa_layout_adaptive(q, k, bs, tau, causal, keep_diagonal) -> (layout, scores)
     topk_sparse_attn(q, kv, idx, attn_sink, scale) -> out
+    bsa_plan_check(plan, plan_cols)       consistency of plan contents (raises)
+    set_debug(on)                         check plans before every call
 """
 
 from __future__ import annotations
@@ -39,6 +41,8 @@ __all__ = [
     "bsa_backward_noalloc",
     "bsa_layout_adaptive",
     "topk_sparse_attn",
+    "bsa_plan_check",
+    "set_debug",
     "library_path",
     "load_library",
 ]
@@ -130,6 +134,13 @@ def load_library():
     lib.bsa_layout_adaptive.restype = ctypes.c_int
     lib.topk_sparse_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp]
     lib.topk_sparse_attn.restype = ctypes.c_int
+    lib.bsa_plan_check.argtypes = [ctypes.POINTER(_PlanT), ctypes.POINTER(_PlanColsT), vp]
+    lib.bsa_plan_check.restype = ctypes.c_int
+    lib.bsa_plan_check_host.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_size_t, i32, i32, i32,
+                                        i32]
+    lib.bsa_plan_check_host.restype = ctypes.c_int
+    lib.bsa_set_debug.argtypes = [ctypes.c_int]
+    lib.bsa_set_debug.restype = ctypes.c_int
     lib.bsa_status_string.argtypes = [ctypes.c_int]
     lib.bsa_status_string.restype = ctypes.c_char_p
     lib.bsa_last_error.argtypes = []
@@ -431,6 +442,26 @@ def bsa_plan_cols(layout: torch.Tensor, kv_heads: Optional[int] = None,
                              ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.byref(raw),
                              _stream(layout)))
     return PlanCols(buf, raw, H, Hkv, Mb, Nb)
+
+
+def bsa_plan_check(plan: Optional[Plan] = None, plan_cols: Optional[PlanCols] = None) -> None:
+    """Check the contents of a plan and/or a column plan (and, given both,
+    that one is the other's transpose); raises BsaError (status
+    BSA_ERR_BAD_PLAN = -7) naming the first inconsistency.  Synchronises the
+    current stream."""
+    if plan is None and plan_cols is None:
+        raise ValueError("give a plan, a column plan or both")
+    buf = plan.buf if plan is not None else plan_cols.buf
+    _check(load_library().bsa_plan_check(
+        ctypes.byref(plan._raw) if plan is not None else None,
+        ctypes.byref(plan_cols._raw) if plan_cols is not None else None, _stream(buf)))
+
+
+def set_debug(on: bool) -> bool:
+    """Debug mode: every call that reads a plan checks it first (as
+    bsa_plan_check) and refuses an inconsistent one.  Returns the previous
+    setting.  The environment variable BSA_DEBUG sets the initial value."""
+    return bool(load_library().bsa_set_debug(1 if on else 0))
 
 
 def _backward_args(q, k, v, out, dout, lse, plan, scale, attn_sink, soft_cap, causal, dq, dk,

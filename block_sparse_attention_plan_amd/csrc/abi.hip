@@ -1,10 +1,13 @@
 // C ABI of libbsa: argument validation, error reporting and dispatch to the
 // kernel launchers.  Every check here runs on the host before any HIP call.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "bsa.h"
 #include "bsa_internal.h"
@@ -65,6 +68,80 @@ int check_plan_cols(const bsa_plan_cols_t *pc, bsa::PlanColsGeometry *g) {
     return fail(BSA_ERR_BUFFER_TOO_SMALL, "column plan buffer is %zu bytes, needs %zu",
                 pc->dev_bytes, g->total);
   return BSA_OK;
+}
+
+// Debug mode (environment variable BSA_DEBUG set to anything but "" or "0",
+// or bsa_set_debug): every call that reads a plan first copies it to the
+// host and checks it, and refuses to launch on an inconsistent one.
+std::atomic<int> g_debug{-1};   // -1: environment not read yet
+
+bool debug_on() {
+  int v = g_debug.load(std::memory_order_relaxed);
+  if (v < 0) {
+    const char *e = std::getenv("BSA_DEBUG");
+    int want = (e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0) ? 1 : 0;
+    g_debug.compare_exchange_strong(v, want);
+    v = g_debug.load(std::memory_order_relaxed);
+  }
+  return v != 0;
+}
+
+// `bytes` bytes of device memory into a host vector, after the work already
+// queued on the stream.
+int fetch(const void *dev, size_t bytes, std::vector<char> *host, hipStream_t stream,
+          const char *who) {
+  host->resize(bytes);
+  hipError_t e = hipMemcpyAsync(host->data(), dev, bytes, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, who);
+  return BSA_OK;
+}
+
+// Checks host copies of a plan and/or a column plan (either may be NULL) and,
+// given both, that one is the other's transpose.
+int check_host_copies(const void *rows, size_t rows_bytes, const void *cols, size_t cols_bytes,
+                      int32_t H, int32_t Hkv, int32_t Mb, int32_t Nb, const char *who) {
+  char msg[320];
+  if (rows != nullptr && !bsa::check_plan_host(rows, rows_bytes, H, Mb, Nb, msg, sizeof(msg)))
+    return fail(BSA_ERR_BAD_PLAN, "%s: plan: %s", who, msg);
+  if (cols != nullptr &&
+      !bsa::check_plan_cols_host(cols, cols_bytes, H, Hkv, Mb, Nb, msg, sizeof(msg)))
+    return fail(BSA_ERR_BAD_PLAN, "%s: column plan: %s", who, msg);
+  if (rows != nullptr && cols != nullptr &&
+      !bsa::check_transpose_host(rows, cols, H, Hkv, Mb, Nb, msg, sizeof(msg)))
+    return fail(BSA_ERR_BAD_PLAN, "%s: plans disagree: %s", who, msg);
+  return BSA_OK;
+}
+
+// The device-side plans (already validated as arguments) checked through
+// host copies.
+int check_device_plans(const bsa_plan_t *plan, const bsa_plan_cols_t *pc, void *stream,
+                       const char *who) {
+  std::vector<char> rows, cols;
+  size_t rows_bytes = 0, cols_bytes = 0;
+  int32_t H = 0, Hkv = 0, Mb = 0, Nb = 0;
+  if (plan != nullptr) {
+    bsa::PlanGeometry g;
+    int st = check_plan(plan, &g);
+    if (st != BSA_OK) return st;
+    st = fetch(plan->dev_buf, g.total, &rows, (hipStream_t)stream, who);
+    if (st != BSA_OK) return st;
+    rows_bytes = g.total;
+    H = plan->H; Mb = plan->Mb; Nb = plan->Nb; Hkv = H;
+  }
+  if (pc != nullptr) {
+    bsa::PlanColsGeometry g;
+    int st = check_plan_cols(pc, &g);
+    if (st != BSA_OK) return st;
+    if (plan != nullptr && (pc->H != H || pc->Mb != Mb || pc->Nb != Nb))
+      return fail(BSA_ERR_PLAN_MISMATCH, "%s: the plans have different dimensions", who);
+    st = fetch(pc->dev_buf, g.total, &cols, (hipStream_t)stream, who);
+    if (st != BSA_OK) return st;
+    cols_bytes = g.total;
+    H = pc->H; Hkv = pc->Hkv; Mb = pc->Mb; Nb = pc->Nb;
+  }
+  return check_host_copies(plan != nullptr ? rows.data() : nullptr, rows_bytes,
+                           pc != nullptr ? cols.data() : nullptr, cols_bytes, H, Hkv, Mb, Nb, who);
 }
 
 // Options of the forward (and of the backward, which must repeat them),
@@ -210,6 +287,10 @@ int backward_impl(const char *who, const void *q, const void *k, const void *v, 
     st = scratch_address(&workspace);
     if (st != BSA_OK) return st;
   }
+  if (debug_on()) {
+    st = check_device_plans(plan, plan_cols, stream, who);
+    if (st != BSA_OK) return st;
+  }
   bsa::BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse;
   a.row_ptr = at<int32_t>(plan->dev_buf, g.off_row_ptr);
@@ -346,6 +427,10 @@ int forward_impl(const void *q, const void *k, const void *v, const bsa_plan_t *
   if (st != BSA_OK) return st;
   fo.sq = Sq;
   fo.sk = Sk;
+  if (debug_on()) {
+    st = check_device_plans(plan, nullptr, stream, "bsa_forward");
+    if (st != BSA_OK) return st;
+  }
   const bsa::PlanArrays pa{at<int32_t>(plan->dev_buf, g.off_row_ptr),
                            at<int32_t>(plan->dev_buf, g.off_col_idx),
                            at<int32_t>(plan->dev_buf, g.off_row_order),
@@ -527,6 +612,41 @@ int topk_sparse_attn(const void *q, const void *kv, const int32_t *idx, const fl
   return BSA_OK;
 }
 
+int bsa_set_debug(int on) {
+  const int prev = debug_on() ? 1 : 0;
+  g_debug.store(on != 0 ? 1 : 0);
+  return prev;
+}
+
+int bsa_plan_check(const bsa_plan_t *plan, const bsa_plan_cols_t *plan_cols, void *stream) {
+  if (plan == nullptr && plan_cols == nullptr)
+    return fail(BSA_ERR_INVALID_ARG, "bsa_plan_check: no plan given");
+  return check_device_plans(plan, plan_cols, stream, "bsa_plan_check");
+}
+
+int bsa_plan_check_host(const void *plan_host, size_t plan_bytes, const void *cols_host,
+                        size_t cols_bytes, int32_t H, int32_t Hkv, int32_t Mb, int32_t Nb) {
+  if (plan_host == nullptr && cols_host == nullptr)
+    return fail(BSA_ERR_INVALID_ARG, "bsa_plan_check_host: no plan given");
+  if (Hkv == 0) Hkv = H;
+  if (H <= 0 || Hkv <= 0 || Mb <= 0 || Nb <= 0 || H % Hkv != 0)
+    return fail(BSA_ERR_INVALID_ARG, "bsa_plan_check_host: invalid dimensions H=%d Hkv=%d Mb=%d Nb=%d",
+                H, Hkv, Mb, Nb);
+  bsa::PlanGeometry g;
+  bsa::PlanColsGeometry gc;
+  if (!bsa::plan_geometry(H, Mb, Nb, &g) || !bsa::plan_cols_geometry(H, Hkv, Mb, Nb, &gc))
+    return fail(BSA_ERR_INVALID_ARG, "bsa_plan_check_host: invalid dimensions");
+  if (plan_host != nullptr && plan_bytes < g.total)
+    return fail(BSA_ERR_BUFFER_TOO_SMALL, "bsa_plan_check_host: plan copy is %zu bytes, needs %zu",
+                plan_bytes, g.total);
+  if (cols_host != nullptr && cols_bytes < gc.total)
+    return fail(BSA_ERR_BUFFER_TOO_SMALL,
+                "bsa_plan_check_host: column plan copy is %zu bytes, needs %zu", cols_bytes,
+                gc.total);
+  return check_host_copies(plan_host, plan_bytes, cols_host, cols_bytes, H, Hkv, Mb, Nb,
+                           "bsa_plan_check_host");
+}
+
 const char *bsa_status_string(int status) {
   switch (status) {
     case BSA_OK: return "ok";
@@ -536,6 +656,7 @@ const char *bsa_status_string(int status) {
     case BSA_ERR_PLAN_MISMATCH: return "plan does not match the call";
     case BSA_ERR_BUFFER_TOO_SMALL: return "buffer too small";
     case BSA_ERR_HIP: return "HIP runtime error";
+    case BSA_ERR_BAD_PLAN: return "inconsistent plan contents";
     default: return "unknown status";
   }
 }

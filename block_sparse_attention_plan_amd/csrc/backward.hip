@@ -57,20 +57,34 @@ template <int D> struct BSwz {
 // of the workgroup share its 1 KiB copy instructions.  Only the first `bytes`
 // bytes exist (a block cut at the sequence end): the rest read as zeros (the
 // whole offset is per lane, where the buffer range check applies).
+//
+// A wave's successive copies are STEP rows apart, and the swizzle depends on
+// the row modulo 16 only, so the per-lane offsets repeat with period P; copy
+// j reuses the offset of copy j % P and moves the (scalar) buffer base by the
+// whole periods instead, which keeps P vector registers live, not NI / NW.
 template <int BS, int D, int NW>
 __device__ __forceinline__ void copy_tile(const __bf16 *src, __bf16 *dst, int wid, int lane,
                                           uint32_t bytes = BS * D * 2) {
   constexpr int CPR = D / 8;
   constexpr int NI = BS * D * 2 / 1024;
   constexpr int RPI = 64 / CPR;
+  constexpr int STEP = RPI * NW;
+  constexpr int P0 = STEP % 16 == 0 ? 1 : STEP % 8 == 0 ? 2 : STEP % 4 == 0 ? 4
+                   : STEP % 2 == 0 ? 8 : 16;
+  constexpr int P = P0 < NI / NW ? P0 : NI / NW;
   static_assert(NI % NW == 0, "copies must split evenly over the waves");
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, bytes);
+  uint32_t voff[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int row = RPI * (wid + NW * p) + lane / CPR;
+    voff[p] = (uint32_t)((row * D + (((lane % CPR) ^ BSwz<D>::f(row)) << 3)) * 2);
+  }
 #pragma unroll
   for (int j = 0; j < NI / NW; ++j) {
-    const int i = wid + NW * j;
-    const int row = RPI * i + lane / CPR;
-    const int logical = (lane % CPR) ^ BSwz<D>::f(row);
-    copy16_to_lds(rs, dst + i * 512, (uint32_t)((row * D + logical * 8) * 2), 0u);
+    const uint32_t shift = (uint32_t)((j - j % P) * STEP * D * 2);   // bytes
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(reinterpret_cast<const char *>(src) + shift, bytes > shift ? bytes - shift : 0u);
+    copy16_to_lds(rs, dst + (wid + NW * j) * 512, voff[j % P], 0u);
   }
 }
 

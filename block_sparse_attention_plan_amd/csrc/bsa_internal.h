@@ -62,6 +62,17 @@ hipError_t launch_plan_cols(const int32_t *layout, int32_t H, int32_t Hkv, int32
                             int32_t *col_ptr, int32_t *col_order, int32_t *nnz_total,
                             int32_t *row_idx, hipStream_t stream);
 
+// Host-side consistency checks of plans copied to host memory (buf holds
+// `bytes` bytes laid out as the plan buffer).  Each returns false with the
+// first violation described in msg; the transpose check assumes both plans
+// passed their own check.
+bool check_plan_host(const void *buf, size_t bytes, int32_t H, int32_t Mb, int32_t Nb, char *msg,
+                     size_t mlen);
+bool check_plan_cols_host(const void *buf, size_t bytes, int32_t H, int32_t Hkv, int32_t Mb,
+                          int32_t Nb, char *msg, size_t mlen);
+bool check_transpose_host(const void *rows, const void *cols, int32_t H, int32_t Hkv, int32_t Mb,
+                          int32_t Nb, char *msg, size_t mlen);
+
 // Everything the backward launchers need (already validated).
 struct BwdArgs {
   const void *q, *k, *v, *out, *dout;

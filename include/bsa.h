@@ -9,12 +9,18 @@
  *   returns, except inside a caller-owned plan buffer).
  * - `stream` is a hipStream_t passed as void*; NULL means the default stream.
  *   All compute calls are asynchronous and ordered on that stream.  Only
- *   bsa_plan_nnz synchronises (it copies one integer to the host).
+ *   bsa_plan_nnz (one integer to the host), bsa_plan_check and calls made
+ *   in debug mode (below) synchronise it.
  * - Return value: BSA_OK (0) or a negative bsa_status_t.  Host-side argument
  *   validation runs before any HIP call, so an invalid call touches neither
  *   the GPU nor the output buffers.  Launch failures are reported as
  *   BSA_ERR_HIP; faults inside a kernel surface at the caller's next sync.
  *   bsa_last_error() returns a thread-local message for the last failure.
+ * - Debug mode (environment variable BSA_DEBUG set and not "0" when the
+ *   library is first used, or bsa_set_debug(1)): every call that reads a
+ *   plan first copies the plan to the host, checks it as bsa_plan_check
+ *   does and synchronises the stream; an inconsistent plan returns
+ *   BSA_ERR_BAD_PLAN and nothing is launched.
  * - Tensors are dense and row-major (last index fastest), with the shapes
  *   given below.  q/k/v/kv/out must be 16-byte aligned.
  * - Nothing throws across this boundary.
@@ -36,7 +42,8 @@ typedef enum {
   BSA_ERR_MISALIGNED = -3,      /* pointer not 16-byte aligned */
   BSA_ERR_PLAN_MISMATCH = -4,   /* plan dims do not match the call */
   BSA_ERR_BUFFER_TOO_SMALL = -5,/* plan buffer smaller than bsa_plan_buffer_bytes */
-  BSA_ERR_HIP = -6              /* a HIP runtime call or launch failed */
+  BSA_ERR_HIP = -6,             /* a HIP runtime call or launch failed */
+  BSA_ERR_BAD_PLAN = -7         /* plan contents inconsistent (plan checks) */
 } bsa_status_t;
 
 typedef enum { BSA_BF16 = 0, BSA_F32 = 1 } bsa_dtype_t;
@@ -231,6 +238,38 @@ int bsa_plan_cols_sections(int32_t H, int32_t Hkv, int32_t Mb, int32_t Nb, size_
  */
 int bsa_plan_cols(const int32_t *layout, int32_t H, int32_t Hkv, int32_t Mb, int32_t Nb,
                   void *dev_buf, size_t dev_bytes, bsa_plan_cols_t *plan_out, void *stream);
+
+/*
+ * Consistency checks of plan contents.  The kernels take the plan's arrays
+ * as the CSR lists of the live tiles (next.gr tutorial, section 3.2) and
+ * index memory with them; a plan damaged after bsa_plan / bsa_plan_cols (or
+ * written by other code) could send them outside their buffers.  Checked:
+ *   plan:        row_ptr starts at 0, every row count in [0, Nb], row_ptr's
+ *                last entry equals nnz_total; each row's col_idx strictly
+ *                ascending in [0, Nb); row_order a permutation of [0, H*Mb);
+ *                pair_info[1] in {0, 1}; pair_ptr as row_ptr with total
+ *                pair_info[0]; every pair's entries equal the merged lists of
+ *                its two rows with their row tags; pair_order a permutation
+ *   column plan: the same for col_ptr / row_idx (values in [0, Mb)) and
+ *                col_order a permutation of [0, Hkv*Nb)
+ *   both:        equal nnz_total and every tile of the plan present in the
+ *                column plan (one is the other's transpose)
+ * Returns BSA_OK, BSA_ERR_BAD_PLAN with the first violation in
+ * bsa_last_error(), or the argument errors of the calls that take plans.
+ *
+ * bsa_plan_check: the device plans (either may be NULL, not both), copied to
+ *   the host after the work queued on `stream`; synchronises the stream.
+ * bsa_plan_check_host: host copies of the plan buffers (plan_bytes /
+ *   cols_bytes bytes, laid out as bsa_plan_sections /
+ *   bsa_plan_cols_sections give; either may be NULL, not both) for the
+ *   layout dimensions H, Hkv (0 means H), Mb, Nb.  Makes no HIP call.
+ * bsa_set_debug: turns debug mode on (nonzero) or off for the process;
+ *   returns the previous setting.
+ */
+int bsa_plan_check(const bsa_plan_t *plan, const bsa_plan_cols_t *plan_cols, void *stream);
+int bsa_plan_check_host(const void *plan_host, size_t plan_bytes, const void *cols_host,
+                        size_t cols_bytes, int32_t H, int32_t Hkv, int32_t Mb, int32_t Nb);
+int bsa_set_debug(int on);
 
 /* Bytes of the backward's workspace: two fp32 values per query row. */
 size_t bsa_backward_workspace_bytes(int32_t B, int32_t H, int32_t Sq);

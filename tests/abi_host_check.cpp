@@ -8,6 +8,8 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <vector>
+#include <algorithm>
 #include <limits>
 
 #include "bsa.h"
@@ -176,8 +178,50 @@ static void topk_checks() {
   CHECK(call(f, nullptr, 1 << 22, 8, 512, 8, 0.1f) == BSA_ERR_UNSUPPORTED);
 }
 
+// The host plan checks read every section of a copied plan through counts
+// and offsets taken from that same copy: over buffers of garbage they must
+// report an inconsistency and stay inside the buffer.
+static void plan_content_checks() {
+  uint32_t x = 12345u;
+  auto next = [&x]() {  // xorshift32
+    x ^= x << 13;
+    x ^= x >> 17;
+    x ^= x << 5;
+    return x;
+  };
+  const int dims[][4] = {{1, 1, 1, 1}, {2, 5, 7, 1}, {3, 8, 4, 3}, {4, 3, 9, 2}};
+  for (const auto &d : dims) {
+    const int H = d[0], Mb = d[1], Nb = d[2], Hkv = d[3];
+    std::vector<int32_t> rows(bsa_plan_buffer_bytes(H, Mb, Nb) / 4);
+    std::vector<int32_t> cols(bsa_plan_cols_buffer_bytes(H, Hkv, Mb, Nb) / 4);
+    for (int trial = 0; trial < 50; ++trial) {
+      for (auto &v : rows) v = (int32_t)(next() % 64) - 8;   // mostly small values
+      for (auto &v : cols) v = (trial % 2) ? (int32_t)next() : (int32_t)(next() % 16);
+      const int st = bsa_plan_check_host(rows.data(), rows.size() * 4, cols.data(),
+                                         cols.size() * 4, H, Hkv, Mb, Nb);
+      CHECK(st == BSA_ERR_BAD_PLAN || st == BSA_OK);
+      CHECK(bsa_plan_check_host(nullptr, 0, cols.data(), cols.size() * 4, H, Hkv, Mb, Nb) <= 0);
+    }
+    // The empty layout's plan: all counts zero, identity orders.
+    std::fill(rows.begin(), rows.end(), 0);
+    std::fill(cols.begin(), cols.end(), 0);
+    size_t ro[4], pr[4], co[4];
+    CHECK(bsa_plan_sections(H, Mb, Nb, ro) == BSA_OK);
+    CHECK(bsa_plan_pair_sections(H, Mb, Nb, pr) == BSA_OK);
+    CHECK(bsa_plan_cols_sections(H, Hkv, Mb, Nb, co) == BSA_OK);
+    for (int i = 0; i < H * Mb; ++i) rows[ro[1] / 4 + i] = i;
+    for (int i = 0; i < H * ((Mb + 1) / 2); ++i) rows[pr[1] / 4 + i] = i;
+    for (int i = 0; i < Hkv * Nb; ++i) cols[co[1] / 4 + i] = i;
+    CHECK(bsa_plan_check_host(rows.data(), rows.size() * 4, cols.data(), cols.size() * 4, H, Hkv,
+                              Mb, Nb) == BSA_OK);
+    CHECK(bsa_plan_check_host(rows.data(), rows.size() * 4 - 4, nullptr, 0, H, Hkv, Mb, Nb) ==
+          BSA_ERR_BUFFER_TOO_SMALL);
+  }
+  CHECK(bsa_plan_check(nullptr, nullptr, nullptr) == BSA_ERR_INVALID_ARG);
+}
+
 static void status_checks() {
-  for (int code = 1; code >= -7; --code) CHECK(bsa_status_string(code) != nullptr);
+  for (int code = 1; code >= -8; --code) CHECK(bsa_status_string(code) != nullptr);
   CHECK(bsa_last_error() != nullptr);
 }
 
@@ -186,6 +230,7 @@ int main() {
   forward_checks();
   backward_checks();
   topk_checks();
+  plan_content_checks();
   status_checks();
   if (g_failed) {
     std::fprintf(stderr, "%d checks failed\n", g_failed);
