@@ -223,9 +223,9 @@ CALIBRATION_BYTES = float(1 << 30)   # read and written by the calibration copy
 # the same kernel in its pair form (last flag Lb1E), which serves the bs-64
 # workload whose neighbouring rows share tiles; and the d-512 top-k instance.
 KERNEL_MATCH = {
-    "bsa_forward": lambda n: "bsa_fwd_dma_kernelILi128ELi128ELi1ELi2ELb0ELb0ELb0EE" in n,
-    "bsa_forward_options": lambda n: "bsa_fwd_dma_kernelILi128ELi128ELi1ELi2ELb1ELb0ELb0EE" in n,
-    "bsa_forward_lgs": lambda n: "bsa_fwd_dma_kernelILi128ELi128ELi1ELi2ELb0ELb0ELb1EE" in n,
+    "bsa_forward": lambda n: "bsa_fwd_dma_kernelILi128ELi128ELi1ELi2ELb0ELb0ELb0ELb0EE" in n,
+    "bsa_forward_options": lambda n: "bsa_fwd_dma_kernelILi128ELi128ELi1ELi2ELb1ELb0ELb0ELb0EE" in n,
+    "bsa_forward_lgs": lambda n: "bsa_fwd_dma_kernelILi128ELi128ELi1ELi2ELb0ELb0ELb1ELb0EE" in n,
     "topk_sparse_attn": lambda n: "topk_kernel" in n and ("<512>" in n or "ILi512EE" in n),
 }
 

@@ -463,8 +463,9 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
     }
   };
 
-  // Options on a fresh score tile of column ncol (MASK instances only): tanh
-  // logit cap, then the causal mask when the tile reaches past the diagonal
+  // Options on a fresh score tile of column ncol (MASK instances; CAUSAL
+  // instances the causal mask alone): tanh logit cap, then the causal mask
+  // when the tile reaches past the diagonal
   // (key row key0 + 32jt + 8(e/4) + 4h2 + e%4, query row 32rg + l32).
   auto apply_opts = [&](f32x16 (&s)[JT], int ncol, int buf) {
     if constexpr (!MASK) return;
@@ -482,7 +483,7 @@ bsa_fwd32_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
         for (int e = 0; e < 16; ++e)
           if (32 * jt + 8 * (e / 4) + (e % 4) > dq) s[jt][e] = -__builtin_inff();
     }
-    if ((int64_t)(ncol + 1) * BS > Sk) {  // keys past a cut last block
+    if (MASK && (int64_t)(ncol + 1) * BS > Sk) {  // keys past a cut last block
       const int kv = (int)(Sk - (int64_t)ncol * BS) - key0 - 4 * h2;
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt)
@@ -665,7 +666,8 @@ template <int D> struct VSwz {
 // sel / sel_want: with sel set, a launch whose *sel differs from sel_want
 // returns at once (the pair and row forms are launched together and the
 // plan's flag picks one).
-template <int BS, int D, int KSPLIT, int PIECES, bool MASK, bool SEG = false, bool GROUP = false>
+template <int BS, int D, int KSPLIT, int PIECES, bool MASK, bool SEG = false, bool GROUP = false,
+          bool CAUSAL = false>
 __global__ void __launch_bounds__(BS * 2 * KSPLIT)
 __attribute__((amdgpu_waves_per_eu(KSPLIT * PIECES)))
 bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
@@ -694,6 +696,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   // instructions of its wave (NSW = 1 when RPI * NW is a multiple of CPR).
   constexpr int NSW = (RPI * NW) % CPR == 0 ? 1 : CPR / ((RPI * NW) % CPR);
   static_assert((RPI * NW * NSW) % CPR == 0 && IPW % NSW == 0, "K swizzle pattern must repeat");
+  static_assert(!CAUSAL || (!MASK && !GROUP), "the causal-only instance has plain copies and rows");
   static_assert(!GROUP || (!MASK && KSPLIT == 1 && NRG == 4 && PIECES == 2),
                 "pairs: four row groups (two per block row), plain scores");
   constexpr int PPE = GROUP ? 1 : PIECES;  // pieces per plan entry
@@ -836,8 +839,9 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
       }
   };
 
-  // Options on a fresh score tile of column ncol (MASK instances only): tanh
-  // logit cap, then the causal mask when the tile reaches past the diagonal
+  // Options on a fresh score tile of column ncol (MASK instances; CAUSAL
+  // instances the causal mask alone): tanh logit cap, then the causal mask
+  // when the tile reaches past the diagonal
   // (key row key0 + 32jt + 8(e/4) + 4h2 + e%4, query row 32rg + l32).
   // Bit 16 jt + e set: score e of block jt belongs to a key of another
   // segment.  Read from the piece's ids in the phase that computed its
@@ -867,9 +871,9 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
         for (int jt = 0; jt < JT; ++jt) s[jt] = f32x16{} - __builtin_inff();
       }
     }
-    if constexpr (!MASK) return;
+    if constexpr (!MASK && !CAUSAL) return;
     const int kb0 = key0 + half * PB;   // this wave's first key inside the tile
-    if (opt.cap_k != 0.f) {
+    if (MASK && opt.cap_k != 0.f) {
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
@@ -883,7 +887,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
         for (int e = 0; e < 16; ++e)
           if (32 * jt + 8 * (e / 4) + (e % 4) > dq) s[jt][e] = -__builtin_inff();
     }
-    if ((int64_t)(ncol + 1) * BS > Sk) {  // keys past a cut last block
+    if (MASK && (int64_t)(ncol + 1) * BS > Sk) {  // keys past a cut last block
       const int kv = (int)(Sk - (int64_t)ncol * BS) - kb0 - 4 * h2;
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt)
@@ -1139,7 +1143,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
 // the kernels (item = (id % 8) * per + id / 8) covers them.
 int64_t grid_for(int64_t W) { return ((W + 7) / 8) * 8; }
 
-template <int BS, int D, typename T, bool MASK>
+template <int BS, int D, typename T, bool MASK, bool CAUSAL = false>
 hipError_t launch_one(const void *q, const void *k, const void *v, const PlanArrays &pa, int32_t B,
                       int32_t H, int32_t Mb, int32_t Nb, float scale, const FwdOptions &opt,
                       void *out, float *lse, hipStream_t stream) {
@@ -1154,7 +1158,7 @@ hipError_t launch_one(const void *q, const void *k, const void *v, const PlanArr
     constexpr int PC = BS == 128 ? kDmaPieces : kDmaPieces64;
     constexpr int KS = PC == 2 ? 1 : BS == 128 ? kDmaKeySplit : 2;
     const int32_t *sel = nullptr;
-    if constexpr (kPairForm && BS == 64 && !MASK && PC == 2 && KS == 1) {
+    if constexpr (kPairForm && BS == 64 && !MASK && !CAUSAL && PC == 2 && KS == 1) {
       // Pairs of block rows when the plan's flag says so (the unions of
       // neighbouring rows hold at most 3/4 of the tiles); both forms are
       // launched and the one the flag does not pick returns at once.
@@ -1169,7 +1173,12 @@ hipError_t launch_one(const void *q, const void *k, const void *v, const PlanArr
                            sel, 1);
       }
     }
-    if (opt.qseg == nullptr) {
+    if constexpr (CAUSAL) {
+      hipLaunchKernelGGL((bsa_fwd_dma_kernel<BS, D, KS, PC, false, false, false, true>),
+                         dim3((unsigned)grid), dim3(BS * 2 * KS), 0, stream, (const __bf16 *)q,
+                         (const __bf16 *)k, (const __bf16 *)v, row_ptr, col_idx, row_order, B, H,
+                         Mb, Nb, scale * kLog2e, (__bf16 *)out, lse, opt, nullptr, 0);
+    } else if (opt.qseg == nullptr) {
       hipLaunchKernelGGL((bsa_fwd_dma_kernel<BS, D, KS, PC, MASK>), dim3((unsigned)grid),
                          dim3(BS * 2 * KS), 0, stream, (const __bf16 *)q, (const __bf16 *)k,
                          (const __bf16 *)v, row_ptr, col_idx, row_order, B, H, Mb, Nb,
@@ -1197,9 +1206,16 @@ hipError_t dispatch(int32_t bs, int32_t d, const void *q, const void *k, const v
   // kernel instances, so the plain forward keeps the code it has without them.
   const bool mask = opt.cap_k != 0.f || opt.causal != 0 || opt.sq % bs != 0 || opt.sk % bs != 0 ||
                     opt.qseg != nullptr;
+  // The causal mask alone (whole blocks, no cap, no segment ids) has an
+  // instance of the bf16 copy-staged kernel with plain copies.
+  const bool causal_only = opt.causal != 0 && opt.cap_k == 0.f && opt.sq % bs == 0 &&
+                           opt.sk % bs == 0 && opt.qseg == nullptr &&
+                           std::is_same<T, __bf16>::value && bs >= 64;
 #define BSA_CASE(BS_, D_)                                                                     \
   if (bs == BS_ && d == D_)                                                                   \
-    return mask ? launch_one<BS_, D_, T, true>(q, k, v, pa, B, H, Mb, Nb, scale, opt, out, lse, \
+    return causal_only ? launch_one<BS_, D_, T, false, true>(q, k, v, pa, B, H, Mb, Nb, scale, \
+                                                             opt, out, lse, s)                \
+         : mask ? launch_one<BS_, D_, T, true>(q, k, v, pa, B, H, Mb, Nb, scale, opt, out, lse, \
                                                s)                                             \
                 : launch_one<BS_, D_, T, false>(q, k, v, pa, B, H, Mb, Nb, scale, opt, out,     \
                                                 lse, s);
