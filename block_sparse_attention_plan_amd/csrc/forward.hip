@@ -72,6 +72,23 @@ constexpr int kDmaPieces64 = BSA_DMA_PIECES64;  // the same for bs=64
 #endif
 // 1: bf16 bs = 64 forwards use the plan's pairs of block rows when its flag is set
 constexpr bool kPairForm = BSA_PAIR_FORM != 0;
+// Live tiles per block row up to which the segment-id instances filter the
+// row's list into LDS (12 bytes each: the column and one id per piece)
+constexpr int kSegList = 512;
+// List entries: the column in the low bits; bit 30 + h set when every key of
+// piece h of the tile carries one segment id (kept in LSEG)
+constexpr int kColBits = 0x3fffffff;
+
+__device__ __forceinline__ int wave_min(int x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x = min(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x = max(x, __shfl_xor(x, o));
+  return x;
+}
 constexpr int kReadAheadK = BSA_READ_AHEAD_K;  // K operand reads issued before the first QK MFMA
 constexpr int kReadAheadV = BSA_READ_AHEAD_V;  // V transpose reads issued before the first PV MFMA
 
@@ -709,11 +726,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   __shared__ __attribute__((aligned(1024))) __bf16 K1[TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 V0[TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 V1[TILE];
-  // segment ids of the keys of the pieces in K0 and K1 (SEG instances:
-  // MASK instances for calls with segment ids)
   static_assert(MASK || !SEG, "segment ids come with the other masks");
-  __shared__ __attribute__((aligned(16))) int32_t KG0[SEG ? PB : 4];
-  __shared__ __attribute__((aligned(16))) int32_t KG1[SEG ? PB : 4];
 
   const int64_t W = (int64_t)B * H * Mb;
   const int64_t per = (W + 7) / 8;
@@ -739,6 +752,88 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
 
   const int64_t bh = (int64_t)b * H + h;
   const int64_t Sq = opt.sq, Sk = opt.sk;
+
+  // SEG instances drop, before the pipeline starts, the live tiles whose key
+  // segment ids cannot meet those of the block row's queries: when the
+  // [min, max] ranges of the two sets of ids are disjoint, every score of
+  // the tile is masked and its weights are exactly zero, so neither its
+  // copies nor its products are needed.  (Ranges only ever keep a tile too
+  // many; the element masks below still decide every score.)  The kept
+  // columns go to LDS, each with a flag per piece whose keys all carry one
+  // id (that id in LSEG): the element mask of such a piece is one compare
+  // per query.  Each wave computes the same list on its own, so no barrier
+  // orders the writes.  A row with more than kSegList live tiles walks the
+  // plan's list unfiltered.
+  static_assert(!SEG || PIECES == 2, "the list holds two pieces per tile");
+  __shared__ int32_t LST[SEG ? kSegList : 1];
+  __shared__ int32_t LSEG[SEG ? 2 * kSegList : 1];
+  int n_live = end - beg;
+  bool use_list = false;
+  if constexpr (SEG) {
+    if (n_live <= kSegList) {
+      use_list = true;
+      int qlo = INT32_MAX, qhi = INT32_MIN;
+      for (int i = lane; i < KBLK; i += 64) {
+        const int64_t qi = (int64_t)m * KBLK + i;
+        if (qi < Sq) {
+          const int sg = opt.qseg[(int64_t)b * Sq + qi];
+          qlo = min(qlo, sg);
+          qhi = max(qhi, sg);
+        }
+      }
+      qlo = wave_min(qlo);
+      qhi = wave_max(qhi);
+      // 16 lanes per tile, four tiles per pass, four passes per round: lane
+      // (g, sub) reads ids sub*IPL .. of tile 4p + g, so the first eight
+      // lanes of a group cover piece 0 and the last eight piece 1.
+      constexpr int IPL = KBLK / 16;
+      const int g = lane / 16, sub = lane % 16;
+      int kept = 0;
+      for (int t0 = 0; t0 < n_live; t0 += 16) {
+        int lo[4], hi[4], colv[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int t = t0 + 4 * p + g;
+          lo[p] = INT32_MAX;
+          hi[p] = INT32_MIN;
+          colv[p] = t < n_live ? col_idx[beg + t] : 0;
+          const int64_t kb = (int64_t)colv[p] * KBLK + sub * IPL;
+          const int32_t *kg = opt.kseg + (int64_t)b * Sk + kb;
+#pragma unroll
+          for (int i = 0; i < IPL; ++i) {
+            if (t < n_live && kb + i < Sk) {
+              const int sg = kg[i];
+              lo[p] = min(lo[p], sg);
+              hi[p] = max(hi[p], sg);
+            }
+          }
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+#pragma unroll
+          for (int o = 1; o < 8; o <<= 1) {
+            lo[p] = min(lo[p], __shfl_xor(lo[p], o));
+            hi[p] = max(hi[p], __shfl_xor(hi[p], o));
+          }
+          // lane sub = 0 holds piece 0's range, and receives piece 1's
+          const int lo1 = __shfl_xor(lo[p], 8), hi1 = __shfl_xor(hi[p], 8);
+          const int t = t0 + 4 * p + g;
+          const bool keep = sub == 0 && t < n_live && min(lo[p], lo1) <= qhi && max(hi[p], hi1) >= qlo;
+          const uint64_t mask = __ballot(keep);
+          if (keep) {
+            // a piece with no key before Sk counts as one id: its scores are masked anyway
+            const int flags = (lo[p] >= hi[p] ? 1 << 30 : 0) | (lo1 >= hi1 ? 1 << 31 : 0);
+            const int pos = kept + __popcll(mask & ((1ull << lane) - 1ull));
+            LST[pos] = colv[p] | flags;
+            LSEG[2 * pos] = lo[p];
+            LSEG[2 * pos + 1] = lo1;
+          }
+          kept += __popcll(mask);
+        }
+      }
+      n_live = kept;
+    }
+  }
   const __bf16 *qh = q + bh * Sq * D;
   const int64_t bkv = (int64_t)b * (H / opt.kv_group) + h / opt.kv_group;  // K/V head
   const __bf16 *kh = k + bkv * Sk * D;
@@ -750,7 +845,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   const bool q_ok = !(MASK || GROUP) || i_row < Sq;
   const int qsg = (SEG && q_ok) ? opt.qseg[(int64_t)b * Sq + i_row] : 0;
 
-  if (beg == end) {
+  if (n_live == 0) {
     if (ks == 0 && q_ok) {
       for (int dt = 0; dt < DT; ++dt)
         for (int a = 0; a < 4; ++a) Io<__bf16>::store_zero4(oh + i_row * D + 32 * dt + 8 * a + 4 * h2);
@@ -799,18 +894,8 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     if constexpr (GROUP) n &= 0xffffff;
     return base + (int64_t)n * KBLK * D + (int64_t)half * PB * D;
   };
-  // SEG instances also copy the piece's key segment ids, 16 per wave with
-  // one 4-byte-per-lane copy: every wave issues the same number of copies.
-  constexpr int IDW = PB / NW;  // ids per wave
-  static_assert(!SEG || (IDW >= 1 && IDW <= 64 && PB % NW == 0), "id copies split over waves");
-  auto load_k = [&](int n, int half, __bf16 *dst, int32_t *ids) {
+  auto load_k = [&](int n, int half, __bf16 *dst) {
     dma(piece_src(kh, n, half), [&](int j) { return k_src[j % NSW]; }, dst, tile_bytes(n, half));
-    if constexpr (SEG) {
-      const int64_t k0 = (int64_t)n * BS + half * PB + wid * IDW;  // first key of this wave's ids
-      const uint32_t nb = (uint32_t)(max((int64_t)0, min((int64_t)IDW, Sk - k0)) * 4);
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(opt.kseg + (int64_t)b * Sk + k0, nb);
-      if (lane < IDW) copy4_to_lds(rs, ids + wid * IDW, (uint32_t)(lane * 4), 0u);
-    }
   };
   auto load_v = [&](int n, int half, __bf16 *dst) {
     dma(piece_src(vh, n, half), [&](int) { return v_src; }, dst, tile_bytes(n, half));
@@ -844,22 +929,24 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   // when the tile reaches past the diagonal
   // (key row key0 + 32jt + 8(e/4) + 4h2 + e%4, query row 32rg + l32).
   // Bit 16 jt + e set: score e of block jt belongs to a key of another
-  // segment.  Read from the piece's ids in the phase that computed its
-  // scores, before the next barrier lets its buffer be refilled.
-  constexpr uint32_t kSegAllOther = JT * 16 >= 32 ? 0xffffffffu : (1u << (JT * 16)) - 1u;
-  auto seg_bits = [&](const int32_t *ids) -> uint32_t {
+  // segment.  ent is the list entry of piece u's tile: a piece whose keys
+  // carry one id needs one compare; the others (segment boundaries, and
+  // every piece of an unfiltered row) read this lane's key ids from memory.
+  // u is an existing piece of the row, sid its id if it has only one.
+  auto seg_bits = [&](int u, int ent, int sid) -> uint32_t {
     uint32_t bits = 0;
     if constexpr (SEG) {
-      {
-        const int32_t *kst = ids + key0 + 4 * h2;
-#pragma unroll
-        for (int jt = 0; jt < JT; ++jt)
-#pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4) {
-            const i32x4 v4 = *reinterpret_cast<const i32x4 *>(kst + 32 * jt + 8 * a4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) bits |= (uint32_t)(v4[i] != qsg) << (16 * jt + 4 * a4 + i);
-          }
+      const int hf = u % PPE;
+      if ((ent >> (30 + hf)) & 1) {
+        bits = sid != qsg ? 0xffffffffu : 0u;
+      } else {
+        const int64_t kp = (int64_t)(ent & kColBits) * BS + hf * PB + key0 + 4 * h2;
+        const int32_t *kg = opt.kseg + (int64_t)b * Sk;
+#pragma unroll 1
+        for (int x = 0; x < 16 * JT; ++x) {
+          const int64_t key = kp + 32 * (x / 16) + 8 * ((x % 16) / 4) + (x % 4);
+          bits |= (uint32_t)(key >= Sk || kg[key] != qsg) << x;
+        }
       }
     }
     return bits;
@@ -974,7 +1061,7 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   //   M_t: V_t has landed; copy K_{t+3} into the K buffer QK(t+1) freed;
   //        then PV of piece t beside the row max of piece t+1.
   // Each copy thus has one and a half steps to land.  Every phase issues
-  // IPW copies (SEG instances: IPW + 1 in M_t, the key ids) -- indices past
+  // IPW copies -- indices past
   // the row's end are clamped, so the last copies are redundant but
   // harmless -- and S_t also a column fetch, so the copy a phase needs is
   // followed by kVmInFlight copies and at most two fetches: waiting until at
@@ -987,12 +1074,37 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   // load in flight would force every LDS wait in between to drain
   // completely.
   // Piece u = 0 .. n-1 is piece u % PIECES of live tile u / PIECES.
-  const int n = (end - beg) * PPE;
+  const int n = n_live * PPE;
   const int32_t *cols = col_idx + beg;
-  auto col_at = [&](int u) -> int { return cols[min(u, n - 1) / PPE]; };
+  // SEG: the raw list entry (column and piece flags); col_at masks the flags
+  auto entry_at = [&](int u) -> int {
+    const int e = min(u, n - 1) / PPE;
+    if constexpr (SEG) {
+      // both loads are issued and the value selected: a selected pointer
+      // would become a flat load, which the copy waits cannot count
+      const int from_list = LST[min(e, kSegList - 1)];
+      const int from_plan = cols[e];
+      return use_list ? from_list : from_plan;
+    }
+    return cols[e];
+  };
+  auto col_at = [&](int u) -> int { return SEG ? entry_at(u) & kColBits : entry_at(u); };
   auto half_at = [&](int u) -> int { return min(u, n - 1) % PPE; };
-  auto fetch_cols = [&](int kpos, int vpos) -> int { return col_at(lane == 0 ? kpos : vpos); };
-  constexpr int kVmInFlight = 2 * IPW + (SEG ? 1 : 0);
+  // SEG: lane 2 fetches the one segment id of piece vpos (meaningful when
+  // its entry's flag says so)
+  auto seg_id_at = [&](int u) -> int {
+    const int uc = min(u, n - 1);
+    return LSEG[min(2 * (uc / PPE) + uc % PPE, 2 * kSegList - 1)];
+  };
+  auto fetch_cols = [&](int kpos, int vpos) -> int {
+    const int e = entry_at(lane == 0 ? kpos : vpos);
+    if constexpr (SEG) {
+      const int sid = seg_id_at(vpos);
+      return lane == 2 ? sid : e;
+    }
+    return e;
+  };
+  constexpr int kVmInFlight = 2 * IPW;
   constexpr int kVmWait = (kVmInFlight & 15) | (7 << 4) | (15 << 8) | ((kVmInFlight >> 4) << 14);
   static_assert(kVmInFlight < 64, "vmcnt holds 6 bits");
   // Block barrier without the release fence of __syncthreads(), which would
@@ -1004,90 +1116,68 @@ bsa_fwd_dma_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
   float mx_a = 0.f, mx_b = 0.f;
   int cv0 = fetch_cols(3, 1);  // for S_0 / M_0
   int cv1 = fetch_cols(4, 2);  // for S_1 / M_1
-  load_k(col_at(0), half_at(0), K0, KG0);
+  load_k(col_at(0), half_at(0), K0);
   load_v(col_at(0), half_at(0), V0);
-  load_k(col_at(1), half_at(1), K1, KG1);
+  load_k(col_at(1), half_at(1), K1);
   const int k2 = col_at(2);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   qk(K0, s_a);
-  apply_opts(s_a, col_at(0), half_at(0), seg_bits(KG0));
+  apply_opts(s_a, col_at(0), half_at(0), SEG ? seg_bits(0, entry_at(0), seg_id_at(0)) : 0u);
   mx_a = tile_max(s_a);
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();  // M_{-1}: K0 free
-  load_k(k2, half_at(2), K0, KG0);
+  load_k(k2, half_at(2), K0);
 
-  // One step; Kq is K[(t+1)%2] (KGq its key ids), Vn is V[(t+1)%2], Vc is
-  // V[t%2].  MORE: piece t+1 exists (every step but the row's last).
-  auto step = [&](auto more_tag, int t, __bf16 *Kq, int32_t *KGq, __bf16 *Vn, const __bf16 *Vc,
+  // One step; Kq is K[(t+1)%2], Vn is V[(t+1)%2], Vc is V[t%2].  MORE:
+  // piece t+1 exists (every step but the row's last).
+  auto step = [&](auto more_tag, int t, __bf16 *Kq, __bf16 *Vn, const __bf16 *Vc,
                   f32x16 (&s_cur)[JT], f32x16 (&s_nxt)[JT], float &mx_cur, float &mx_nxt,
-                  bool &sk_cur, bool &sk_nxt, int &cv) {
+                  int &cv) {
     constexpr bool MORE = decltype(more_tag)::value;
     __builtin_amdgcn_s_waitcnt(kVmWait);  // K_{t+1} landed (this wave's part)
     __builtin_amdgcn_sched_barrier(0);
     block_barrier();
-    const int kcol = __builtin_amdgcn_readlane(cv, 0);  // column of piece t+3's tile
-    const int vcol = __builtin_amdgcn_readlane(cv, 1);  // column of piece t+1's tile
+    const int kent = __builtin_amdgcn_readlane(cv, 0);  // column of piece t+3's tile
+    const int vent = __builtin_amdgcn_readlane(cv, 1);  // column of piece t+1's tile
+    const int kcol = SEG ? kent & kColBits : kent;
+    const int vcol = SEG ? vent & kColBits : vent;
+    const int vsid = SEG ? __builtin_amdgcn_readlane(cv, 2) : 0;  // its one segment id, if any
     cv = fetch_cols(t + 5, t + 3);
     load_v(vcol, half_at(t + 1), Vn);
     rescale(mx_cur);
     bf16x8 pf[2 * JT];
-    uint32_t segbits = 0u;
-    if constexpr (SEG) {
-      // With segment ids, a piece none of whose keys shares a segment with
-      // any of this wave's queries has only -inf scores: its weights are
-      // exactly zero, so its score and output products are skipped (a wave
-      // vote; the copies still run, as every wave shares them).
-      if constexpr (MORE) {
-        segbits = seg_bits(KGq);
-        sk_nxt = !__any(segbits != kSegAllOther);
-        if (!sk_nxt) qk(Kq, s_nxt);
-        if (!sk_cur) exp_pack(s_cur, pf);
-      } else {
-        if (!sk_cur) exp_pack(s_cur, pf);
-      }
-    } else {
-      if constexpr (MORE) qk(Kq, s_nxt);
-      exp_pack(s_cur, pf);
-      if constexpr (MORE) sched_interleave<JT * QC, JT * QC, kReadAheadK, 3 * 16 * JT / (JT * QC)>();
-    }
+    if constexpr (MORE) qk(Kq, s_nxt);
+    exp_pack(s_cur, pf);
+    if constexpr (MORE) sched_interleave<JT * QC, JT * QC, kReadAheadK, 3 * 16 * JT / (JT * QC)>();
     __builtin_amdgcn_s_waitcnt(kVmWait);  // V_t landed
     __builtin_amdgcn_sched_barrier(0);
     block_barrier();
-    load_k(kcol, half_at(t + 3), Kq, KGq);
-    if constexpr (SEG) {
-      const bool opts_nxt = MORE && !sk_nxt;
-      if (!sk_cur) pv(pf, Vc);
-      if (opts_nxt) {
-        apply_opts(s_nxt, vcol, half_at(t + 1), segbits);
-        mx_nxt = tile_max(s_nxt);
-      }
-      if (MORE && sk_nxt) mx_nxt = -__builtin_inff();   // no rescale for a skipped piece
+    load_k(kcol, half_at(t + 3), Kq);
+    uint32_t segbits = 0u;
+    if constexpr (SEG && MORE) segbits = seg_bits(t + 1, vent, vsid);
+    pv(pf, Vc);
+    if constexpr (MORE) {
+      apply_opts(s_nxt, vcol, half_at(t + 1), segbits);
+      mx_nxt = tile_max(s_nxt);
+      sched_interleave<JT * 2 * DT, 4 * JT * DT, kReadAheadV, 1>();
     } else {
-      pv(pf, Vc);
-      if constexpr (MORE) {
-        apply_opts(s_nxt, vcol, half_at(t + 1), segbits);
-        mx_nxt = tile_max(s_nxt);
-        sched_interleave<JT * 2 * DT, 4 * JT * DT, kReadAheadV, 1>();
-      } else {
-        sched_interleave<JT * 2 * DT, 4 * JT * DT, kReadAheadV, 0>();
-      }
+      sched_interleave<JT * 2 * DT, 4 * JT * DT, kReadAheadV, 0>();
     }
     __builtin_amdgcn_sched_barrier(0);
   };
   using More = std::true_type;
   using Last = std::false_type;
   int t = 0;
-  bool sk_a = false, sk_b = false;   // piece skipped (segment ids only); piece 0 never is
   for (; t + 2 < n; t += 2) {
-    step(More{}, t, K1, KG1, V1, V0, s_a, s_b, mx_a, mx_b, sk_a, sk_b, cv0);
-    step(More{}, t + 1, K0, KG0, V0, V1, s_b, s_a, mx_b, mx_a, sk_b, sk_a, cv1);
+    step(More{}, t, K1, V1, V0, s_a, s_b, mx_a, mx_b, cv0);
+    step(More{}, t + 1, K0, V0, V1, s_b, s_a, mx_b, mx_a, cv1);
   }
   if (t + 1 < n) {
-    step(More{}, t, K1, KG1, V1, V0, s_a, s_b, mx_a, mx_b, sk_a, sk_b, cv0);
-    step(Last{}, t + 1, K0, KG0, V0, V1, s_b, s_a, mx_b, mx_a, sk_b, sk_a, cv1);
+    step(More{}, t, K1, V1, V0, s_a, s_b, mx_a, mx_b, cv0);
+    step(Last{}, t + 1, K0, V0, V1, s_b, s_a, mx_b, mx_a, cv1);
   } else {
-    step(Last{}, t, K1, KG1, V1, V0, s_a, s_b, mx_a, mx_b, sk_a, sk_b, cv0);
+    step(Last{}, t, K1, V1, V0, s_a, s_b, mx_a, mx_b, cv0);
   }
   __builtin_amdgcn_s_waitcnt(0);  // no copy may still be landing in the buffers reused below
 
@@ -1183,7 +1273,7 @@ hipError_t launch_one(const void *q, const void *k, const void *v, const PlanArr
                          dim3(BS * 2 * KS), 0, stream, (const __bf16 *)q, (const __bf16 *)k,
                          (const __bf16 *)v, row_ptr, col_idx, row_order, B, H, Mb, Nb,
                          scale * kLog2e, (__bf16 *)out, lse, opt, sel, 0);
-    } else {  // segment ids: the instance that also copies the key ids
+    } else {  // segment ids: the instance that filters each row's tiles by segment
       hipLaunchKernelGGL((bsa_fwd_dma_kernel<BS, D, KS, PC, true, true>), dim3((unsigned)grid),
                          dim3(BS * 2 * KS), 0, stream, (const __bf16 *)q, (const __bf16 *)k,
                          (const __bf16 *)v, row_ptr, col_idx, row_order, B, H, Mb, Nb,

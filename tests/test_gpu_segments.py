@@ -90,8 +90,8 @@ def test_backward_segments(gpu, bs, d, S, causal):
                                           (64, 64, (128, 64, 64, 256, 512))])
 def test_forward_segments_equal_reduced_layout(gpu, bs, d, lengths):
     """Segments that start and end on block boundaries mask exactly the tiles
-    between different segments, so the forward with segment ids (which skips
-    the pieces whose keys all lie in other segments) equals the forward
+    between different segments, so the forward with segment ids (which drops
+    the tiles whose keys all lie in other segments) equals the forward
     without them on the layout with those tiles removed.  At bs = 64 the
     reduced layout's neighbouring rows share tiles, so its forward runs in the
     paired form (64-key pieces instead of 32), whose bf16 weights and rescale
@@ -121,3 +121,84 @@ def test_forward_segments_equal_reduced_layout(gpu, bs, d, lengths):
     assert torch.allclose(lse, lse_r, atol=1e-5, rtol=0)
     ref, _ = O.attention_live_tiles(to64(x.q), to64(x.k), to64(x.v), reduced, bs, x.scale)
     compare(to64(out), ref, f"segments reduced bs={bs} d={d}")
+
+
+def _segment_case(gpu, lay, bs, d, Sq, Sk, qs, ks, seed, causal=False, sink=False, what=""):
+    """Forward with segment ids against the oracle, outputs and lse."""
+    B, H = qs.shape[0], lay.shape[0]
+    x = W.make_bsa("segments_filter", B=B, H=H, S=Sq, Sk=Sk, bs=bs, d=d, dtype="bf16",
+                   layout="given", layout_array=lay, seed=seed,
+                   sink_mean=1.0 if sink else None)
+    plan, _ = check_plan(gpu, lay)
+    kw = dict(bs=bs, causal=causal, q_segment_ids=qs.to(gpu), kv_segment_ids=ks.to(gpu))
+    if sink:
+        kw["attn_sink"] = x.sink.to(gpu)
+    out, lse = bsa.bsa_forward(x.q.to(gpu), x.k.to(gpu), x.v.to(gpu), plan, x.scale, **kw)
+    torch.cuda.synchronize()
+    okw = dict(causal=causal, q_segment_ids=qs.numpy(), kv_segment_ids=ks.numpy())
+    if sink:
+        okw["sink"] = x.sink.numpy().astype(np.float64)
+    ref, ref_lse = O.attention_live_tiles(to64(x.q), to64(x.k), to64(x.v), lay, bs, x.scale, **okw)
+    compare(to64(out), ref, what)
+    compare_lse(lse.cpu().numpy(), ref_lse, what)
+    return out, lse, ref, ref_lse
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("bs,d,S", [(128, 128, 512), (128, 64, 500), (64, 128, 448), (64, 64, 390)])
+def test_forward_segments_unordered_ids(gpu, bs, d, S, causal):
+    """Ids drawn per token from {0, 1, 2} (not contiguous runs): the id ranges
+    of every query block and key tile overlap, so no tile is dropped and every
+    piece mixes ids -- each score's mask comes from the key ids read one by
+    one.  S not a multiple of bs puts keys past the end into mixed pieces."""
+    H, B = 2, 2
+    nb = -(-S // bs)
+    rng = np.random.default_rng(S + bs + d)
+    lay = (rng.random((H, nb, nb)) < 0.6).astype(np.int32)
+    lay[:, np.arange(nb), np.arange(nb)] = 1
+    ids = torch.from_numpy(rng.integers(0, 3, size=(B, S)).astype(np.int32))
+    say(f"[segments] unordered ids bs={bs} d={d} S={S} causal={causal}")
+    _segment_case(gpu, lay, bs, d, S, S, ids, ids, seed=S + 1, causal=causal,
+                  what=f"unordered ids bs={bs} d={d}")
+
+
+@pytest.mark.parametrize("sink", [False, True])
+@pytest.mark.parametrize("bs,d", [(128, 128), (64, 64)])
+def test_forward_segments_rows_without_same_segment_tiles(gpu, bs, d, sink):
+    """Block-aligned segments of two blocks each; in every head, block rows
+    3 and 6 list only tiles of other segments.  Their tiles are all dropped
+    before the pipeline: the rows come out as zeros with lse -inf (the sink
+    logit with a sink), as the oracle's fully masked rows do; the other rows
+    keep their same-segment tiles and mixed layouts."""
+    H, B, nb = 2, 2, 8
+    S = nb * bs
+    rng = np.random.default_rng(bs + d + sink)
+    lay = (rng.random((H, nb, nb)) < 0.6).astype(np.int32)
+    lay[:, np.arange(nb), np.arange(nb)] = 1
+    blk_seg = np.arange(nb) // 2
+    for m in (3, 6):
+        other = blk_seg != blk_seg[m]
+        lay[:, m, :] = 0
+        lay[:, m, other] = 1
+    seg = torch.from_numpy(np.repeat(np.repeat(blk_seg, bs)[None], B, 0).astype(np.int32))
+    say(f"[segments] rows without same-segment tiles bs={bs} d={d} sink={sink}")
+    out, lse, ref, ref_lse = _segment_case(gpu, lay, bs, d, S, S, seg, seg, seed=S + 2,
+                                           sink=sink, what=f"dropped rows bs={bs} d={d}")
+    rows = np.concatenate([np.arange(3 * bs, 4 * bs), np.arange(6 * bs, 7 * bs)])
+    assert torch.count_nonzero(out[:, :, rows]).item() == 0
+    if not sink:
+        assert np.isneginf(lse.cpu().numpy()[:, :, rows]).all()
+
+
+@pytest.mark.parametrize("bs,d", [(64, 64), (128, 32)])
+def test_forward_segments_long_row_unfiltered(gpu, bs, d):
+    """One block row with more live tiles (520) than the filter's list holds:
+    the row walks the plan's list unfiltered, and every piece's mask comes
+    from its key ids read one by one."""
+    H, B, nb = 1, 1, 520
+    Sq, Sk = bs, nb * bs - 5
+    lay = np.ones((H, 1, nb), np.int32)
+    qs = torch.from_numpy(np.full((B, Sq), 3, np.int32))
+    ks = W.packed_segment_ids(B, Sk, 50, 4000, seed=nb)
+    say(f"[segments] long row, {nb} tiles, bs={bs} d={d}")
+    _segment_case(gpu, lay, bs, d, Sq, Sk, qs, ks, seed=nb + bs, what=f"long row bs={bs} d={d}")
