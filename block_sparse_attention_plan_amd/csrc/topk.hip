@@ -48,8 +48,10 @@ constexpr float kMaxFloor = -1e30f;
 constexpr float kLazy = 8.0f;  // tolerated staleness of the running max (log2 units)
 // KV row reads issued before the first score MFMA
 template <int D> constexpr int kReadAheadS = D == 512 ? 6 : 3;
+// Largest topk whose valid indices are compacted into LDS (4 bytes each)
+constexpr int kWindow = 2048;
 
-template <int D>
+template <int D, bool COMPACT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
             const int32_t *__restrict__ idx, const float *__restrict__ sink, int32_t M,
@@ -69,6 +71,11 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
   __shared__ __attribute__((aligned(16))) __bf16 C1[T * STR];
   __shared__ __attribute__((aligned(16))) __bf16 Ps[64 * PSTR];  // P of every head, [head][slot]
   __shared__ float As[64];  // per-head rescale factor of the chunk; 1/l at the end
+  // COMPACT instances (topk <= kWindow): the valid indices of the slots, in
+  // slot order; chunks take T of them at a time, so slots without a valid
+  // index cost no products.  (The other instances read the slots in place.)
+  __shared__ __attribute__((aligned(16))) int32_t LST[COMPACT ? kWindow : 1];
+  __shared__ int32_t WCNT[4];
 
   const int64_t pos = blockIdx.x;  // b * M + m
   const int64_t b = pos / M;
@@ -98,11 +105,44 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
       qf[c] = bf16x8{};
   }
 
-  auto chunk_idx = [&](int ch) -> int {
-    const int slot = ch * T + lane;
-    return (lane < T && slot < topk) ? ib[slot] : -1;
-  };
   auto valid = [&](int my) -> int { return (my >= 0 && my < N) ? my : -1; };
+  // COMPACT: slots [w0, w1) (at most kWindow): each wave takes a quarter of
+  // them, 64 per load; the waves' counts give each its offset in LST.
+  // Returns the number of valid indices.
+  auto compact_window = [&](int w0, int w1) -> int {
+    constexpr int PERW = kWindow / 4 / 64;
+    int raw[PERW];
+#pragma unroll
+    for (int j = 0; j < PERW; ++j) {
+      const int slot = w0 + (wid * PERW + j) * 64 + lane;
+      raw[j] = slot < w1 ? ib[slot] : -1;
+    }
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < PERW; ++j) {
+      raw[j] = (raw[j] >= 0 && raw[j] < N) ? raw[j] : -1;
+      cnt += __popcll(__ballot(raw[j] >= 0));
+    }
+    if (lane == 0) WCNT[wid] = cnt;
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int c = WCNT[w];
+      off += w < wid ? c : 0;
+      tot += c;
+    }
+#pragma unroll
+    for (int j = 0; j < PERW; ++j) {
+      const uint64_t vm = __ballot(raw[j] >= 0);
+      const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(vm >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)vm, 0u));
+      if (raw[j] >= 0) LST[off + below] = raw[j];
+      off += __popcll(vm);
+    }
+    __syncthreads();
+    return tot;
+  };
   const __amdgpu_buffer_rsrc_t kv_rs = make_rsrc(kvb, (uint32_t)((int64_t)N * D * 2));
   // The row offset rides in the per-lane offset, which is what the buffer
   // range check covers: an invalid slot (-1) wraps it past the end of the
@@ -209,6 +249,16 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
     __builtin_amdgcn_s_waitcnt(0xC07F);
     asm volatile("s_barrier" ::: "memory");
   };
+  int nv = 0;  // COMPACT: valid indices in LST
+  // Raw index of this lane's slot of chunk ch (lanes T.. and slots past the
+  // end: -1); it is validated only in the step that uses it, since testing a
+  // fresh load would make the compiler wait for it and for every row copy
+  // issued before it.
+  auto chunk_idx = [&](int ch) -> int {
+    const int i = ch * T + lane;
+    if constexpr (COMPACT) return (lane < T && i < nv) ? LST[i] : -1;
+    return (lane < T && i < topk) ? ib[i] : -1;
+  };
   auto step = [&](int ch, int nchunks, int &my_cur, int &raw_next, const __bf16 *cur, __bf16 *nxt) {
     const uint64_t vmask = __ballot(my_cur >= 0);
     int my_following = -1;
@@ -225,7 +275,8 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
     my_cur = my_following;
   };
 
-  const int nchunks = (topk + T - 1) / T;
+  if constexpr (COMPACT) nv = compact_window(0, topk);
+  const int nchunks = COMPACT ? max(1, (nv + T - 1) / T) : (topk + T - 1) / T;
   int my_cur = valid(chunk_idx(0));
   gather(my_cur, C0);
   int my_next = nchunks > 1 ? chunk_idx(1) : -1;
@@ -273,15 +324,19 @@ hipError_t launch_topk(const void *q, const void *kv, const int32_t *idx, const 
   const int64_t grid = (int64_t)B * M;
   const int64_t groups = ((int64_t)H + 63) / 64;  // 64 heads per workgroup
   if (grid > 0x7fffffff || groups > 65535) return hipErrorInvalidValue;
-#define BSA_TOPK_LAUNCH(D_)                                                                    \
-  hipLaunchKernelGGL(topk_kernel<D_>, dim3((unsigned)grid, (unsigned)groups), dim3(256), 0,    \
-                     stream,                                                                   \
-                     (const __bf16 *)q, (const __bf16 *)kv, idx, sink, M, N, H, topk,           \
-                     scale * kLog2e, (__bf16 *)out)
-  if (d == 512) BSA_TOPK_LAUNCH(512);
-  else if (d == 256) BSA_TOPK_LAUNCH(256);
-  else BSA_TOPK_LAUNCH(128);
-#undef BSA_TOPK_LAUNCH
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid, (unsigned)groups), dim3(256), 0, stream,
+                       (const __bf16 *)q, (const __bf16 *)kv, idx, sink, M, N, H, topk,
+                       scale * kLog2e, (__bf16 *)out);
+  };
+  const bool compact = topk <= kWindow;
+  if (d == 512) {
+    if (compact) launch(topk_kernel<512, true>); else launch(topk_kernel<512, false>);
+  } else if (d == 256) {
+    if (compact) launch(topk_kernel<256, true>); else launch(topk_kernel<256, false>);
+  } else {
+    if (compact) launch(topk_kernel<128, true>); else launch(topk_kernel<128, false>);
+  }
   return hipGetLastError();
 }
 

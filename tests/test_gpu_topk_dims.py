@@ -60,3 +60,28 @@ def test_topk_many_heads(gpu, d, H, with_sink):
                            t.sink.numpy() if with_sink else None, t.scale)
     compare(to64(out), ref, f"topk d={d} H={H}")
     assert torch.all(out[0, 3] == 0)
+
+
+@pytest.mark.parametrize("d", [128, 256, 512])
+@pytest.mark.parametrize("topk", [2048, 2049, 3000])
+def test_topk_long_lists(gpu, d, topk):
+    """Lists of up to 2048 slots have their valid indices compacted in LDS
+    before chunks are formed; longer lists are read in place.  Both forms
+    against the oracle, with -1 and out-of-range slots, a position whose only
+    valid slots are its last three, and a position with none."""
+    N = 4096
+    t = W.make_topk("topk_long", B=1, M=4, H=20, d=d, N=N, topk=topk, seed=topk + d, drop=0.2,
+                    with_sink=True)
+    idx = t.idx.clone()
+    idx[0, 1, :] = -1
+    idx[0, 1, -3:] = torch.tensor([5, 17, N - 1], dtype=idx.dtype)
+    idx[0, 2, :] = -1
+    idx[0, 3, ::7] = N + 11
+    say(f"[topk] long list d={d} topk={topk}")
+    out = bsa.topk_sparse_attn(t.q.to(gpu), t.kv.to(gpu), idx.to(gpu), t.sink.to(gpu), t.scale)
+    torch.cuda.synchronize()
+    ref_idx = idx.numpy().copy()
+    ref_idx[(ref_idx < 0) | (ref_idx >= N)] = -1
+    ref = O.topk_attention(to64(t.q), to64(t.kv), ref_idx, t.sink.numpy(), t.scale)
+    compare(to64(out), ref, f"topk long d={d} topk={topk}")
+    assert torch.all(out[0, 2] == 0)
