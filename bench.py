@@ -226,7 +226,8 @@ KERNEL_MATCH = {
     "bsa_forward": lambda n: "bsa_fwd_dma_kernelILi128ELi128ELi1ELi2ELb0ELb0ELb0ELb0EE" in n,
     "bsa_forward_options": lambda n: "bsa_fwd_dma_kernelILi128ELi128ELi1ELi2ELb1ELb0ELb0ELb0EE" in n,
     "bsa_forward_lgs": lambda n: "bsa_fwd_dma_kernelILi128ELi128ELi1ELi2ELb0ELb0ELb1ELb0EE" in n,
-    "topk_sparse_attn": lambda n: "topk_kernel" in n and ("<512>" in n or "ILi512EE" in n),
+    # the instance for topk <= 2048 (valid slots compacted first)
+    "topk_sparse_attn": lambda n: "topk_kernel" in n and ("<512, true>" in n or "ILi512ELb1EE" in n),
 }
 
 
