@@ -19,8 +19,9 @@
 //   count  one wave per pair of rows: live counts of both rows and of their
 //          union by ballot + popcount -> row_ptr[r+1], pair_ptr[q+1]
 //   scan   one workgroup per array: in-place inclusive scans of row_ptr[1..R]
-//          and pair_ptr[1..Q] built from wavefront prefix scans; writes
-//          nnz_total and pair_total
+//          and pair_ptr[1..Q], 8192 entries per round (8 per thread in
+//          registers, then wavefront prefix scans); writes nnz_total and
+//          pair_total
 //   fill   one wave per pair of rows: ballot + mbcnt compaction of each row's
 //          live columns and of the union with its row tags
 //   order  one workgroup per head and array: stable counting sort of the
@@ -108,32 +109,44 @@ struct ScanJob {
   int32_t *total;
 };
 
-// One workgroup of 1024 threads per job (blockIdx.x selects the job).
+// One workgroup of 1024 threads per job (blockIdx.x selects the job).  Each
+// round covers 8192 entries: a thread loads 8 consecutive ones (all loads in
+// flight at once) and scans them in registers; the threads' totals are
+// scanned across the wavefront and the 16 wavefronts through LDS.
 __global__ void __launch_bounds__(1024) plan_scan_kernel(ScanJob j0, ScanJob j1) {
+  constexpr int PER = 8;
   __shared__ int wave_tot[16];
-  __shared__ int carry_s;
   const ScanJob job = blockIdx.x == 0 ? j0 : j1;
   const int64_t R = job.n;
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = lane_id();
-  if (tid == 0) carry_s = 0;
-  __syncthreads();
   int32_t *a = job.ptr + 1;
-  for (int64_t base = 0; base < R; base += 1024) {
-    const int64_t i = base + tid;
-    const int x = i < R ? a[i] : 0;
-    const int incl = wave_incl_scan(x);
+  int carry = 0;
+  for (int64_t base = 0; base < R; base += 1024 * PER) {
+    const int64_t i0 = base + (int64_t)tid * PER;
+    int x[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) x[k] = i0 + k < R ? a[i0 + k] : 0;
+#pragma unroll
+    for (int k = 1; k < PER; ++k) x[k] += x[k - 1];
+    const int incl = wave_incl_scan(x[PER - 1]);
     if (lane == kWave - 1) wave_tot[wave] = incl;
     __syncthreads();
-    int wave_off = 0;
-    for (int w = 0; w < wave; ++w) wave_off += wave_tot[w];
-    const int carry = carry_s;
-    if (i < R) a[i] = carry + wave_off + incl;
-    __syncthreads();
-    if (tid == 1023) carry_s = carry + wave_off + incl;
-    __syncthreads();
+    int wave_off = 0, round = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const int t = wave_tot[w];
+      wave_off += w < wave ? t : 0;
+      round += t;
+    }
+    const int off = carry + wave_off + incl - x[PER - 1];
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+      if (i0 + k < R) a[i0 + k] = off + x[k];
+    carry += round;
+    __syncthreads();  // wave_tot is rewritten by the next round
   }
-  if (tid == 0) *job.total = carry_s;
+  if (tid == 0) *job.total = carry;
 }
 
 // One wave per pair, as the count kernel: each row's live columns, and the
