@@ -12,12 +12,13 @@
 //   dQ  = scale * dS K,   dK = scale * dS^T Q,   dV = P^T dO
 //   dsink_h = -sum_i exp(sink_h - lse_i) D_i
 //
-// Four kernels, none with atomics, so every gradient is bit-for-bit
-// repeatable:
-//   bwd_pre_kernel   D_i and lse_i * log2(e) per query row (workspace)
+// Three kernels (four at bs = 16), none with atomics, so every gradient is
+// bit-for-bit repeatable:
 //   bwd_dq_kernel    work item (b, h, query block m) over the row plan; the
-//                    wave owning 32 query rows keeps Q^T and dO^T in registers
-//                    and computes S^T = K Q^T, dP^T = V dO^T and
+//                    wave owning 32 query rows first forms its rows' D_i and
+//                    lse_i * log2(e) (written to the workspace for the two
+//                    kernels after it), keeps Q^T and dO^T in registers and
+//                    computes S^T = K Q^T, dP^T = V dO^T and
 //                    dQ^T += K^T dS^T (dS^T straight from the accumulators as
 //                    the B operand, K^T by LDS transpose reads)
 //   bwd_dkdv_kernel  work item (b, K/V head, key block n) over the column plan
@@ -26,6 +27,7 @@
 //                    computes S = Q K^T, dP = dO V^T, dV^T += dO^T P and
 //                    dK^T += Q^T dS
 //   bwd_dsink_kernel one workgroup per head, fixed-order reduction
+// (bs = 16 runs bwd_pre_kernel for D and lse2, then one-wave kernels below.)
 // Tiles travel from HBM straight into LDS (buffer_load_dwordx4 ... lds); each
 // tile is read both row-wise (16-byte reads) and transposed
 // (ds_read_b64_tr_b16), so its 16-byte chunks are XOR-swizzled per row with a
@@ -247,7 +249,8 @@ template <int BS, int D, typename T, bool MASK>
 __global__ void __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
               const T *__restrict__ v, const T *__restrict__ dout,
-              const float *__restrict__ lse2, const float *__restrict__ Dv,
+              const T *__restrict__ out, const float *__restrict__ lse,
+              float *__restrict__ lse2, float *__restrict__ Dv,
               const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
               const int32_t *__restrict__ row_order, int32_t B, int32_t H, int32_t Mb, int32_t Nb,
               float scale_log2, float scale, const FwdOptions opt, T *__restrict__ dq) {
@@ -288,8 +291,31 @@ bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
   const bool q_ok = !MASK || i_row < Sq;     // rows past a cut last block
   const int qsg = (MASK && opt.qseg && q_ok) ? opt.qseg[(int64_t)b * Sq + i_row] : 0;
 
-  const float l2 = q_ok ? lse2[bh * Sq + i_row] : __builtin_inff();
-  const float dd = q_ok ? Dv[bh * Sq + i_row] : 0.f;
+  // D_i = dO_i . out_i (fp32 over the I/O values) and lse_i log2 e of this
+  // lane's row (+inf for a row without a live key, so that its weights
+  // vanish); lane l and l + 32 each hold half of the row.  Written to the
+  // workspace for the dK/dV and d sink kernels, which run after this one.
+  float dd = 0.f, l2 = __builtin_inff();
+  {
+    float part = 0.f;
+    if (q_ok) {
+#pragma unroll
+      for (int c = 0; c < QC; ++c) {
+        float o8[8], g8[8];
+        BIo<T>::load8f(out + (bh * Sq + i_row) * D + 16 * c + 8 * h2, o8);
+        BIo<T>::load8f(dout + (bh * Sq + i_row) * D + 16 * c + 8 * h2, g8);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part = fmaf(o8[i], g8[i], part);
+      }
+      const float l = lse[bh * Sq + i_row];
+      l2 = l == -__builtin_inff() ? __builtin_inff() : l * kLog2e;
+    }
+    dd = sum_xor32(part);
+    if (q_ok && h2 == 0) {
+      Dv[bh * Sq + i_row] = dd;
+      lse2[bh * Sq + i_row] = l2;
+    }
+  }
   bf16x8 qf[QC], gf[QC];
 #pragma unroll
   for (int c = 0; c < QC; ++c) {
@@ -802,7 +828,8 @@ hipError_t launch_grads(const BwdArgs &a, hipStream_t stream) {
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL((bwd_dq_kernel<BS, D, T, MASK>), dim3((unsigned)grid), dim3(BS * 2), 0, stream,
                        (const T *)a.q, (const T *)a.k, (const T *)a.v,
-                       (const T *)a.dout, a.lse2, a.Dv, a.row_ptr, a.col_idx, a.row_order,
+                       (const T *)a.dout, (const T *)a.out, a.lse, a.lse2, a.Dv, a.row_ptr,
+                       a.col_idx, a.row_order,
                        a.B, a.H, a.Mb, a.Nb, scale_log2, a.scale, a.opt, (T *)a.dq);
   }
   {
@@ -840,16 +867,19 @@ bool backward_supported(int32_t bs, int32_t d) {
 hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
   if (!backward_supported(a.bs, a.d)) return hipErrorInvalidValue;
   if (a.opt.kv_group < 1 || a.H % a.opt.kv_group != 0) return hipErrorInvalidValue;
-  hipError_t e;
-  if (a.f32)
-    e = a.d == 32 ? launch_pre<float, 32>(a, stream)
-      : a.d == 64 ? launch_pre<float, 64>(a, stream)
-                  : launch_pre<float, 128>(a, stream);
-  else
-    e = a.d == 32 ? launch_pre<__bf16, 32>(a, stream)
-      : a.d == 64 ? launch_pre<__bf16, 64>(a, stream)
-                  : launch_pre<__bf16, 128>(a, stream);
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  // bs = 16: D and lse2 by their own pass; larger blocks: by the dQ kernel
+  if (a.bs == 16) {
+    if (a.f32)
+      e = a.d == 32 ? launch_pre<float, 32>(a, stream)
+        : a.d == 64 ? launch_pre<float, 64>(a, stream)
+                    : launch_pre<float, 128>(a, stream);
+    else
+      e = a.d == 32 ? launch_pre<__bf16, 32>(a, stream)
+        : a.d == 64 ? launch_pre<__bf16, 64>(a, stream)
+                    : launch_pre<__bf16, 128>(a, stream);
+    if (e != hipSuccess) return e;
+  }
   const bool mask = a.opt.cap_k != 0.f || a.opt.causal != 0 || a.opt.sq % a.bs != 0 ||
                     a.opt.sk % a.bs != 0 || a.opt.qseg != nullptr;
 #define BSA_BWD_CASE(BS_, D_)                                                                  \
