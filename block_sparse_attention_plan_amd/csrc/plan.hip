@@ -31,7 +31,8 @@
 // The backward's column plan is the same construction on the transposed
 // layout (columns c = h * Nb + n, the live query blocks m of each column in
 // ascending order), built by a column count and a column fill kernel (one
-// lane per column, walking m; neighbouring lanes read neighbouring words),
+// lane per column, neighbouring lanes reading neighbouring words, and eight
+// waves per 64 columns, each walking one stretch of m),
 // the same scan, and the same counting sort over the key-block work items
 // (K/V head, n), whose key is the live count summed over the query heads of
 // the K/V head's group.
@@ -264,32 +265,62 @@ __global__ void __launch_bounds__(256) plan_order_kernel(OrderJob j0, OrderJob j
   }
 }
 
-// Live count of each column c = h * Nb + n (one lane per column).
-__global__ void __launch_bounds__(256) plan_col_count_kernel(const int32_t *__restrict__ layout,
-                                                             int32_t H, int32_t Mb, int32_t Nb,
-                                                             int32_t *__restrict__ col_ptr) {
-  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (c == 0) col_ptr[0] = 0;
-  if (c >= (int64_t)H * Nb) return;
-  const int64_t h = c / Nb, n = c % Nb;
-  const int32_t *col = layout + h * Mb * Nb + n;
+// Column kernels: one workgroup per 64 columns c = h * Nb + n (lane = column,
+// so neighbouring lanes read neighbouring layout words) and kColWaves
+// waves, wave s walking the contiguous stretch of query blocks
+// [s * seg, (s + 1) * seg), seg = ceil(Mb / kColWaves).  The waves' counts
+// meet in LDS.
+constexpr int kColWaves = 8;
+
+__device__ __forceinline__ int col_count_stretch(const int32_t *col, int64_t stride, int m0,
+                                                 int m1) {
   int cnt = 0;
 #pragma unroll 8
-  for (int m = 0; m < Mb; ++m) cnt += col[(int64_t)m * Nb] != 0;
-  col_ptr[c + 1] = cnt;
+  for (int m = m0; m < m1; ++m) cnt += col[(int64_t)m * stride] != 0;
+  return cnt;
 }
 
-// Query blocks of each column in ascending order.
-__global__ void __launch_bounds__(256) plan_col_fill_kernel(const int32_t *__restrict__ layout,
-                                                            int32_t H, int32_t Mb, int32_t Nb,
-                                                            const int32_t *__restrict__ col_ptr,
-                                                            int32_t *__restrict__ row_idx) {
-  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= (int64_t)H * Nb) return;
+// Live count of each column.
+__global__ void __launch_bounds__(64 * kColWaves) plan_col_count_kernel(
+    const int32_t *__restrict__ layout, int32_t H, int32_t Mb, int32_t Nb,
+    int32_t *__restrict__ col_ptr) {
+  __shared__ int part[kColWaves][64];
+  const int lane = threadIdx.x % 64, s = threadIdx.x / 64;
+  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
+  if (blockIdx.x == 0 && threadIdx.x == 0) col_ptr[0] = 0;
+  const bool ok = c < (int64_t)H * Nb;
+  const int seg = (Mb + kColWaves - 1) / kColWaves;
+  const int m0 = min(Mb, s * seg), m1 = min(Mb, (s + 1) * seg);
+  const int64_t h = c / Nb, n = c % Nb;
+  part[s][lane] = ok ? col_count_stretch(layout + h * Mb * Nb + n, Nb, m0, m1) : 0;
+  __syncthreads();
+  if (s == 0 && ok) {
+    int cnt = 0;
+#pragma unroll
+    for (int w = 0; w < kColWaves; ++w) cnt += part[w][lane];
+    col_ptr[c + 1] = cnt;
+  }
+}
+
+// Query blocks of each column in ascending order: each wave counts its
+// stretch, the counts of the stretches before it give its first slot.
+__global__ void __launch_bounds__(64 * kColWaves) plan_col_fill_kernel(
+    const int32_t *__restrict__ layout, int32_t H, int32_t Mb, int32_t Nb,
+    const int32_t *__restrict__ col_ptr, int32_t *__restrict__ row_idx) {
+  __shared__ int part[kColWaves][64];
+  const int lane = threadIdx.x % 64, s = threadIdx.x / 64;
+  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
+  const bool ok = c < (int64_t)H * Nb;
+  const int seg = (Mb + kColWaves - 1) / kColWaves;
+  const int m0 = min(Mb, s * seg), m1 = min(Mb, (s + 1) * seg);
   const int64_t h = c / Nb, n = c % Nb;
   const int32_t *col = layout + h * Mb * Nb + n;
+  part[s][lane] = ok ? col_count_stretch(col, Nb, m0, m1) : 0;
+  __syncthreads();
+  if (!ok) return;
   int pos = col_ptr[c];
-  for (int m = 0; m < Mb; ++m)
+  for (int w = 0; w < s; ++w) pos += part[w][lane];
+  for (int m = m0; m < m1; ++m)
     if (col[(int64_t)m * Nb] != 0) row_idx[pos++] = m;
 }
 
@@ -365,13 +396,13 @@ hipError_t launch_plan_cols(const int32_t *layout, int32_t H, int32_t Hkv, int32
                             int32_t *col_ptr, int32_t *col_order, int32_t *nnz_total,
                             int32_t *row_idx, hipStream_t stream) {
   const int32_t C = H * Nb;
-  const int nblk = (C + 255) / 256;
-  hipLaunchKernelGGL(plan_col_count_kernel, dim3(nblk), dim3(256), 0, stream, layout, H, Mb, Nb,
-                     col_ptr);
+  const int nblk = (C + 63) / 64;
+  hipLaunchKernelGGL(plan_col_count_kernel, dim3(nblk), dim3(64 * kColWaves), 0, stream, layout,
+                     H, Mb, Nb, col_ptr);
   const ScanJob scan{C, col_ptr, nnz_total};
   hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, scan, scan);
-  hipLaunchKernelGGL(plan_col_fill_kernel, dim3(nblk), dim3(256), 0, stream, layout, H, Mb, Nb,
-                     (const int32_t *)col_ptr, row_idx);
+  hipLaunchKernelGGL(plan_col_fill_kernel, dim3(nblk), dim3(64 * kColWaves), 0, stream, layout,
+                     H, Mb, Nb, (const int32_t *)col_ptr, row_idx);
   const int32_t g = H / Hkv;
   const OrderJob order{Hkv, Nb, g * Mb, g, col_ptr, col_order};
   return launch_order(order, OrderJob{0, 0, 0, 1, nullptr, nullptr}, PairFlag{nullptr, nullptr, nullptr},
