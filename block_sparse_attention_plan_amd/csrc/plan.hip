@@ -15,7 +15,8 @@
 // whether the unions hold at most three quarters of the live tiles, which is
 // when the forward uses the pairs.
 //
-// Four kernels, all stream-ordered:
+// Four steps in three launches, all stream-ordered (fill and order share the
+// last launch, as both need only the scanned counts):
 //   count  one wave per pair of rows: live counts of both rows and of their
 //          union by ballot + popcount -> row_ptr[r+1], pair_ptr[q+1]
 //   scan   one workgroup per array: in-place inclusive scans of row_ptr[1..R]
@@ -152,16 +153,17 @@ __global__ void __launch_bounds__(1024) plan_scan_kernel(ScanJob j0, ScanJob j1)
 
 // One wave per pair, as the count kernel: each row's live columns, and the
 // union with bit 24 (row 2p) and bit 25 (row 2p + 1) set per column.
-__global__ void __launch_bounds__(256) plan_fill_kernel(const int32_t *__restrict__ layout,
-                                                        int32_t H, int32_t Mb, int32_t Nb,
-                                                        const int32_t *__restrict__ row_ptr,
-                                                        int32_t *__restrict__ col_idx,
-                                                        const int32_t *__restrict__ pair_ptr,
-                                                        int32_t *__restrict__ pair_cols) {
+// (A body run by the first blocks of the fill-and-order launch.)
+__device__ __forceinline__ void plan_fill_body(int block, const int32_t *__restrict__ layout,
+                                               int32_t H, int32_t Mb, int32_t Nb,
+                                               const int32_t *__restrict__ row_ptr,
+                                               int32_t *__restrict__ col_idx,
+                                               const int32_t *__restrict__ pair_ptr,
+                                               int32_t *__restrict__ pair_cols) {
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
   const int Mp = (Mb + 1) / 2;
-  const int64_t q = (int64_t)blockIdx.x * (blockDim.x / kWave) + wave;
+  const int64_t q = (int64_t)block * (blockDim.x / kWave) + wave;
   if (q >= (int64_t)H * Mp) return;
   const int64_t h = q / Mp, p = q % Mp;
   const int64_t r0 = h * Mb + 2 * p;
@@ -203,16 +205,17 @@ struct PairFlag {
   int32_t *flag;  // nullptr: no flag to write
 };
 
-// One workgroup per segment of job 0, then per segment of job 1.
-// Dynamic LDS: start[max_key+1] (bucket start, then running position) as int.
-__global__ void __launch_bounds__(256) plan_order_kernel(OrderJob j0, OrderJob j1, PairFlag pf) {
-  extern __shared__ int start[];
-  const bool first = (int)blockIdx.x < j0.segs;
+// One workgroup per segment of job 0, then per segment of job 1 (block =
+// the workgroup's index among them).  start[max_key+1] in LDS (bucket
+// start, then running position).
+__device__ __forceinline__ void plan_order_body(int block, int *start, OrderJob j0, OrderJob j1,
+                                                PairFlag pf) {
+  const bool first = block < j0.segs;
   const OrderJob job = first ? j0 : j1;
-  const int seg = first ? blockIdx.x : blockIdx.x - j0.segs;
+  const int seg = first ? block : block - j0.segs;
   const int items = job.items, max_key = job.max_key, g = job.g;
   const int tid = threadIdx.x;
-  if (blockIdx.x == 0 && tid == 0 && pf.flag != nullptr)
+  if (block == 0 && tid == 0 && pf.flag != nullptr)
     *pf.flag = 4 * (int64_t)*pf.pair_total <= 3 * (int64_t)*pf.nnz_total ? 1 : 0;
   const int nkeys = max_key + 1;
   const int32_t *sp = job.ptr + (int64_t)seg * g * items;
@@ -263,6 +266,26 @@ __global__ void __launch_bounds__(256) plan_order_kernel(OrderJob j0, OrderJob j
       __builtin_amdgcn_wave_barrier();
     }
   }
+}
+
+// Dynamic LDS: the order body's start[].
+__global__ void __launch_bounds__(256) plan_order_kernel(OrderJob j0, OrderJob j1, PairFlag pf) {
+  extern __shared__ int start[];
+  plan_order_body(blockIdx.x, start, j0, j1, pf);
+}
+
+// The row plan's fill and order in one launch (both need only the scanned
+// counts): blocks 0 .. nfill-1 fill, the rest order.
+__global__ void __launch_bounds__(256) plan_fill_order_kernel(
+    int32_t nfill, const int32_t *__restrict__ layout, int32_t H, int32_t Mb, int32_t Nb,
+    const int32_t *__restrict__ row_ptr, int32_t *__restrict__ col_idx,
+    const int32_t *__restrict__ pair_ptr, int32_t *__restrict__ pair_cols, OrderJob j0,
+    OrderJob j1, PairFlag pf) {
+  extern __shared__ int start[];
+  if ((int)blockIdx.x < nfill)
+    plan_fill_body(blockIdx.x, layout, H, Mb, Nb, row_ptr, col_idx, pair_ptr, pair_cols);
+  else
+    plan_order_body((int)blockIdx.x - nfill, start, j0, j1, pf);
 }
 
 // Column kernels: one workgroup per 64 columns c = h * Nb + n (lane = column,
@@ -324,14 +347,20 @@ __global__ void __launch_bounds__(64 * kColWaves) plan_col_fill_kernel(
     if (col[(int64_t)m * Nb] != 0) row_idx[pos++] = m;
 }
 
+size_t order_lds(const OrderJob &j0, const OrderJob &j1) {
+  return (size_t)(std::max(j0.max_key, j1.max_key) + 1) * sizeof(int);
+}
+
+hipError_t allow_lds(const void *kernel, size_t lds) {
+  if (lds <= 64 * 1024) return hipSuccess;
+  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
 hipError_t launch_order(const OrderJob &j0, const OrderJob &j1, const PairFlag &pf,
                         hipStream_t stream) {
-  const size_t lds = (size_t)(std::max(j0.max_key, j1.max_key) + 1) * sizeof(int);
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void *)plan_order_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
+  const size_t lds = order_lds(j0, j1);
+  hipError_t e = allow_lds((const void *)plan_order_kernel, lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(plan_order_kernel, dim3(j0.segs + j1.segs), dim3(256), lds, stream, j0, j1,
                      pf);
   return hipGetLastError();
@@ -372,11 +401,15 @@ hipError_t launch_plan(const int32_t *layout, int32_t H, int32_t Mb, int32_t Nb,
                      row_ptr, pair_ptr);
   hipLaunchKernelGGL(plan_scan_kernel, dim3(2), dim3(1024), 0, stream,
                      ScanJob{R, row_ptr, nnz_total}, ScanJob{Q, pair_ptr, pair_info});
-  hipLaunchKernelGGL(plan_fill_kernel, dim3(nblk), dim3(256), 0, stream, layout, H, Mb, Nb,
-                     (const int32_t *)row_ptr, col_idx, (const int32_t *)pair_ptr, pair_cols);
-  return launch_order(OrderJob{H, Mb, Nb, 1, row_ptr, row_order},
-                      OrderJob{H, Mp, Nb, 1, pair_ptr, pair_order},
-                      PairFlag{nnz_total, pair_info, pair_info + 1}, stream);
+  const OrderJob j0{H, Mb, Nb, 1, row_ptr, row_order}, j1{H, Mp, Nb, 1, pair_ptr, pair_order};
+  const size_t lds = order_lds(j0, j1);
+  hipError_t e = allow_lds((const void *)plan_fill_order_kernel, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(plan_fill_order_kernel, dim3(nblk + j0.segs + j1.segs), dim3(256), lds, stream,
+                     nblk, layout, H, Mb, Nb, (const int32_t *)row_ptr, col_idx,
+                     (const int32_t *)pair_ptr, pair_cols, j0, j1,
+                     PairFlag{nnz_total, pair_info, pair_info + 1});
+  return hipGetLastError();
 }
 
 bool plan_cols_geometry(int32_t H, int32_t Hkv, int32_t Mb, int32_t Nb, PlanColsGeometry *g) {
