@@ -10,8 +10,11 @@
 // [0, N)) contribute nothing; the running maximum starts at a finite floor so
 // a position without a valid slot produces zeros instead of NaN.
 //
-// Work item = (batch, position); one workgroup of four waves.  Slots are
-// processed in chunks of 32 whose rows are copied straight from HBM into LDS
+// Work item = (batch, position); one workgroup of four waves.  With topk up
+// to 2048 the position's valid indices are first compacted, in slot order,
+// into an LDS list, so that slots holding -1 cost nothing; longer lists are
+// read in place.  Slots (list entries) are processed in chunks of 32 whose
+// rows are copied straight from HBM into LDS
 // (at d = 512 one buffer_load_dwordx4 ... lds per 1 KiB row; at d = 128 and
 // 256 one or two buffer_load_dword ... lds of 256 bytes, so that every row
 // keeps its padding; a slot without a valid index reads as a zero row), one
@@ -33,10 +36,10 @@
 // gathered element once per workgroup instead of once per wave; the LDS
 // transpose reads were what bounded the head-split form.  The two chunk
 // buffers (2 x 33 KiB, rows padded by 32 bytes against bank conflicts) plus
-// P (5 KiB) let two workgroups share a CU, so each SIMD interleaves the waves
-// of two positions.  The buffers are distinct LDS objects and the chunk loop
-// is unrolled by two, so the compiler never waits for a copy into the buffer
-// it is not reading.
+// P (5 KiB) and the index list (8 KiB) let two workgroups share a CU, so
+// each SIMD interleaves the waves of two positions.  The buffers are
+// distinct LDS objects and the chunk loop is unrolled by two, so the
+// compiler never waits for a copy into the buffer it is not reading.
 #include "bsa_device.h"
 #include "bsa_internal.h"
 
