@@ -42,6 +42,72 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Packed sequences: a tile whose query and key segment ids have disjoint
+// [min, max] ranges has only masked scores, so its weights are exactly zero
+// and it adds nothing to any gradient; the bs >= 32 kernels skip it, copies
+// included.  (Ranges only ever keep a tile too many; the element masks still
+// decide every score.)
+
+// [lo, hi] of the n ids at ids[0 ..], over one wave (lo > hi: none).
+__device__ __forceinline__ void wave_id_range(const int32_t *ids, int n, int &lo, int &hi) {
+  lo = INT32_MAX;
+  hi = INT32_MIN;
+  for (int i = __lane_id(); i < n; i += 64) {
+    const int v = ids[i];
+    lo = min(lo, v);
+    hi = max(hi, v);
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    lo = min(lo, __shfl_xor(lo, o));
+    hi = max(hi, __shfl_xor(hi, o));
+  }
+}
+
+// Bit i (i < 16, i < nblocks) set when id block i holds an id in [lo, hi].
+// block(i, ids, len) names block i's ids; 16 lanes read each block (IPL ids
+// per lane), four blocks per pass, the four passes' loads in flight
+// together.  Every wave of a workgroup computes the same bits.
+template <int IPL, typename F>
+__device__ __forceinline__ uint32_t keep_bits16(F block, int nblocks, int lo, int hi) {
+  const int lane = __lane_id();
+  const int g = lane / 16, sub = lane % 16;
+  int mn[4], mx[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    mn[p] = INT32_MAX;
+    mx[p] = INT32_MIN;
+    const int i = 4 * p + g;
+    if (i < nblocks) {
+      const int32_t *ids;
+      int len;
+      block(i, ids, len);
+#pragma unroll
+      for (int k = 0; k < IPL; ++k) {
+        const int e = sub * IPL + k;
+        if (e < len) {
+          const int v = ids[e];
+          mn[p] = min(mn[p], v);
+          mx[p] = max(mx[p], v);
+        }
+      }
+    }
+  }
+  uint32_t bits = 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      mn[p] = min(mn[p], __shfl_xor(mn[p], o));
+      mx[p] = max(mx[p], __shfl_xor(mx[p], o));
+    }
+    const uint64_t ball = __ballot(sub == 0 && mn[p] <= hi && mx[p] >= lo);
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) bits |= (uint32_t)((ball >> (16 * gg)) & 1u) << (4 * p + gg);
+  }
+  return bits;
+}
+
 // Chunk c of tile row r sits at chunk c ^ f(r).  Row reads touch 16
 // consecutive rows at one logical chunk (f is a bijection on r % 16 among the
 // rows that share LDS banks); transpose reads touch 4 aligned rows at 4
@@ -245,7 +311,9 @@ __device__ __forceinline__ Weight weight(float s, float scale_log2, float l2, co
   return Weight{fast_exp2(fmaf(s, scale_log2, -l2)), slope};
 }
 
-template <int BS, int D, typename T, bool MASK>
+// SEG instances (calls with segment ids) also skip the tiles whose ids
+// cannot meet.
+template <int BS, int D, typename T, bool MASK, bool SEG = false>
 __global__ void __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
               const T *__restrict__ v, const T *__restrict__ dout,
@@ -332,7 +400,25 @@ bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
   const int lc_off = 2 * (G % 2) + c_src / 2, pc = 4 * (c_src % 2);
   const int sw0 = BSwz<D>::f(tr_r), sw8 = BSwz<D>::f(tr_r + 8);
 
+  // segment ids: the block row's query id range, and keep bits for the
+  // row's tiles, 16 at a time
+  int qlo = 0, qhi = 0;
+  uint32_t keep = 0;
+  if constexpr (SEG)
+    wave_id_range(opt.qseg + (int64_t)b * Sq + (int64_t)m * BS,
+                  (int)min((int64_t)BS, Sq - (int64_t)m * BS), qlo, qhi);
   for (int t = beg; t < end; ++t) {
+    if constexpr (SEG) {
+      if ((t - beg) % 16 == 0)
+        keep = keep_bits16<BS / 16>(
+            [&](int i, const int32_t *&ids, int &len) {
+              const int64_t k0 = (int64_t)col_idx[t + i] * BS;
+              ids = opt.kseg + (int64_t)b * Sk + k0;
+              len = (int)min((int64_t)BS, Sk - k0);
+            },
+            min(16, end - t), qlo, qhi);
+      if (!((keep >> ((t - beg) % 16)) & 1u)) continue;   // no key shares a segment
+    }
     const int ncol = col_idx[t];
     if (MASK && opt.causal && ncol > m) continue;   // every key after every query
     __syncthreads();                                // previous tile fully read
@@ -385,7 +471,7 @@ bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
                      scale * acc[dt][4 * a + 3]);
 }
 
-template <int BS, int D, typename T, bool MASK>
+template <int BS, int D, typename T, bool MASK, bool SEG = false>
 __global__ void __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dkdv_kernel(const T *__restrict__ q, const T *__restrict__ k,
                 const T *__restrict__ v, const T *__restrict__ dout,
@@ -449,12 +535,30 @@ bwd_dkdv_kernel(const T *__restrict__ q, const T *__restrict__ k,
   const int lc_off = 2 * (G % 2) + c_src / 2, pc = 4 * (c_src % 2);
   const int sw0 = BSwz<D>::f(tr_r), sw8 = BSwz<D>::f(tr_r + 8);
 
+  // segment ids: the key block's id range, and keep bits for the visited
+  // tiles of each query head, 16 at a time
+  int klo = 0, khi = 0;
+  uint32_t keep = 0;
+  if constexpr (SEG)
+    wave_id_range(opt.kseg + (int64_t)b * Sk + (int64_t)n * BS,
+                  (int)min((int64_t)BS, Sk - (int64_t)n * BS), klo, khi);
   for (int hh = 0; hh < g; ++hh) {
     const int h = kvh * g + hh;
     const int64_t bh = (int64_t)b * H + h;
     const int beg = col_ptr[h * Nb + n];
     const int end = col_ptr[h * Nb + n + 1];
     for (int t = beg; t < end; ++t) {
+      if constexpr (SEG) {
+        if ((t - beg) % 16 == 0)
+          keep = keep_bits16<BS / 16>(
+              [&](int i, const int32_t *&ids, int &len) {
+                const int64_t q0 = (int64_t)row_idx[t + i] * BS;
+                ids = opt.qseg + (int64_t)b * Sq + q0;
+                len = (int)min((int64_t)BS, Sq - q0);
+              },
+              min(16, end - t), klo, khi);
+        if (!((keep >> ((t - beg) % 16)) & 1u)) continue;   // no query shares a segment
+      }
       const int m = row_idx[t];
       if (MASK && opt.causal && m < n) continue;    // every key after every query
       __syncthreads();                              // previous tile fully read
@@ -819,14 +923,15 @@ hipError_t launch_grads16(const BwdArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BS, int D, typename T, bool MASK>
+template <int BS, int D, typename T, bool MASK, bool SEG = false>
 hipError_t launch_grads(const BwdArgs &a, hipStream_t stream) {
   const float scale_log2 = a.scale * kLog2e;
   {
     const int64_t W = (int64_t)a.B * a.H * a.Mb;
     const int64_t grid = (W + 7) / 8 * 8;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dq_kernel<BS, D, T, MASK>), dim3((unsigned)grid), dim3(BS * 2), 0, stream,
+    hipLaunchKernelGGL((bwd_dq_kernel<BS, D, T, MASK, SEG>), dim3((unsigned)grid), dim3(BS * 2), 0,
+                       stream,
                        (const T *)a.q, (const T *)a.k, (const T *)a.v,
                        (const T *)a.dout, (const T *)a.out, a.lse, a.lse2, a.Dv, a.row_ptr,
                        a.col_idx, a.row_order,
@@ -837,8 +942,8 @@ hipError_t launch_grads(const BwdArgs &a, hipStream_t stream) {
     const int64_t W = (int64_t)a.B * Hkv * a.Nb;
     const int64_t grid = (W + 7) / 8 * 8;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<BS, D, T, MASK>), dim3((unsigned)grid), dim3(BS * 2), 0,
-                       stream,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<BS, D, T, MASK, SEG>), dim3((unsigned)grid), dim3(BS * 2),
+                       0, stream,
                        (const T *)a.q, (const T *)a.k, (const T *)a.v,
                        (const T *)a.dout, a.lse2, a.Dv, a.col_ptr, a.row_idx, a.col_order,
                        a.B, a.H, Hkv, a.Mb, a.Nb, scale_log2, a.scale, a.opt, (T *)a.dk,
@@ -882,12 +987,15 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
   }
   const bool mask = a.opt.cap_k != 0.f || a.opt.causal != 0 || a.opt.sq % a.bs != 0 ||
                     a.opt.sk % a.bs != 0 || a.opt.qseg != nullptr;
+  const bool seg = a.opt.qseg != nullptr;
 #define BSA_BWD_CASE(BS_, D_)                                                                  \
   if (a.bs == BS_ && a.d == D_)                                                               \
-    e = a.f32 ? (mask ? launch_grads<BS_, D_, float, true>(a, stream)                         \
-                      : launch_grads<BS_, D_, float, false>(a, stream))                       \
-              : (mask ? launch_grads<BS_, D_, __bf16, true>(a, stream)                        \
-                      : launch_grads<BS_, D_, __bf16, false>(a, stream));
+    e = a.f32 ? (seg    ? launch_grads<BS_, D_, float, true, true>(a, stream)                 \
+                 : mask ? launch_grads<BS_, D_, float, true>(a, stream)                       \
+                        : launch_grads<BS_, D_, float, false>(a, stream))                     \
+              : (seg    ? launch_grads<BS_, D_, __bf16, true, true>(a, stream)                \
+                 : mask ? launch_grads<BS_, D_, __bf16, true>(a, stream)                      \
+                        : launch_grads<BS_, D_, __bf16, false>(a, stream));
 #define BSA_BWD16_CASE(D_)                                                                     \
   if (a.bs == 16 && a.d == D_)                                                                \
     e = a.f32 ? (mask ? launch_grads16<D_, float, true>(a, stream)                            \

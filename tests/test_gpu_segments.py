@@ -202,3 +202,41 @@ def test_forward_segments_long_row_unfiltered(gpu, bs, d):
     ks = W.packed_segment_ids(B, Sk, 50, 4000, seed=nb)
     say(f"[segments] long row, {nb} tiles, bs={bs} d={d}")
     _segment_case(gpu, lay, bs, d, Sq, Sk, qs, ks, seed=nb + bs, what=f"long row bs={bs} d={d}")
+
+
+@pytest.mark.parametrize("ids", ["packed", "unordered"])
+@pytest.mark.parametrize("bs,d,S,lo,hi", [(32, 64, 1024, 60, 300), (64, 128, 1536, 100, 600),
+                                          (128, 64, 2560, 300, 1200)])
+def test_backward_segments_long_lists(gpu, bs, d, S, lo, hi, ids):
+    """Rows and columns of more than 16 live tiles, so the bs >= 32 kernels
+    test their tiles' segment ranges in several batches of 16; with packed
+    sequences most tiles are skipped (disjoint id ranges), with ids drawn
+    per token from {0, 1, 2} none are.  Two query heads share each K/V head
+    and there is a sink; every gradient against the oracle."""
+    H, Hkv, B = 2, 1, 1
+    nb = S // bs
+    rng = np.random.default_rng(S + bs)
+    lay = (rng.random((H, nb, nb)) < 0.8).astype(np.int32)
+    lay[:, np.arange(nb), np.arange(nb)] = 1
+    x = W.make_bsa("segments_bwd_long", B=B, H=H, S=S, bs=bs, d=d, dtype="bf16", layout="given",
+                   layout_array=lay, seed=S + 5, Hkv=Hkv, sink_mean=1.0)
+    if ids == "packed":
+        seg = W.packed_segment_ids(B, S, lo, hi, seed=S + 6)
+    else:
+        seg = torch.from_numpy(rng.integers(0, 3, size=(B, S)).astype(np.int32))
+    dout = W.upstream_gradient(x.q.shape, seed=S + 7)
+    say(f"[segments] backward long lists bs={bs} d={d} S={S} ids={ids}")
+    plan, _ = check_plan(gpu, lay)
+    pc = check_plan_cols(gpu, lay, Hkv)
+    q, k, v, sink, sg = x.q.to(gpu), x.k.to(gpu), x.v.to(gpu), x.sink.to(gpu), seg.to(gpu)
+    kw = dict(attn_sink=sink, bs=bs, q_segment_ids=sg, kv_segment_ids=sg)
+    out, lse = bsa.bsa_forward(q, k, v, plan, x.scale, **kw)
+    dq, dk, dv, _ = bsa.bsa_backward(q, k, v, out, dout.to(gpu), lse, plan, pc, x.scale, **kw)
+    torch.cuda.synchronize()
+    okw = dict(sink=x.sink.numpy().astype(np.float64), q_segment_ids=seg.numpy(),
+               kv_segment_ids=seg.numpy())
+    rq, rk, rv, _ = O.attention_backward_dense(to64(x.q), to64(x.k), to64(x.v), to64(dout), lay,
+                                               bs, x.scale, **okw)
+    compare_grad(to64(dq), rq, f"dq long lists bs={bs} {ids}")
+    compare_grad(to64(dk), rk, f"dk long lists bs={bs} {ids}")
+    compare_grad(to64(dv), rv, f"dv long lists bs={bs} {ids}")
