@@ -11,9 +11,10 @@
 // a position without a valid slot produces zeros instead of NaN.
 //
 // Work item = (batch, position); one workgroup of four waves.  With topk up
-// to 2048 the position's valid indices are first compacted, in slot order,
-// into an LDS list, so that slots holding -1 cost nothing; longer lists are
-// read in place.  Slots (list entries) are processed in chunks of 32 whose
+// to 2048 the position's valid indices are first compacted into an LDS list,
+// grouped by table range (slot order within a range), so that slots holding
+// -1 cost nothing and the workgroups on an XCD gather from one range of the
+// table at a time; longer lists are read in place.  Slots (list entries) are processed in chunks of 32 whose
 // rows are copied straight from HBM into LDS
 // (at d = 512 one buffer_load_dwordx4 ... lds per 1 KiB row; at d = 128 and
 // 256 one or two buffer_load_dword ... lds of 256 bytes, so that every row
@@ -53,6 +54,13 @@ constexpr float kLazy = 8.0f;  // tolerated staleness of the running max (log2 u
 template <int D> constexpr int kReadAheadS = D == 512 ? 6 : 3;
 // Largest topk whose valid indices are compacted into LDS (4 bytes each)
 constexpr int kWindow = 2048;
+// The compacted list groups the valid indices by index range (in slot order
+// within a range): a range spans 2^shift table rows, about 2 MiB at this d,
+// at most kMaxRanges ranges (wider ones for larger tables).  Workgroups that
+// run together then gather from the same range at the same time, which
+// stays in an XCD's 4 MB L2, instead of from the whole table.
+template <int D> constexpr int kRangeShift = D == 512 ? 11 : D == 256 ? 12 : 13;
+constexpr int kMaxRanges = 8;
 
 template <int D, bool COMPACT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
@@ -78,7 +86,7 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
   // slot order; chunks take T of them at a time, so slots without a valid
   // index cost no products.  (The other instances read the slots in place.)
   __shared__ __attribute__((aligned(16))) int32_t LST[COMPACT ? kWindow : 1];
-  __shared__ int32_t WCNT[4];
+  __shared__ int32_t WCNT[4 * kMaxRanges];  // [range][wave] counts
 
   const int64_t pos = blockIdx.x;  // b * M + m
   const int64_t b = pos / M;
@@ -110,38 +118,47 @@ topk_kernel(const __bf16 *__restrict__ q, const __bf16 *__restrict__ kv,
 
   auto valid = [&](int my) -> int { return (my >= 0 && my < N) ? my : -1; };
   // COMPACT: slots [w0, w1) (at most kWindow): each wave takes a quarter of
-  // them, 64 per load; the waves' counts give each its offset in LST.
-  // Returns the number of valid indices.
+  // them, 64 per load.  Per index range, the waves' counts give each wave
+  // its offset in LST, after the earlier ranges; ballots with mbcnt give
+  // each lane its place, so the list is the same on every run.  Returns the
+  // number of valid indices.
+  int rshift = kRangeShift<D>;
+  while (((N - 1) >> rshift) >= kMaxRanges) ++rshift;
+  const int nranges = N > 0 ? ((N - 1) >> rshift) + 1 : 1;
   auto compact_window = [&](int w0, int w1) -> int {
     constexpr int PERW = kWindow / 4 / 64;
-    int raw[PERW];
+    int raw[PERW], rng[PERW];  // index; its range, -1 for an invalid slot
 #pragma unroll
     for (int j = 0; j < PERW; ++j) {
       const int slot = w0 + (wid * PERW + j) * 64 + lane;
       raw[j] = slot < w1 ? ib[slot] : -1;
     }
-    int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < PERW; ++j) {
-      raw[j] = (raw[j] >= 0 && raw[j] < N) ? raw[j] : -1;
-      cnt += __popcll(__ballot(raw[j] >= 0));
+    for (int j = 0; j < PERW; ++j) rng[j] = (raw[j] >= 0 && raw[j] < N) ? raw[j] >> rshift : -1;
+    for (int r = 0; r < nranges; ++r) {
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < PERW; ++j) cnt += __popcll(__ballot(rng[j] == r));
+      if (lane == 0) WCNT[4 * r + wid] = cnt;
     }
-    if (lane == 0) WCNT[wid] = cnt;
     __syncthreads();
-    int off = 0, tot = 0;
+    int tot = 0;
+    for (int r = 0; r < nranges; ++r) {
+      int off = tot;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int c = WCNT[w];
-      off += w < wid ? c : 0;
-      tot += c;
-    }
+      for (int w = 0; w < 4; ++w) {
+        const int c = WCNT[4 * r + w];
+        off += w < wid ? c : 0;
+        tot += c;
+      }
 #pragma unroll
-    for (int j = 0; j < PERW; ++j) {
-      const uint64_t vm = __ballot(raw[j] >= 0);
-      const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(vm >> 32),
-                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)vm, 0u));
-      if (raw[j] >= 0) LST[off + below] = raw[j];
-      off += __popcll(vm);
+      for (int j = 0; j < PERW; ++j) {
+        const uint64_t vm = __ballot(rng[j] == r);
+        const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(vm >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)vm, 0u));
+        if (rng[j] == r) LST[off + below] = raw[j];
+        off += __popcll(vm);
+      }
     }
     __syncthreads();
     return tot;

@@ -85,3 +85,31 @@ def test_topk_long_lists(gpu, d, topk):
     ref = O.topk_attention(to64(t.q), to64(t.kv), ref_idx, t.sink.numpy(), t.scale)
     compare(to64(out), ref, f"topk long d={d} topk={topk}")
     assert torch.all(out[0, 2] == 0)
+
+
+@pytest.mark.parametrize("d,N", [(128, 8193), (128, 65536), (128, 70000), (256, 4097),
+                                 (256, 40000), (512, 2049), (512, 16384), (512, 20000)])
+def test_topk_index_ranges(gpu, d, N):
+    """The compacted list groups valid indices by table range (about 2 MiB of
+    rows each, at most eight ranges, wider ones past that): two ranges with a
+    last range of one row, exactly eight, and tables that widen the ranges.
+    Positions with indices in descending order, all in the last range, and
+    -1 / out-of-range slots; every output against the oracle, and two
+    launches bit for bit."""
+    t = W.make_topk("topk_ranges", B=1, M=4, H=20, d=d, N=N, topk=600, seed=N + d, drop=0.1,
+                    with_sink=True)
+    idx = t.idx.clone()
+    idx[0, 1] = torch.sort(idx[0, 1], descending=True).values
+    idx[0, 2, :] = torch.arange(N - 600, N, dtype=idx.dtype).flip(0)
+    idx[0, 2, ::5] = N
+    idx[0, 3, ::9] = -3
+    say(f"[topk] index ranges d={d} N={N}")
+    q, kv, ig, sink = t.q.to(gpu), t.kv.to(gpu), idx.to(gpu), t.sink.to(gpu)
+    out = bsa.topk_sparse_attn(q, kv, ig, sink, t.scale)
+    out2 = bsa.topk_sparse_attn(q, kv, ig, sink, t.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "top-k is not deterministic"
+    ref_idx = idx.numpy().copy()
+    ref_idx[(ref_idx < 0) | (ref_idx >= N)] = -1
+    ref = O.topk_attention(to64(t.q), to64(t.kv), ref_idx, t.sink.numpy(), t.scale)
+    compare(to64(out), ref, f"topk ranges d={d} N={N}")
