@@ -402,6 +402,9 @@ int bsa_layout_adaptive(const void *q, const void *k, int32_t H, int32_t Hkv, in
  *   topk >= 1 (no alignment needed); one batch's kv (N * d * 2 bytes) at
  *   most 4 GiB - 1 KiB
  *   out   device bf16 [B, M, H, d], written
+ * The sums run over the valid slots in a fixed order (with topk <= 2048,
+ * grouped by range of kv rows, slot order within a range), so repeated
+ * calls agree bit for bit; a reordered index list changes only rounding.
  * Errors: BSA_ERR_INVALID_ARG, BSA_ERR_UNSUPPORTED, BSA_ERR_MISALIGNED,
  * BSA_ERR_HIP.
  */
