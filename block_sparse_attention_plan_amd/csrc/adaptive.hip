@@ -12,11 +12,13 @@
 //   pool   one wave per (head, block): fp32 sum of the block's rows in a
 //          fixed order, then the unit vector (zero for a zero sum) into the
 //          workspace.  Reads q and k once: bound by HBM.
-//   score  one workgroup per (head, 16 block rows, 64 block columns): the
+//   score  one workgroup per (head, 64 block rows, 64 block columns): the
 //          unit vectors staged in LDS with 16-byte copies (rows padded by
-//          four floats), each thread 2 x 2 fp32 dot products from 16-byte
-//          reads, the threshold, and optionally the scores themselves.  Under the causal rule, a tile wholly above
-//          the diagonal only writes zeros when no scores are asked for.
+//          four floats), each thread 4 x 4 fp32 dot products from 16-byte
+//          reads (eight reads feed 64 FMAs), the threshold, and optionally
+//          the scores themselves.  Under the causal rule, a tile wholly
+//          above the diagonal only writes zeros when no scores are asked
+//          for.
 #include "bsa_device.h"
 #include "bsa_internal.h"
 
@@ -82,7 +84,7 @@ __global__ void __launch_bounds__(256) adaptive_pool_kernel(const T *__restrict_
   }
 }
 
-constexpr int kTileM = 16, kTileN = 64;
+constexpr int kTileM = 64, kTileN = 64;
 
 template <int D>
 __global__ void __launch_bounds__(256) adaptive_score_kernel(const float *__restrict__ unit,
@@ -118,29 +120,35 @@ __global__ void __launch_bounds__(256) adaptive_score_kernel(const float *__rest
         n0 + r < Nb ? *reinterpret_cast<const f32x4 *>(&ku[(int64_t)(n0 + r) * D + 4 * c4]) : f32x4{};
   }
   __syncthreads();
-  // thread: block rows 2rg, 2rg + 1 and block columns cg, cg + 32 of the tile
-  const int cg = tid % 32, rg = tid / 32;
-  float dots[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-#pragma unroll 4
-  for (int c4 = 0; c4 < D / 4; ++c4) {
-    f32x4 qv[2], kv[2];
+  // thread: block rows rg + 16i and block columns cg + 16j of the tile
+  // (i, j < 4); the 16 lanes of a row group read one q row (broadcast) and
+  // 16 k rows 528 bytes apart (distinct banks)
+  const int cg = tid % 16, rg = tid / 16;
+  float dots[4][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      qv[i] = *reinterpret_cast<const f32x4 *>(&qs[(2 * rg + i) * STR + 4 * c4]);
-      kv[i] = *reinterpret_cast<const f32x4 *>(&ks[(cg + 32 * i) * STR + 4 * c4]);
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dots[i][j] = 0.f;
+#pragma unroll 2
+  for (int c4 = 0; c4 < D / 4; ++c4) {
+    f32x4 qv[4], kv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qv[i] = *reinterpret_cast<const f32x4 *>(&qs[(rg + 16 * i) * STR + 4 * c4]);
+      kv[i] = *reinterpret_cast<const f32x4 *>(&ks[(cg + 16 * i) * STR + 4 * c4]);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) dots[i][j] = fmaf(qv[i][e], kv[j][e], dots[i][j]);
+        for (int j = 0; j < 4; ++j) dots[i][j] = fmaf(qv[i][e], kv[j][e], dots[i][j]);
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int m = m0 + 2 * rg + i, n = n0 + cg + 32 * j;
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + rg + 16 * i, n = n0 + cg + 16 * j;
       if (m >= Mb || n >= Nb) continue;
       const float dot = dots[i][j];
       bool live = dot >= tau;
