@@ -94,15 +94,16 @@ def test_topk_index_ranges(gpu, d, N):
     rows each, at most eight ranges, wider ones past that): two ranges with a
     last range of one row, exactly eight, and tables that widen the ranges.
     Positions with indices in descending order, all in the last range, and
-    -1 / out-of-range slots; every output against the oracle, and two
-    launches bit for bit."""
-    t = W.make_topk("topk_ranges", B=1, M=4, H=20, d=d, N=N, topk=600, seed=N + d, drop=0.1,
+    -1 / out-of-range slots, over two batch items (two tables); every output
+    against the oracle, and two launches bit for bit."""
+    t = W.make_topk("topk_ranges", B=2, M=4, H=20, d=d, N=N, topk=600, seed=N + d, drop=0.1,
                     with_sink=True)
     idx = t.idx.clone()
     idx[0, 1] = torch.sort(idx[0, 1], descending=True).values
     idx[0, 2, :] = torch.arange(N - 600, N, dtype=idx.dtype).flip(0)
     idx[0, 2, ::5] = N
     idx[0, 3, ::9] = -3
+    idx[1, 0] = torch.sort(idx[1, 0]).values   # second batch item: its own table
     say(f"[topk] index ranges d={d} N={N}")
     q, kv, ig, sink = t.q.to(gpu), t.kv.to(gpu), idx.to(gpu), t.sink.to(gpu)
     out = bsa.topk_sparse_attn(q, kv, ig, sink, t.scale)
