@@ -150,8 +150,12 @@ __device__ __forceinline__ void copy_tile(const __bf16 *src, __bf16 *dst, int wi
 #pragma unroll
   for (int j = 0; j < NI / NW; ++j) {
     const uint32_t shift = (uint32_t)((j - j % P) * STEP * D * 2);   // bytes
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(reinterpret_cast<const char *>(src) + shift, bytes > shift ? bytes - shift : 0u);
+    // the bytes left past `shift`, formed with scalar-capable signed max (a
+    // saturating unsigned subtract exists only as a vector instruction, and a
+    // descriptor built from a vector register makes the compiler wrap the
+    // copy in a loop over its distinct values)
+    const uint32_t left = (uint32_t)max((int)bytes - (int)shift, 0);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const char *>(src) + shift, left);
     copy16_to_lds(rs, dst + (wid + NW * j) * 512, voff[j % P], 0u);
   }
 }
@@ -312,8 +316,10 @@ __device__ __forceinline__ Weight weight(float s, float scale_log2, float l2, co
 }
 
 // SEG instances (calls with segment ids) also skip the tiles whose ids
-// cannot meet.
-template <int BS, int D, typename T, bool MASK, bool SEG = false>
+// cannot meet.  CAUSAL instances serve the causal mask alone (whole blocks,
+// no cap, no segment ids): the plain code, with the keys after each query
+// masked on the diagonal tile only, before the weights.
+template <int BS, int D, typename T, bool MASK, bool SEG = false, bool CAUSAL = false>
 __global__ void __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
               const T *__restrict__ v, const T *__restrict__ dout,
@@ -420,7 +426,7 @@ bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
       if (!((keep >> ((t - beg) % 16)) & 1u)) continue;   // no key shares a segment
     }
     const int ncol = col_idx[t];
-    if (MASK && opt.causal && ncol > m) continue;   // every key after every query
+    if ((CAUSAL || (MASK && opt.causal)) && ncol > m) continue;  // every key after every query
     __syncthreads();                                // previous tile fully read
     const int kv = MASK ? (int)min((int64_t)BS, Sk - (int64_t)ncol * BS) : BS;  // keys that exist
     stage_tile<BS, D, NW, T>(kh + (int64_t)ncol * TILE, Ks, wid, lane, kv);
@@ -435,6 +441,13 @@ bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
       for (int c = 0; c < QC; ++c) {
         s = mfma32(row_read<D>(Ks, 32 * jt + l32, 2 * c + h2, sw_row), qf[c], s);
         dp = mfma32(row_read<D>(Vs, 32 * jt + l32, 2 * c + h2, sw_row), gf[c], dp);
+      }
+      if constexpr (CAUSAL) {
+        if (ncol == m) {  // the diagonal tile: keys after the query weigh nothing
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (32 * jt + 8 * (e / 4) + 4 * h2 + (e % 4) > qrow) s[e] = -__builtin_inff();
+        }
       }
       // S^T[key][query]: key 32jt + 8(e/4) + 4h2 + e%4, query qrow
 #pragma unroll
@@ -471,7 +484,7 @@ bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
                      scale * acc[dt][4 * a + 3]);
 }
 
-template <int BS, int D, typename T, bool MASK, bool SEG = false>
+template <int BS, int D, typename T, bool MASK, bool SEG = false, bool CAUSAL = false>
 __global__ void __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dkdv_kernel(const T *__restrict__ q, const T *__restrict__ k,
                 const T *__restrict__ v, const T *__restrict__ dout,
@@ -560,7 +573,7 @@ bwd_dkdv_kernel(const T *__restrict__ q, const T *__restrict__ k,
         if (!((keep >> ((t - beg) % 16)) & 1u)) continue;   // no query shares a segment
       }
       const int m = row_idx[t];
-      if (MASK && opt.causal && m < n) continue;    // every key after every query
+      if ((CAUSAL || (MASK && opt.causal)) && m < n) continue;  // every key after every query
       __syncthreads();                              // previous tile fully read
       const int qv = MASK ? (int)min((int64_t)BS, Sq - (int64_t)m * BS) : BS;  // rows that exist
       stage_tile<BS, D, NW, T>(q + (bh * Sq + (int64_t)m * BS) * D, Qs, wid, lane, qv);
@@ -587,6 +600,13 @@ bwd_dkdv_kernel(const T *__restrict__ q, const T *__restrict__ k,
 #pragma unroll
         for (int c = 0; c < QC; ++c)
           s = mfma32(row_read<D>(Qs, 32 * jq + l32, 2 * c + h2, sw_row), kf[c], s);
+        if constexpr (CAUSAL) {
+          if (m == n) {  // the diagonal tile: this key weighs nothing for earlier queries
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              if (krow > 32 * jq + 8 * (e / 4) + 4 * h2 + (e % 4)) s[e] = -__builtin_inff();
+          }
+        }
         // S[query][key]: query 32jq + 8(e/4) + 4h2 + e%4, key krow
         f32x16 w;   // P times the cap slope (MASK instances)
 #pragma unroll
@@ -923,14 +943,14 @@ hipError_t launch_grads16(const BwdArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BS, int D, typename T, bool MASK, bool SEG = false>
+template <int BS, int D, typename T, bool MASK, bool SEG = false, bool CAUSAL = false>
 hipError_t launch_grads(const BwdArgs &a, hipStream_t stream) {
   const float scale_log2 = a.scale * kLog2e;
   {
     const int64_t W = (int64_t)a.B * a.H * a.Mb;
     const int64_t grid = (W + 7) / 8 * 8;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dq_kernel<BS, D, T, MASK, SEG>), dim3((unsigned)grid), dim3(BS * 2), 0,
+    hipLaunchKernelGGL((bwd_dq_kernel<BS, D, T, MASK, SEG, CAUSAL>), dim3((unsigned)grid), dim3(BS * 2), 0,
                        stream,
                        (const T *)a.q, (const T *)a.k, (const T *)a.v,
                        (const T *)a.dout, (const T *)a.out, a.lse, a.lse2, a.Dv, a.row_ptr,
@@ -942,7 +962,7 @@ hipError_t launch_grads(const BwdArgs &a, hipStream_t stream) {
     const int64_t W = (int64_t)a.B * Hkv * a.Nb;
     const int64_t grid = (W + 7) / 8 * 8;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<BS, D, T, MASK, SEG>), dim3((unsigned)grid), dim3(BS * 2),
+    hipLaunchKernelGGL((bwd_dkdv_kernel<BS, D, T, MASK, SEG, CAUSAL>), dim3((unsigned)grid), dim3(BS * 2),
                        0, stream,
                        (const T *)a.q, (const T *)a.k, (const T *)a.v,
                        (const T *)a.dout, a.lse2, a.Dv, a.col_ptr, a.row_idx, a.col_order,
@@ -988,14 +1008,19 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
   const bool mask = a.opt.cap_k != 0.f || a.opt.causal != 0 || a.opt.sq % a.bs != 0 ||
                     a.opt.sk % a.bs != 0 || a.opt.qseg != nullptr;
   const bool seg = a.opt.qseg != nullptr;
+  // the causal mask alone (bf16, whole blocks, no cap, no segment ids) has
+  // instances of its own that mask the diagonal tiles only
+  const bool causal_only = a.opt.causal != 0 && a.opt.cap_k == 0.f && a.opt.sq % a.bs == 0 &&
+                           a.opt.sk % a.bs == 0 && a.opt.qseg == nullptr;
 #define BSA_BWD_CASE(BS_, D_)                                                                  \
   if (a.bs == BS_ && a.d == D_)                                                               \
     e = a.f32 ? (seg    ? launch_grads<BS_, D_, float, true, true>(a, stream)                 \
                  : mask ? launch_grads<BS_, D_, float, true>(a, stream)                       \
                         : launch_grads<BS_, D_, float, false>(a, stream))                     \
-              : (seg    ? launch_grads<BS_, D_, __bf16, true, true>(a, stream)                \
-                 : mask ? launch_grads<BS_, D_, __bf16, true>(a, stream)                      \
-                        : launch_grads<BS_, D_, __bf16, false>(a, stream));
+              : (seg           ? launch_grads<BS_, D_, __bf16, true, true>(a, stream)         \
+                 : causal_only ? launch_grads<BS_, D_, __bf16, false, false, true>(a, stream) \
+                 : mask        ? launch_grads<BS_, D_, __bf16, true>(a, stream)               \
+                               : launch_grads<BS_, D_, __bf16, false>(a, stream));
 #define BSA_BWD16_CASE(D_)                                                                     \
   if (a.bs == 16 && a.d == D_)                                                                \
     e = a.f32 ? (mask ? launch_grads16<D_, float, true>(a, stream)                            \

@@ -137,20 +137,23 @@ def test_backward_small(gpu, bs, d, opt_name):
         assert dsink is None
 
 
-def test_backward_full_workload(gpu):
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_full_workload(gpu, causal):
     """The 32-head, 32768-token, bs-128 causal workload: sampled query blocks
     for dq and sampled key blocks for dk and dv against the oracle; two
-    launches bit-identical."""
+    launches bit-identical.  With the element causal mask as well (the
+    instances that mask the diagonal tiles only): every sampled block row
+    and key block column holds its diagonal tile."""
     name = "causal_bernoulli_h32_s32768_bs128_d128"
-    say(f"[backward] full {name}: generating inputs")
+    say(f"[backward] full {name} causal={causal}: generating inputs")
     x = W.make_workload(name)
     dout = W.upstream_gradient(x.q.shape, seed=41)
     plan, _ = check_plan(gpu, x.layout)
     H = x.layout.shape[0]
     pc = check_plan_cols(gpu, x.layout, H)
     say(f"[backward] full {name}: launching")
-    g1 = _forward_backward(gpu, x, {}, plan, pc, dout)
-    g2 = _forward_backward(gpu, x, {}, plan, pc, dout)
+    g1 = _forward_backward(gpu, x, {"causal": causal}, plan, pc, dout)
+    g2 = _forward_backward(gpu, x, {"causal": causal}, plan, pc, dout)
     for a, b in zip(g1[:3], g2[:3]):
         assert torch.equal(a, b), "backward is not deterministic"
     dq, dk, dv, _ = g1
@@ -162,7 +165,7 @@ def test_backward_full_workload(gpu):
     say(f"[backward] full {name}: oracle on {len(rows)} row blocks, {len(cols)} key blocks")
     rq, rk, rv, _ = O.attention_backward_live_tiles(
         to64(x.q), to64(x.k), to64(x.v), to64(dout), x.layout, x.bs, x.scale,
-        row_blocks=rows, col_blocks=cols)
+        row_blocks=rows, col_blocks=cols, causal=causal)
     bs = x.bs
     compare_grad(np.concatenate([to64(dq[b, h, m * bs:(m + 1) * bs]) for b, h, m in rows]),
                  np.concatenate([rq[b, h, m * bs:(m + 1) * bs] for b, h, m in rows]), "dq full")
