@@ -316,10 +316,14 @@ __device__ __forceinline__ Weight weight(float s, float scale_log2, float l2, co
 }
 
 // SEG instances (calls with segment ids) also skip the tiles whose ids
-// cannot meet.  CAUSAL instances serve the causal mask alone (whole blocks,
-// no cap, no segment ids): the plain code, with the keys after each query
-// masked on the diagonal tile only, before the weights.
-template <int BS, int D, typename T, bool MASK, bool SEG = false, bool CAUSAL = false>
+// cannot meet.  LITE instances serve the causal mask and cut last blocks
+// without cap or segment ids: the plain code, with the keys after each query
+// (diagonal tiles) and the keys past a cut end (the last key tile) set to
+// -inf before the weights, under one uniform branch per tile each.  Rows
+// past a cut end weigh nothing through their lse2 of +inf.  LITE = 1: the
+// causal mask on whole blocks; LITE = 2: cut last blocks, with or without
+// the causal mask.
+template <int BS, int D, typename T, bool MASK, bool SEG = false, int LITE = 0>
 __global__ void __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
               const T *__restrict__ v, const T *__restrict__ dout,
@@ -362,7 +366,8 @@ bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
   const T *vh = v + bkv * Sk * D;
   const int qrow = 32 * wid + l32;            // query row inside the block
   const int64_t i_row = (int64_t)m * BS + qrow;
-  const bool q_ok = !MASK || i_row < Sq;     // rows past a cut last block
+  constexpr bool CUT = MASK || LITE == 2;      // lengths may end inside a block
+  const bool q_ok = !CUT || i_row < Sq;        // rows past a cut last block
   const int qsg = (MASK && opt.qseg && q_ok) ? opt.qseg[(int64_t)b * Sq + i_row] : 0;
 
   // D_i = dO_i . out_i (fp32 over the I/O values) and lse_i log2 e of this
@@ -426,9 +431,9 @@ bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
       if (!((keep >> ((t - beg) % 16)) & 1u)) continue;   // no key shares a segment
     }
     const int ncol = col_idx[t];
-    if ((CAUSAL || (MASK && opt.causal)) && ncol > m) continue;  // every key after every query
+    if ((MASK || LITE != 0) && opt.causal && ncol > m) continue;  // every key after every query
     __syncthreads();                                // previous tile fully read
-    const int kv = MASK ? (int)min((int64_t)BS, Sk - (int64_t)ncol * BS) : BS;  // keys that exist
+    const int kv = CUT ? (int)min((int64_t)BS, Sk - (int64_t)ncol * BS) : BS;  // keys that exist
     stage_tile<BS, D, NW, T>(kh + (int64_t)ncol * TILE, Ks, wid, lane, kv);
     stage_tile<BS, D, NW, T>(vh + (int64_t)ncol * TILE, Vs, wid, lane, kv);
     __builtin_amdgcn_s_waitcnt(0);
@@ -442,11 +447,16 @@ bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
         s = mfma32(row_read<D>(Ks, 32 * jt + l32, 2 * c + h2, sw_row), qf[c], s);
         dp = mfma32(row_read<D>(Vs, 32 * jt + l32, 2 * c + h2, sw_row), gf[c], dp);
       }
-      if constexpr (CAUSAL) {
-        if (ncol == m) {  // the diagonal tile: keys after the query weigh nothing
+      if constexpr (LITE != 0) {
+        if ((LITE == 1 || opt.causal) && ncol == m) {  // the diagonal tile: keys after the query weigh nothing
 #pragma unroll
           for (int e = 0; e < 16; ++e)
             if (32 * jt + 8 * (e / 4) + 4 * h2 + (e % 4) > qrow) s[e] = -__builtin_inff();
+        }
+        if (LITE == 2 && kv < BS) {  // the cut last key tile: keys past the end weigh nothing
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (32 * jt + 8 * (e / 4) + 4 * h2 + (e % 4) >= kv) s[e] = -__builtin_inff();
         }
       }
       // S^T[key][query]: key 32jt + 8(e/4) + 4h2 + e%4, query qrow
@@ -484,7 +494,7 @@ bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
                      scale * acc[dt][4 * a + 3]);
 }
 
-template <int BS, int D, typename T, bool MASK, bool SEG = false, bool CAUSAL = false>
+template <int BS, int D, typename T, bool MASK, bool SEG = false, int LITE = 0>
 __global__ void __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dkdv_kernel(const T *__restrict__ q, const T *__restrict__ k,
                 const T *__restrict__ v, const T *__restrict__ dout,
@@ -526,7 +536,8 @@ bwd_dkdv_kernel(const T *__restrict__ q, const T *__restrict__ k,
   const int64_t bkv = (int64_t)b * Hkv + kvh;
   const int krow = 32 * wid + l32;            // key row inside the block
   const int64_t j_row = (int64_t)n * BS + krow;
-  const bool k_ok = !MASK || j_row < Sk;     // keys past a cut last block
+  constexpr bool CUT = MASK || LITE == 2;      // lengths may end inside a block
+  const bool k_ok = !CUT || j_row < Sk;        // keys past a cut last block
   const int ksg = (MASK && opt.kseg && k_ok) ? opt.kseg[(int64_t)b * Sk + j_row] : 0;
 
   bf16x8 kf[QC], vf[QC];
@@ -573,9 +584,9 @@ bwd_dkdv_kernel(const T *__restrict__ q, const T *__restrict__ k,
         if (!((keep >> ((t - beg) % 16)) & 1u)) continue;   // no query shares a segment
       }
       const int m = row_idx[t];
-      if ((CAUSAL || (MASK && opt.causal)) && m < n) continue;  // every key after every query
+      if ((MASK || LITE != 0) && opt.causal && m < n) continue;  // every key after every query
       __syncthreads();                              // previous tile fully read
-      const int qv = MASK ? (int)min((int64_t)BS, Sq - (int64_t)m * BS) : BS;  // rows that exist
+      const int qv = CUT ? (int)min((int64_t)BS, Sq - (int64_t)m * BS) : BS;  // rows that exist
       stage_tile<BS, D, NW, T>(q + (bh * Sq + (int64_t)m * BS) * D, Qs, wid, lane, qv);
       stage_tile<BS, D, NW, T>(dout + (bh * Sq + (int64_t)m * BS) * D, Gs, wid, lane, qv);
       if (tid < BS) {
@@ -600,8 +611,10 @@ bwd_dkdv_kernel(const T *__restrict__ q, const T *__restrict__ k,
 #pragma unroll
         for (int c = 0; c < QC; ++c)
           s = mfma32(row_read<D>(Qs, 32 * jq + l32, 2 * c + h2, sw_row), kf[c], s);
-        if constexpr (CAUSAL) {
-          if (m == n) {  // the diagonal tile: this key weighs nothing for earlier queries
+        // (LITE: rows past a cut end weigh nothing through lse2 = +inf, and a
+        // key past it only feeds its own dK and dV rows, which are not stored)
+        if constexpr (LITE != 0) {
+          if ((LITE == 1 || opt.causal) && m == n) {  // the diagonal tile: this key weighs nothing for earlier queries
 #pragma unroll
             for (int e = 0; e < 16; ++e)
               if (krow > 32 * jq + 8 * (e / 4) + 4 * h2 + (e % 4)) s[e] = -__builtin_inff();
@@ -943,14 +956,14 @@ hipError_t launch_grads16(const BwdArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BS, int D, typename T, bool MASK, bool SEG = false, bool CAUSAL = false>
+template <int BS, int D, typename T, bool MASK, bool SEG = false, int LITE = 0>
 hipError_t launch_grads(const BwdArgs &a, hipStream_t stream) {
   const float scale_log2 = a.scale * kLog2e;
   {
     const int64_t W = (int64_t)a.B * a.H * a.Mb;
     const int64_t grid = (W + 7) / 8 * 8;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dq_kernel<BS, D, T, MASK, SEG, CAUSAL>), dim3((unsigned)grid), dim3(BS * 2), 0,
+    hipLaunchKernelGGL((bwd_dq_kernel<BS, D, T, MASK, SEG, LITE>), dim3((unsigned)grid), dim3(BS * 2), 0,
                        stream,
                        (const T *)a.q, (const T *)a.k, (const T *)a.v,
                        (const T *)a.dout, (const T *)a.out, a.lse, a.lse2, a.Dv, a.row_ptr,
@@ -962,7 +975,7 @@ hipError_t launch_grads(const BwdArgs &a, hipStream_t stream) {
     const int64_t W = (int64_t)a.B * Hkv * a.Nb;
     const int64_t grid = (W + 7) / 8 * 8;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<BS, D, T, MASK, SEG, CAUSAL>), dim3((unsigned)grid), dim3(BS * 2),
+    hipLaunchKernelGGL((bwd_dkdv_kernel<BS, D, T, MASK, SEG, LITE>), dim3((unsigned)grid), dim3(BS * 2),
                        0, stream,
                        (const T *)a.q, (const T *)a.k, (const T *)a.v,
                        (const T *)a.dout, a.lse2, a.Dv, a.col_ptr, a.row_idx, a.col_order,
@@ -1008,19 +1021,20 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
   const bool mask = a.opt.cap_k != 0.f || a.opt.causal != 0 || a.opt.sq % a.bs != 0 ||
                     a.opt.sk % a.bs != 0 || a.opt.qseg != nullptr;
   const bool seg = a.opt.qseg != nullptr;
-  // the causal mask alone (bf16, whole blocks, no cap, no segment ids) has
-  // instances of its own that mask the diagonal tiles only
-  const bool causal_only = a.opt.causal != 0 && a.opt.cap_k == 0.f && a.opt.sq % a.bs == 0 &&
-                           a.opt.sk % a.bs == 0 && a.opt.qseg == nullptr;
+  // the causal mask and cut last blocks without cap or segment ids (bf16)
+  // have instances of their own that mask the diagonal and last tiles only
+  const bool lite = mask && a.opt.cap_k == 0.f && a.opt.qseg == nullptr;
+  const bool whole = a.opt.sq % a.bs == 0 && a.opt.sk % a.bs == 0;
 #define BSA_BWD_CASE(BS_, D_)                                                                  \
   if (a.bs == BS_ && a.d == D_)                                                               \
     e = a.f32 ? (seg    ? launch_grads<BS_, D_, float, true, true>(a, stream)                 \
                  : mask ? launch_grads<BS_, D_, float, true>(a, stream)                       \
                         : launch_grads<BS_, D_, float, false>(a, stream))                     \
-              : (seg           ? launch_grads<BS_, D_, __bf16, true, true>(a, stream)         \
-                 : causal_only ? launch_grads<BS_, D_, __bf16, false, false, true>(a, stream) \
-                 : mask        ? launch_grads<BS_, D_, __bf16, true>(a, stream)               \
-                               : launch_grads<BS_, D_, __bf16, false>(a, stream));
+              : (seg    ? launch_grads<BS_, D_, __bf16, true, true>(a, stream)                \
+                 : lite ? (whole ? launch_grads<BS_, D_, __bf16, false, false, 1>(a, stream)  \
+                                 : launch_grads<BS_, D_, __bf16, false, false, 2>(a, stream)) \
+                 : mask ? launch_grads<BS_, D_, __bf16, true>(a, stream)                      \
+                        : launch_grads<BS_, D_, __bf16, false>(a, stream));
 #define BSA_BWD16_CASE(D_)                                                                     \
   if (a.bs == 16 && a.d == D_)                                                                \
     e = a.f32 ? (mask ? launch_grads16<D_, float, true>(a, stream)                            \
