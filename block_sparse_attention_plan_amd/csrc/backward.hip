@@ -308,8 +308,10 @@ template <bool MASK>
 __device__ __forceinline__ Weight weight(float s, float scale_log2, float l2, const FwdOptions &opt) {
   float slope = 1.f;
   if (MASK && opt.cap_k != 0.f) {
-    s = capped_score(s, opt.cap_k, opt.cap_b);
-    const float t = s / opt.cap_b;   // tanh of the scaled score over the cap
+    // the forward's capped score b * tanh, with the tanh kept for the slope:
+    // tanh(y) = 1 - 2 / (e^(2y) + 1), e^(2y) = exp2(s * k2)
+    const float t = fmaf(-2.f, __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(s * opt.cap_k) + 1.f), 1.f);
+    s = opt.cap_b * t;
     slope = fmaf(-t, t, 1.f);
   }
   return Weight{fast_exp2(fmaf(s, scale_log2, -l2)), slope};
