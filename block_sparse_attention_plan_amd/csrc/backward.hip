@@ -483,6 +483,12 @@ bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
           acc[dt] = mfma32(tr_read<D>(Ks, 32 * jt + 16 * c2, dt, tr_r, lc_off, pc, sw0, sw8), dsf,
                            acc[dt]);
       }
+      if constexpr (!MASK && LITE == 0) {
+        // S and dP: four row reads ahead, then one per product; dQ: two
+        // transpose reads per product
+        sched_interleave<2 * QC, 2 * QC, 4, 0>();
+        sched_steps<0, 2 * DT, 2, 0>();
+      }
     }
   }
   if (!q_ok) return;
