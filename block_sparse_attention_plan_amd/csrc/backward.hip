@@ -317,6 +317,14 @@ __device__ __forceinline__ Weight weight(float s, float scale_log2, float l2, co
   return Weight{fast_exp2(fmaf(s, scale_log2, -l2)), slope};
 }
 
+// The capped weight of the LITE = 3 instances, the cap decided at compile
+// time (the same operations as weight<true> with a cap).
+__device__ __forceinline__ Weight weight_cap(float s, float scale_log2, float l2,
+                                             const FwdOptions &opt) {
+  const float t = fmaf(-2.f, __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(s * opt.cap_k) + 1.f), 1.f);
+  return Weight{fast_exp2(fmaf(opt.cap_b * t, scale_log2, -l2)), fmaf(-t, t, 1.f)};
+}
+
 // SEG instances (calls with segment ids) also skip the tiles whose ids
 // cannot meet.  LITE instances serve the causal mask and cut last blocks
 // without cap or segment ids: the plain code, with the keys after each query
@@ -324,7 +332,10 @@ __device__ __forceinline__ Weight weight(float s, float scale_log2, float l2, co
 // -inf before the weights, under one uniform branch per tile each.  Rows
 // past a cut end weigh nothing through their lse2 of +inf.  LITE = 1: the
 // causal mask on whole blocks; LITE = 2: cut last blocks, with or without
-// the causal mask.
+// the causal mask; LITE = 3: the tanh cap, with or without the causal mask
+// and cut last blocks -- the cap decided at compile time, and the masked
+// weights set to zero after it by one compare and select per score (a
+// capped score of -inf would still be finite).
 template <int BS, int D, typename T, bool MASK, bool SEG = false, int LITE = 0>
 __global__ void __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
@@ -368,7 +379,7 @@ bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
   const T *vh = v + bkv * Sk * D;
   const int qrow = 32 * wid + l32;            // query row inside the block
   const int64_t i_row = (int64_t)m * BS + qrow;
-  constexpr bool CUT = MASK || LITE == 2;      // lengths may end inside a block
+  constexpr bool CUT = MASK || LITE >= 2;      // lengths may end inside a block
   const bool q_ok = !CUT || i_row < Sq;        // rows past a cut last block
   const int qsg = (MASK && opt.qseg && q_ok) ? opt.qseg[(int64_t)b * Sq + i_row] : 0;
 
@@ -441,6 +452,11 @@ bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const bool diag = MASK && opt.causal && ncol == m;
+    int limit = BS;   // LITE = 3: keys at or past it weigh nothing
+    if constexpr (LITE == 3) {
+      if (opt.causal && ncol == m) limit = qrow + 1;
+      limit = min(limit, kv);
+    }
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt) {
       f32x16 s = f32x16{}, dp = f32x16{};
@@ -449,7 +465,7 @@ bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
         s = mfma32(row_read<D>(Ks, 32 * jt + l32, 2 * c + h2, sw_row), qf[c], s);
         dp = mfma32(row_read<D>(Vs, 32 * jt + l32, 2 * c + h2, sw_row), gf[c], dp);
       }
-      if constexpr (LITE != 0) {
+      if constexpr (LITE == 1 || LITE == 2) {
         if ((LITE == 1 || opt.causal) && ncol == m) {  // the diagonal tile: keys after the query weigh nothing
 #pragma unroll
           for (int e = 0; e < 16; ++e)
@@ -464,8 +480,10 @@ bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
       // S^T[key][query]: key 32jt + 8(e/4) + 4h2 + e%4, query qrow
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const Weight wt = weight<MASK>(s[e], scale_log2, l2, opt);
+        const Weight wt = LITE == 3 ? weight_cap(s[e], scale_log2, l2, opt)
+                                    : weight<MASK>(s[e], scale_log2, l2, opt);
         float p = wt.p;
+        if constexpr (LITE == 3) p = 32 * jt + 8 * (e / 4) + 4 * h2 + (e % 4) >= limit ? 0.f : p;
         if (diag && 32 * jt + 8 * (e / 4) + 4 * h2 + (e % 4) > qrow) p = 0.f;
         if (MASK && 32 * jt + 8 * (e / 4) + 4 * h2 + (e % 4) >= kv) p = 0.f;
         if (MASK && opt.qseg) {  // packed sequences: only keys of the query's segment
@@ -483,9 +501,9 @@ bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
           acc[dt] = mfma32(tr_read<D>(Ks, 32 * jt + 16 * c2, dt, tr_r, lc_off, pc, sw0, sw8), dsf,
                            acc[dt]);
       }
-      if constexpr (!MASK && LITE == 0) {
+      if constexpr (!MASK && (LITE == 0 || LITE == 3)) {
         // S and dP: four row reads ahead, then one per product; dQ: two
-        // transpose reads per product
+        // transpose reads per product (blocks without branches only)
         sched_interleave<2 * QC, 2 * QC, 4, 0>();
         sched_steps<0, 2 * DT, 2, 0>();
       }
@@ -544,7 +562,7 @@ bwd_dkdv_kernel(const T *__restrict__ q, const T *__restrict__ k,
   const int64_t bkv = (int64_t)b * Hkv + kvh;
   const int krow = 32 * wid + l32;            // key row inside the block
   const int64_t j_row = (int64_t)n * BS + krow;
-  constexpr bool CUT = MASK || LITE == 2;      // lengths may end inside a block
+  constexpr bool CUT = MASK || LITE >= 2;      // lengths may end inside a block
   const bool k_ok = !CUT || j_row < Sk;        // keys past a cut last block
   const int ksg = (MASK && opt.kseg && k_ok) ? opt.kseg[(int64_t)b * Sk + j_row] : 0;
 
@@ -606,6 +624,9 @@ bwd_dkdv_kernel(const T *__restrict__ q, const T *__restrict__ k,
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       const bool diag = MASK && opt.causal && m == n;
+      int qlim = 0;   // LITE = 3: queries before it weigh nothing (diagonal tile)
+      if constexpr (LITE == 3)
+        if (opt.causal && m == n) qlim = krow;
       // One 32-query chunk at a time: K^T, V^T and both accumulators stay
       // live across the loop, so the chunks are not unrolled into each other,
       // and each chunk runs in phases (fenced against the scheduler) that keep
@@ -621,7 +642,7 @@ bwd_dkdv_kernel(const T *__restrict__ q, const T *__restrict__ k,
           s = mfma32(row_read<D>(Qs, 32 * jq + l32, 2 * c + h2, sw_row), kf[c], s);
         // (LITE: rows past a cut end weigh nothing through lse2 = +inf, and a
         // key past it only feeds its own dK and dV rows, which are not stored)
-        if constexpr (LITE != 0) {
+        if constexpr (LITE == 1 || LITE == 2) {
           if ((LITE == 1 || opt.causal) && m == n) {  // the diagonal tile: this key weighs nothing for earlier queries
 #pragma unroll
             for (int e = 0; e < 16; ++e)
@@ -629,20 +650,23 @@ bwd_dkdv_kernel(const T *__restrict__ q, const T *__restrict__ k,
           }
         }
         // S[query][key]: query 32jq + 8(e/4) + 4h2 + e%4, key krow
-        f32x16 w;   // P times the cap slope (MASK instances)
+        constexpr bool SLOPE = MASK || LITE == 3;   // weights carry a cap slope
+        f32x16 w;   // P times the cap slope (SLOPE instances)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&Ls[32 * jq + 8 * a + 4 * h2]);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int e = 4 * a + i;
-            const Weight wt = weight<MASK>(s[e], scale_log2, l4[i], opt);
+            const Weight wt = LITE == 3 ? weight_cap(s[e], scale_log2, l4[i], opt)
+                                        : weight<MASK>(s[e], scale_log2, l4[i], opt);
             float p = wt.p;
+            if constexpr (LITE == 3) p = 32 * jq + 8 * a + 4 * h2 + i < qlim ? 0.f : p;
             if (diag && krow > 32 * jq + 8 * a + 4 * h2 + i) p = 0.f;
             if (!k_ok) p = 0.f;
             if (MASK && opt.qseg && Gq[32 * jq + 8 * a + 4 * h2 + i] != ksg) p = 0.f;
             s[e] = p;
-            if constexpr (MASK) w[e] = p * wt.slope;
+            if constexpr (SLOPE) w[e] = p * wt.slope;
           }
         }
         bf16x8 pf[2], wf[2];
@@ -650,7 +674,7 @@ bwd_dkdv_kernel(const T *__restrict__ q, const T *__restrict__ k,
         for (int c2 = 0; c2 < 2; ++c2) {
           pf[c2] = to_bf16x8(s[8 * c2 + 0], s[8 * c2 + 1], s[8 * c2 + 2], s[8 * c2 + 3],
                              s[8 * c2 + 4], s[8 * c2 + 5], s[8 * c2 + 6], s[8 * c2 + 7]);
-          if constexpr (MASK)
+          if constexpr (SLOPE)
             wf[c2] = to_bf16x8(w[8 * c2 + 0], w[8 * c2 + 1], w[8 * c2 + 2], w[8 * c2 + 3],
                                w[8 * c2 + 4], w[8 * c2 + 5], w[8 * c2 + 6], w[8 * c2 + 7]);
           else
@@ -1033,6 +1057,9 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
   // have instances of their own that mask the diagonal and last tiles only
   const bool lite = mask && a.opt.cap_k == 0.f && a.opt.qseg == nullptr;
   const bool whole = a.opt.sq % a.bs == 0 && a.opt.sk % a.bs == 0;
+  // the cap without segment ids (bf16) likewise: the cap decided at compile
+  // time, the masks by a select per score
+  const bool capped = a.opt.cap_k != 0.f && a.opt.qseg == nullptr;
 #define BSA_BWD_CASE(BS_, D_)                                                                  \
   if (a.bs == BS_ && a.d == D_)                                                               \
     e = a.f32 ? (seg    ? launch_grads<BS_, D_, float, true, true>(a, stream)                 \
@@ -1041,6 +1068,7 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
               : (seg    ? launch_grads<BS_, D_, __bf16, true, true>(a, stream)                \
                  : lite ? (whole ? launch_grads<BS_, D_, __bf16, false, false, 1>(a, stream)  \
                                  : launch_grads<BS_, D_, __bf16, false, false, 2>(a, stream)) \
+                 : capped ? launch_grads<BS_, D_, __bf16, false, false, 3>(a, stream)         \
                  : mask ? launch_grads<BS_, D_, __bf16, true>(a, stream)                      \
                         : launch_grads<BS_, D_, __bf16, false>(a, stream));
 #define BSA_BWD16_CASE(D_)                                                                     \

@@ -81,11 +81,11 @@ def test_forward_ragged(gpu, bs, d, dtype, Sq, Sk, causal, sink):
     compare_lse(lse.cpu().numpy(), ref_lse, f"ragged bs={bs} d={d}")
 
 
-@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("causal,cap", [(False, None), (True, None), (True, 2.0)])
 @pytest.mark.parametrize("bs,d,Sq,Sk", [(32, 64, 3 * 32 - 5, 4 * 32 - 31), (64, 128, 200, 150),
                                         (128, 128, 3 * 128 - 1, 2 * 128 + 3), (128, 32, 129, 300),
                                         (16, 32, 3 * 16 - 7, 5 * 16 + 1)])
-def test_backward_ragged(gpu, bs, d, Sq, Sk, causal):
+def test_backward_ragged(gpu, bs, d, Sq, Sk, causal, cap):
     H, Hkv, B = 4, 2, 2
     Mb, Nb = -(-Sq // bs), -(-Sk // bs)
     rng = np.random.default_rng(bs * 3 + Sq + Sk)
@@ -95,22 +95,24 @@ def test_backward_ragged(gpu, bs, d, Sq, Sk, causal):
     x = W.make_bsa("ragged_bwd", B=B, H=H, S=Sq, Sk=Sk, bs=bs, d=d, dtype="bf16",
                    layout="given", layout_array=lay, seed=Sq + 7, Hkv=Hkv, sink_mean=1.0)
     dout = W.upstream_gradient(x.q.shape, seed=Sk)
-    say(f"[ragged] backward bs={bs} d={d} Sq={Sq} Sk={Sk} causal={causal}")
+    say(f"[ragged] backward bs={bs} d={d} Sq={Sq} Sk={Sk} causal={causal} cap={cap}")
     plan, _ = check_plan(gpu, lay)
     pc = check_plan_cols(gpu, lay, Hkv)
     q, k, v, sink = x.q.to(gpu), x.k.to(gpu), x.v.to(gpu), x.sink.to(gpu)
-    out, lse = bsa.bsa_forward(q, k, v, plan, x.scale, attn_sink=sink, causal=causal, bs=bs)
+    out, lse = bsa.bsa_forward(q, k, v, plan, x.scale, attn_sink=sink, causal=causal, bs=bs,
+                               soft_cap=cap)
     qb, dq = padded(tuple(q.shape), torch.bfloat16, gpu)
     kb, dk = padded(tuple(k.shape), torch.bfloat16, gpu)
     vb, dv = padded(tuple(v.shape), torch.bfloat16, gpu)
     _, _, _, dsink = bsa.bsa_backward(q, k, v, out, dout.to(gpu), lse, plan, pc, x.scale,
-                                      attn_sink=sink, causal=causal, dq=dq, dk=dk, dv=dv, bs=bs)
+                                      attn_sink=sink, causal=causal, dq=dq, dk=dk, dv=dv, bs=bs,
+                                      soft_cap=cap)
     torch.cuda.synchronize()
     for buf, t in ((qb, dq), (kb, dk), (vb, dv)):
         assert sentinel_intact(buf, t.numel())
     rq, rk, rv, rs = O.attention_backward_dense(
         to64(x.q), to64(x.k), to64(x.v), to64(dout), lay, bs, x.scale,
-        sink=x.sink.numpy().astype(np.float64), causal=causal)
+        sink=x.sink.numpy().astype(np.float64), causal=causal, soft_cap=cap)
     compare_grad(to64(dq), rq, f"dq ragged bs={bs}")
     compare_grad(to64(dk), rk, f"dk ragged bs={bs}")
     compare_grad(to64(dv), rv, f"dv ragged bs={bs}")
@@ -118,7 +120,7 @@ def test_backward_ragged(gpu, bs, d, Sq, Sk, causal):
     # of the bf16 output inside D_i, twice 2^-9 of the summed magnitudes)
     sk64 = x.sink.numpy().astype(np.float64)
     o64, l64 = O.attention_dense_masked(to64(x.q), to64(x.k), to64(x.v), lay, bs, x.scale,
-                                        sink=sk64, causal=causal)
+                                        sink=sk64, causal=causal, soft_cap=cap)
     w = np.exp(sk64[None, :, None] - l64)
     bound = 2.0 * 2.0 ** -9 * (w * np.abs(to64(dout) * o64).sum(-1)).sum(axis=(0, 2))
     assert np.all(np.abs(dsink.cpu().numpy() - rs) <= bound + 1e-6)
