@@ -1058,19 +1058,19 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
   const bool lite = mask && a.opt.cap_k == 0.f && a.opt.qseg == nullptr;
   const bool whole = a.opt.sq % a.bs == 0 && a.opt.sk % a.bs == 0;
   // the cap without segment ids (bf16) likewise: the cap decided at compile
-  // time, the masks by a select per score
+  // time, the masks by a select per score.  (Every other bf16 call with a
+  // mask has segment ids, so the bf16 MASK instances are the SEG ones.)
   const bool capped = a.opt.cap_k != 0.f && a.opt.qseg == nullptr;
 #define BSA_BWD_CASE(BS_, D_)                                                                  \
   if (a.bs == BS_ && a.d == D_)                                                               \
     e = a.f32 ? (seg    ? launch_grads<BS_, D_, float, true, true>(a, stream)                 \
                  : mask ? launch_grads<BS_, D_, float, true>(a, stream)                       \
                         : launch_grads<BS_, D_, float, false>(a, stream))                     \
-              : (seg    ? launch_grads<BS_, D_, __bf16, true, true>(a, stream)                \
-                 : lite ? (whole ? launch_grads<BS_, D_, __bf16, false, false, 1>(a, stream)  \
-                                 : launch_grads<BS_, D_, __bf16, false, false, 2>(a, stream)) \
+              : (seg      ? launch_grads<BS_, D_, __bf16, true, true>(a, stream)              \
+                 : lite   ? (whole ? launch_grads<BS_, D_, __bf16, false, false, 1>(a, stream) \
+                                   : launch_grads<BS_, D_, __bf16, false, false, 2>(a, stream))\
                  : capped ? launch_grads<BS_, D_, __bf16, false, false, 3>(a, stream)         \
-                 : mask ? launch_grads<BS_, D_, __bf16, true>(a, stream)                      \
-                        : launch_grads<BS_, D_, __bf16, false>(a, stream));
+                          : launch_grads<BS_, D_, __bf16, false>(a, stream));
 #define BSA_BWD16_CASE(D_)                                                                     \
   if (a.bs == 16 && a.d == D_)                                                                \
     e = a.f32 ? (mask ? launch_grads16<D_, float, true>(a, stream)                            \
