@@ -353,6 +353,7 @@ bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
 
   __shared__ __attribute__((aligned(1024))) __bf16 Ks[TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 Vs[TILE];
+  __shared__ __attribute__((aligned(16))) int32_t Gk[SEG ? BS : 4];  // segment ids of the tile's keys
 
   const int64_t W = (int64_t)B * H * Mb;
   const int64_t per = (W + 7) / 8;
@@ -449,6 +450,8 @@ bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
     const int kv = CUT ? (int)min((int64_t)BS, Sk - (int64_t)ncol * BS) : BS;  // keys that exist
     stage_tile<BS, D, NW, T>(kh + (int64_t)ncol * TILE, Ks, wid, lane, kv);
     stage_tile<BS, D, NW, T>(vh + (int64_t)ncol * TILE, Vs, wid, lane, kv);
+    if constexpr (SEG)
+      if (tid < BS) Gk[tid] = tid < kv ? opt.kseg[(int64_t)b * Sk + (int64_t)ncol * BS + tid] : 0;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const bool diag = MASK && opt.causal && ncol == m;
@@ -486,9 +489,11 @@ bwd_dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
         if constexpr (LITE == 3) p = 32 * jt + 8 * (e / 4) + 4 * h2 + (e % 4) >= limit ? 0.f : p;
         if (diag && 32 * jt + 8 * (e / 4) + 4 * h2 + (e % 4) > qrow) p = 0.f;
         if (MASK && 32 * jt + 8 * (e / 4) + 4 * h2 + (e % 4) >= kv) p = 0.f;
-        if (MASK && opt.qseg) {  // packed sequences: only keys of the query's segment
-          const int kt = 32 * jt + 8 * (e / 4) + 4 * h2 + (e % 4);
-          if (kt < kv && opt.kseg[(int64_t)b * Sk + (int64_t)ncol * BS + kt] != qsg) p = 0.f;
+        if constexpr (SEG) {  // packed sequences: only keys of the query's segment
+          // the 4 keys 32jt + 8(e/4) + 4h2 + 0..3 are consecutive: one 16-byte read
+          const int4 g4 = *reinterpret_cast<const int4 *>(&Gk[32 * jt + 8 * (e / 4) + 4 * h2]);
+          const int kid = (e % 4) == 0 ? g4.x : (e % 4) == 1 ? g4.y : (e % 4) == 2 ? g4.z : g4.w;
+          if (kid != qsg) p = 0.f;
         }
         s[e] = p * (dp[e] - dd) * wt.slope;
       }
