@@ -184,3 +184,46 @@ def test_topk_sweep(gpu, seed):
     compare(to64(out), ref, f"topk sweep {seed}")
     empty = (ref_idx < 0).all(axis=-1)       # positions without a valid slot give zeros
     assert torch.all(out.cpu()[torch.from_numpy(empty)] == 0)
+
+
+TOPK_WIDE_SEEDS = list(range(9800, 9820))
+
+
+def draw_topk_wide_case(seed: int):
+    """Tables of 2 to 35 index ranges (N up to 70,000 rows) and lists of up
+    to 2048 slots, so the compacted list groups indices by range."""
+    r = np.random.default_rng(seed)
+    d = int(r.choice([128, 256, 512]))
+    return dict(d=d, H=int(r.integers(1, 21)), B=int(r.integers(1, 3)), M=int(r.integers(1, 5)),
+                N=int(r.integers(2049, 70001)), topk=int(r.integers(1, 2049)),
+                drop=float(r.choice([0.0, 0.1, 0.5])), with_sink=bool(r.random() < 0.6),
+                dups=bool(r.random() < 0.3), wild=bool(r.random() < 0.3))
+
+
+@pytest.mark.parametrize("seed", TOPK_WIDE_SEEDS)
+def test_topk_wide_sweep(gpu, seed):
+    c = draw_topk_wide_case(seed)
+    say(f"[sweep] topk wide seed={seed} {c}")
+    t = W.make_topk("sweep_topk_wide", B=c["B"], M=c["M"], H=c["H"], d=c["d"], N=c["N"],
+                    topk=c["topk"], seed=seed, drop=0.0, with_sink=c["with_sink"])
+    r = np.random.default_rng(seed + 1)
+    if c["dups"]:
+        idx = r.integers(0, c["N"], size=(c["B"], c["M"], c["topk"])).astype(np.int32)
+    else:
+        idx = t.idx.numpy().copy()
+    idx[r.random(idx.shape) < c["drop"]] = -1
+    if c["wild"]:
+        wild = r.random(idx.shape) < 0.1
+        idx[wild] = r.choice([-7, c["N"], c["N"] + 3, 2 ** 31 - 1], size=int(wild.sum()))
+    sink = t.sink.to(gpu) if c["with_sink"] else None
+    ig = torch.from_numpy(idx).to(gpu)
+    q, kv = t.q.to(gpu), t.kv.to(gpu)
+    out = bsa.topk_sparse_attn(q, kv, ig, sink, t.scale)
+    out2 = bsa.topk_sparse_attn(q, kv, ig, sink, t.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "top-k is not deterministic"
+    ref_idx = idx.copy()
+    ref_idx[(ref_idx < 0) | (ref_idx >= c["N"])] = -1
+    ref = O.topk_attention(to64(t.q), to64(t.kv), ref_idx,
+                           t.sink.numpy() if c["with_sink"] else None, t.scale)
+    compare(to64(out), ref, f"topk wide sweep {seed}")
