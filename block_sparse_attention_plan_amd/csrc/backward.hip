@@ -32,6 +32,10 @@
 // tile is read both row-wise (16-byte reads) and transposed
 // (ds_read_b64_tr_b16), so its 16-byte chunks are XOR-swizzled per row with a
 // pattern that keeps both read shapes free of bank conflicts.
+// Instances of the bs >= 32 kernels by option set: plain; LITE (bf16) for the
+// causal mask, cut last blocks and the cap, each decided per tile or at
+// compile time so that no per-score test on an option remains; MASK + SEG
+// for segment ids; MASK for fp32 I/O with any option.
 #include <type_traits>
 
 #include "bsa_device.h"
