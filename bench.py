@@ -218,14 +218,16 @@ def cpu_baseline(fwd, topk_in, budget_s: float):
 
 CALIBRATION_BYTES = float(1 << 30)   # read and written by the calibration copy
 # Kernel-name tests on mangled names: the copy-staged forward for bs 128, d 128
-# (one wave per row group, tiles in two pieces) with its options flag `false`
-# (Lb0E) or `true` (Lb1E), no segment ids (Lb0E) and rows, not pairs (Lb0E);
-# the same kernel in its pair form (last flag Lb1E), which serves the bs-64
+# (one wave per row group, tiles in two pieces) with its five flags (MASK,
+# segment ids, pairs, the plain-copy option form, the cap compiled into that
+# form) all `false` (Lb0E) for the plain step; the plain-copy option form with
+# the cap (last two flags Lb1E), which serves the forward with every option on
+# whole blocks; the pair form (third flag Lb1E), which serves the bs-64
 # workload whose neighbouring rows share tiles; and the d-512 top-k instance.
 KERNEL_MATCH = {
-    "bsa_forward": lambda n: "bsa_fwd_dma_kernelILi128ELi128ELi1ELi2ELb0ELb0ELb0ELb0EE" in n,
-    "bsa_forward_options": lambda n: "bsa_fwd_dma_kernelILi128ELi128ELi1ELi2ELb1ELb0ELb0ELb0EE" in n,
-    "bsa_forward_lgs": lambda n: "bsa_fwd_dma_kernelILi128ELi128ELi1ELi2ELb0ELb0ELb1ELb0EE" in n,
+    "bsa_forward": lambda n: "bsa_fwd_dma_kernelILi128ELi128ELi1ELi2ELb0ELb0ELb0ELb0ELb0EE" in n,
+    "bsa_forward_options": lambda n: "bsa_fwd_dma_kernelILi128ELi128ELi1ELi2ELb0ELb0ELb0ELb1ELb1EE" in n,
+    "bsa_forward_lgs": lambda n: "bsa_fwd_dma_kernelILi128ELi128ELi1ELi2ELb0ELb0ELb1ELb0ELb0EE" in n,
     # the instance for topk <= 2048 (valid slots compacted first)
     "topk_sparse_attn": lambda n: "topk_kernel" in n and ("<512, true>" in n or "ILi512ELb1EE" in n),
 }

@@ -61,7 +61,7 @@ def _write_counters(path, counter, rows):
 
 
 def test_summarize_counters_scales_by_the_calibration_copy(tmp_path):
-    fwd = "_ZN3bsa12_GLOBAL__N_118bsa_fwd_dma_kernelILi128ELi128ELi1ELi2ELb0ELb0ELb0ELb0EEEvPK"
+    fwd = "_ZN3bsa12_GLOBAL__N_118bsa_fwd_dma_kernelILi128ELi128ELi1ELi2ELb0ELb0ELb0ELb0ELb0EEEvPK"
     topk = "void topk_kernel<512, true>(bool _Accum const*, ...)"
     neg = "void at::native::neg_kernel_cuda(...)"
     fetch = tmp_path / "fetch.csv"
